@@ -1,0 +1,137 @@
+"""Host-side block manager: free list, per-sequence block tables, reference
+counts and copy-on-write decisions for a pool of fixed-size KV blocks.
+
+It produces the three index inputs of the device entry points: block tables,
+slot mappings and (src, dst) copy pairs.  It runs on the host and touches no
+KV data.
+
+Rules followed (source pages by title and section):
+- "PagedAttention" glossary page (Ultralytics), how paging works: a sequence
+  takes a new block only when its last one is full, from any free location;
+  the table records the order; the worked example pops free blocks from the
+  front of a free list, and token ``pos`` goes to slot ``pos % 16`` of block
+  ``table[pos // 16]``.
+- Same page, sharing blocks between sequences: tables of several sequences
+  may name one physical block, with a per-block reference count; a sequence
+  about to write into a block that others still use copies it first.
+- Russian page on PagedAttention in vLLM, "two answers to one request": full
+  shared blocks stay shared; only the block that has to split is copied;
+  blocks left without references are freed.
+- Same page, logical order vs physical placement: the prompt is allocated
+  first, then the last block fills, and a new block is added only when needed.
+  (The French dev.to article says every new token takes a block from the free
+  list; the two other pages are followed.)
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+BLOCK_SIZE = 16
+
+
+class NoFreeBlock(RuntimeError):
+    """The pool has no free block left."""
+
+
+@dataclass
+class _Seq:
+    table: list = field(default_factory=list)
+    length: int = 0
+
+
+class BlockManager:
+    def __init__(self, num_blocks: int, free_list=None, block_size: int = BLOCK_SIZE):
+        if block_size != BLOCK_SIZE:
+            raise ValueError("block size is fixed at 16 tokens")
+        self.num_blocks = int(num_blocks)
+        self.block_size = block_size
+        self.free = list(range(num_blocks)) if free_list is None else [int(b) for b in free_list]
+        if len(set(self.free)) != len(self.free) or any(
+                b < 0 or b >= num_blocks for b in self.free):
+            raise ValueError("free list must hold distinct block ids inside the pool")
+        self.refcount = [0] * self.num_blocks
+        self.seqs: dict = {}
+        # event counters (allocations, copies, frees) for accounting reports
+        self.n_alloc = 0
+        self.n_cow = 0
+        self.n_freed = 0
+
+    # ----------------------------------------------------------- allocation
+    def _allocate(self) -> int:
+        if not self.free:
+            raise NoFreeBlock("no free block in a pool of %d" % self.num_blocks)
+        b = self.free.pop(0)
+        self.refcount[b] = 1
+        self.n_alloc += 1
+        return b
+
+    def add_sequence(self, seq_id) -> None:
+        if seq_id in self.seqs:
+            raise KeyError("sequence %r exists" % (seq_id,))
+        self.seqs[seq_id] = _Seq()
+
+    def append_tokens(self, seq_id, n: int):
+        """Reserve slots for ``n`` new tokens of ``seq_id``.
+
+        Returns ``(slots, cow_pairs)``: the slot of each new token, and the
+        (src, dst) block copies that must run before those tokens are written.
+        """
+        seq = self.seqs[seq_id]
+        slots, pairs = [], []
+        for _ in range(int(n)):
+            pos = seq.length
+            if pos % self.block_size == 0:
+                seq.table.append(self._allocate())
+            else:
+                last = seq.table[-1]
+                if self.refcount[last] > 1:
+                    new = self._allocate()
+                    pairs.append((last, new))
+                    self.refcount[last] -= 1
+                    seq.table[-1] = new
+                    self.n_cow += 1
+            slots.append(seq.table[pos // self.block_size] * self.block_size
+                         + pos % self.block_size)
+            seq.length += 1
+        return slots, pairs
+
+    def fork(self, parent, child) -> None:
+        """``child`` starts as a copy of ``parent``'s table, sharing every block."""
+        p = self.seqs[parent]
+        self.add_sequence(child)
+        c = self.seqs[child]
+        c.table = list(p.table)
+        c.length = p.length
+        for b in p.table:
+            self.refcount[b] += 1
+
+    def free_sequence(self, seq_id) -> None:
+        seq = self.seqs.pop(seq_id)
+        for b in seq.table:
+            self.refcount[b] -= 1
+            if self.refcount[b] == 0:
+                self.free.append(b)
+                self.n_freed += 1
+
+    # -------------------------------------------------------------- queries
+    def block_table(self, seq_id) -> list:
+        return list(self.seqs[seq_id].table)
+
+    def length(self, seq_id) -> int:
+        return self.seqs[seq_id].length
+
+    def physical_blocks_in_use(self) -> int:
+        return sum(1 for r in self.refcount if r > 0)
+
+    def logical_blocks(self) -> int:
+        return sum(len(s.table) for s in self.seqs.values())
+
+
+def blocks_for(n_tokens: int, block_size: int = BLOCK_SIZE) -> int:
+    """Blocks a sequence of n tokens occupies: ceil(n / block_size)."""
+    return -(-int(n_tokens) // block_size)
+
+
+def unused_slots(n_tokens: int, block_size: int = BLOCK_SIZE) -> int:
+    """Slots reserved but unused: only the unfilled part of the last block."""
+    return blocks_for(n_tokens, block_size) * block_size - int(n_tokens)

@@ -1,0 +1,243 @@
+"""Seeded synthetic workloads for paged decode attention.
+
+This module draws inputs only: context lengths, block placement (through the
+host block manager), q/K/V values and the order of cache operations.  It holds
+no attention, scatter or gather arithmetic, and both the GPU path and the CPU
+oracle consume what it returns.
+
+The five workload shapes come from the source pages' scenarios:
+- ``tiny``: the worked example of the "PagedAttention" glossary page
+  (Ultralytics), section on how paging works: one 40-token request, head
+  dim 64, blocks of 16 drawn at random from a pool of 64, fp32.
+- ``mha13b``: a LLaMA-13B-shaped layer (40 heads of 128, the model whose
+  per-sequence KV cache the same page's memory-problem section sizes at
+  1.7 GB): batch 32, bf16, contexts uniform in [1, 2048].
+- ``gqa70b``: one layer of the French page's Llama 3.1 70B scenario (memory
+  problem section: 256 users x 4096 tokens): 64 query heads over 8 KV heads,
+  every context 4096 tokens, blocks scattered.
+- ``sampling``: parallel sampling over shared prompts (glossary page, section
+  on sharing blocks): 64 prompts x 3 samples, 40 query / 8 KV heads; each
+  prompt's blocks are shared by its samples; each sample then appends
+  0..512 private tokens.  Variant "a" uses 1024-token prompts (no partial
+  shared block, so no copy-on-write); variant "b" uses 1016-token prompts so
+  the shared last block is half full and the first writers copy it.
+- ``fp8``: FP8 cache (glossary page, related techniques): 128 sequences,
+  64 / 8 heads, K/V stored as E4M3 with one fp32 scale per pool
+  (max |x| / 448), q in bf16, lognormal context lengths (median 2048,
+  sigma 1, clipped to [16, 32768]), split-K partitions of 512 tokens.
+
+Random draws: numpy ``default_rng(seed)`` for lengths and block placement;
+``torch.Generator`` seeded with the same seed for N(0, 1) values drawn in
+fp32 and rounded to the storage dtype (round-to-nearest-even).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+from .blocks import BlockManager, blocks_for
+
+F32, BF16, FP8 = 0, 1, 2
+TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16}
+CONFIG_IDS = ("tiny", "mha13b", "gqa70b", "sampling_a", "sampling_b", "fp8")
+SEEDS = {"tiny": 0, "mha13b": 1, "gqa70b": 2, "sampling_a": 3, "sampling_b": 3, "fp8": 4}
+
+
+@dataclass
+class Workload:
+    name: str
+    S: int
+    Hq: int
+    Hkv: int
+    D: int
+    pool_dtype: int
+    q_dtype: int
+    kv_in_dtype: int
+    num_blocks: int
+    context_lens: np.ndarray          # int32 [S]
+    block_tables: np.ndarray          # int32 [S][MBS]; unused entries are -1
+    q: torch.Tensor                   # [S][Hq][D]
+    scale: float
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+    partition_tokens: int = 0
+    # cache operations that build the pool, in order:
+    #   ("write", k [N][Hkv][D], v [N][Hkv][D], slots int32 [N]) or ("copy", pairs int32 [P][2])
+    ops: list = field(default_factory=list)
+    # the newest token of every sequence (what one decode step writes)
+    step_k: torch.Tensor | None = None
+    step_v: torch.Tensor | None = None
+    step_slots: np.ndarray | None = None
+    info: dict = field(default_factory=dict)
+
+    @property
+    def max_blocks_per_seq(self) -> int:
+        return int(self.block_tables.shape[1])
+
+    @property
+    def group(self) -> int:
+        return self.Hq // self.Hkv
+
+    def kv_bytes(self) -> int:
+        """Algorithmic K+V bytes one decode pass reads: sum ctx * Hkv * D * 2 * elem."""
+        eb = {F32: 4, BF16: 2, FP8: 1}[self.pool_dtype]
+        return int(self.context_lens.astype(np.int64).sum()) * self.Hkv * self.D * 2 * eb
+
+
+def _f32(x: float) -> float:
+    """The nearest fp32 value: the entry points take the softmax scale as fp32."""
+    return float(np.float32(x))
+
+
+def _randn(gen, shape, dtype, device):
+    x = torch.randn(shape, generator=gen, dtype=torch.float32, device=device)
+    return x.to(dtype)
+
+
+def _tables_from(mgr: BlockManager, seq_ids, mbs=None) -> np.ndarray:
+    rows = [mgr.block_table(s) for s in seq_ids]
+    mbs = mbs or max(1, max(len(r) for r in rows))
+    t = np.full((len(rows), mbs), -1, dtype=np.int32)
+    for i, r in enumerate(rows):
+        t[i, :len(r)] = r
+    return t
+
+
+def _simple(name, S, Hq, Hkv, D, ctx, pool_dt, q_dt, in_dt, scale, seed, device,
+            rng, num_blocks=None, free_list=None, partition_tokens=0, fp8_scales=False):
+    """Independent sequences, each filled by one bulk write."""
+    ctx = np.asarray(ctx, dtype=np.int32)
+    need = int(sum(blocks_for(c) for c in ctx))
+    nb = need if num_blocks is None else num_blocks
+    if free_list is None:
+        free_list = rng.permutation(nb)
+    mgr = BlockManager(nb, free_list=free_list)
+    slots = []
+    for s in range(S):
+        mgr.add_sequence(s)
+        sl, pairs = mgr.append_tokens(s, int(ctx[s]))
+        assert not pairs
+        slots.extend(sl)
+    tables = _tables_from(mgr, range(S))
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    tdt = TORCH_DTYPE[in_dt]
+    N = int(ctx.sum())
+    q = _randn(gen, (S, Hq, D), TORCH_DTYPE[q_dt], device)
+    k = _randn(gen, (N, Hkv, D), tdt, device)
+    v = _randn(gen, (N, Hkv, D), tdt, device)
+    slots = np.asarray(slots, dtype=np.int32)
+    k_scale = v_scale = 1.0
+    if fp8_scales:
+        k_scale = float((k.abs().max().float() / 448.0).item())
+        v_scale = float((v.abs().max().float() / 448.0).item())
+    last = np.cumsum(ctx.astype(np.int64)) - 1
+    lt = torch.as_tensor(last, device=device)
+    w = Workload(name=name, S=S, Hq=Hq, Hkv=Hkv, D=D, pool_dtype=pool_dt, q_dtype=q_dt,
+                 kv_in_dtype=in_dt, num_blocks=nb, context_lens=ctx, block_tables=tables,
+                 q=q, scale=scale, k_scale=k_scale, v_scale=v_scale,
+                 partition_tokens=partition_tokens, ops=[("write", k, v, slots)],
+                 step_k=k.index_select(0, lt), step_v=v.index_select(0, lt),
+                 step_slots=slots[last])
+    w.info["manager"] = mgr
+    return w
+
+
+def make_workload(name: str, small: bool = False, device="cpu", seed: int | None = None,
+                  num_seqs: int | None = None) -> Workload:
+    """Build one of the named workloads.  ``small`` keeps every per-sequence
+    shape but uses a few sequences, so the oracle finishes in seconds."""
+    if seed is None:
+        seed = SEEDS[name]
+    rng = np.random.default_rng(seed)
+    if name == "tiny":
+        table = rng.choice(64, 3, replace=False)
+        free = list(table) + [b for b in range(64) if b not in set(table.tolist())]
+        return _simple("tiny", 1, 1, 1, 64, [40], F32, F32, F32, 1.0 / 8.0, seed, device,
+                       rng, num_blocks=64, free_list=free)
+    if name == "mha13b":
+        S = num_seqs or (5 if small else 32)
+        ctx = rng.integers(1, 2049, size=S)
+        return _simple("mha13b", S, 40, 40, 128, ctx, BF16, BF16, BF16,
+                       _f32(1.0 / math.sqrt(128)), seed, device, rng)
+    if name == "gqa70b":
+        S = num_seqs or (3 if small else 256)
+        ctx = np.full(S, 4096)
+        return _simple("gqa70b", S, 64, 8, 128, ctx, BF16, BF16, BF16,
+                       _f32(1.0 / math.sqrt(128)), seed, device, rng)
+    if name == "fp8":
+        S = num_seqs or (5 if small else 128)
+        z = rng.standard_normal(S)
+        ctx = np.clip(np.rint(np.exp(math.log(2048.0) + 1.0 * z)), 16, 32768).astype(np.int64)
+        return _simple("fp8", S, 64, 8, 128, ctx, FP8, BF16, BF16, _f32(1.0 / math.sqrt(128)),
+                       seed, device, rng, partition_tokens=512, fp8_scales=True)
+    if name in ("sampling_a", "sampling_b"):
+        return _sampling(name, small, device, seed, rng, num_seqs)
+    raise KeyError(name)
+
+
+def _sampling(name, small, device, seed, rng, num_prompts=None) -> Workload:
+    P = num_prompts or (2 if small else 64)
+    n = 3
+    Hq, Hkv, D = 40, 8, 128
+    prompt = 1024 if name == "sampling_a" else 1016
+    cont = rng.integers(0, 513, size=(P, n))
+    # pool: prompt blocks + worst-case private blocks per sample (+1 copy each)
+    nb = P * blocks_for(prompt) + int(sum(blocks_for(prompt + c) + 1 for c in cont.ravel()))
+    mgr = BlockManager(nb, free_list=rng.permutation(nb))
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    ops = []
+    # 1. prompts, written once
+    pslots = []
+    for p in range(P):
+        mgr.add_sequence(("prompt", p))
+        sl, pairs = mgr.append_tokens(("prompt", p), prompt)
+        assert not pairs
+        pslots.extend(sl)
+    q = _randn(gen, (P * n, Hq, D), torch.bfloat16, device)
+    kp = _randn(gen, (P * prompt, Hkv, D), torch.bfloat16, device)
+    vp = _randn(gen, (P * prompt, Hkv, D), torch.bfloat16, device)
+    ops.append(("write", kp, vp, np.asarray(pslots, dtype=np.int32)))
+    shared_blocks = mgr.physical_blocks_in_use()
+    # 2. fork n samples per prompt; the prompt's own handle is then released
+    for p in range(P):
+        for j in range(n):
+            mgr.fork(("prompt", p), (p, j))
+        mgr.free_sequence(("prompt", p))
+    # 3. each sample appends its private tokens; first writers into a shared
+    #    partial block copy it (copy-on-write), in sample order
+    cslots, cow = [], []
+    for p in range(P):
+        for j in range(n):
+            sl, pairs = mgr.append_tokens((p, j), int(cont[p, j]))
+            cslots.extend(sl)
+            cow.extend(pairs)
+    if cow:
+        ops.append(("copy", np.asarray(cow, dtype=np.int32).reshape(-1, 2)))
+    Nc = len(cslots)
+    kc = _randn(gen, (Nc, Hkv, D), torch.bfloat16, device)
+    vc = _randn(gen, (Nc, Hkv, D), torch.bfloat16, device)
+    ops.append(("write", kc, vc, np.asarray(cslots, dtype=np.int32)))
+    seqs = [(p, j) for p in range(P) for j in range(n)]
+    ctx = np.asarray([mgr.length(s) for s in seqs], dtype=np.int32)
+    tables = _tables_from(mgr, seqs)
+    w = Workload(name=name, S=P * n, Hq=Hq, Hkv=Hkv, D=D, pool_dtype=BF16, q_dtype=BF16,
+                 kv_in_dtype=BF16, num_blocks=nb, context_lens=ctx, block_tables=tables, q=q,
+                 scale=_f32(1.0 / math.sqrt(D)), ops=ops)
+    w.info.update(manager=mgr, prompt_len=prompt, continuation=cont,
+                  shared_prompt_blocks=shared_blocks,
+                  physical_blocks=mgr.physical_blocks_in_use(),
+                  logical_blocks=mgr.logical_blocks(), cow_pairs=len(cow))
+    return w
+
+
+def raw_numpy(t: torch.Tensor) -> np.ndarray:
+    """The raw element bits of a CPU/GPU tensor as a numpy array (bf16 as uint16)."""
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
