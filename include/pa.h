@@ -1,0 +1,168 @@
+/*
+ * pa.h -- C ABI of the MI355X (gfx950) paged KV cache library (libpa.so).
+ *
+ * Three operations on a pool of fixed-size KV blocks, as the source pages
+ * state the problem:
+ *   - pa_reshape_and_cache: write new tokens' K/V into their slots
+ *     ("PagedAttention" glossary page (Ultralytics), how paging works, and the
+ *     French page's second article, "what is the KV cache": only the new
+ *     token's K and V are computed and appended to the cache; token `pos` of
+ *     a request lives at slot `pos % 16` of block `table[pos / 16]`).
+ *   - pa_copy_blocks: copy whole blocks before a sequence writes into a block
+ *     others still use (glossary page, sharing blocks between sequences:
+ *     copy-on-write; Russian page, "two answers to one request": only the
+ *     block that has to split is copied).
+ *   - pa_decode: single-query attention of every sequence over its context,
+ *     read block by block through its block table in logical order (glossary
+ *     page, how paging works; Russian page, logical order vs physical
+ *     placement), with query heads grouped over shared KV heads (glossary
+ *     page, related techniques: grouped-query attention).  The pages print no
+ *     formula; the operation is softmax(scale * q K^T) V over the ctx tokens.
+ *
+ * Conventions for every entry point
+ *   - Pointers are device pointers unless stated; the caller owns every
+ *     buffer and keeps it alive until the enqueued work completes.  The
+ *     library allocates no device memory and keeps no pointer after return.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
+ *     work on it and never synchronise the host.
+ *   - Return value: PA_OK (0) or a negative pa_status.  On error nothing is
+ *     enqueued and pa_last_error() describes the cause (thread-local).
+ *     Host-visible scalars and pointer alignment are checked; index data in
+ *     device memory (tables, slots, pairs, lengths) is not read by the host.
+ *     Kernels skip block ids outside [0, num_blocks) and clamp context lengths
+ *     to [0, max_blocks_per_seq * 16] instead of faulting.
+ *
+ * Pool layout (pa_pool_t.k_pool / v_pool, each num_blocks * num_kv_heads
+ * tiles of 16 * head_dim elements of kv_dtype).  Tile (b, g) -- block b,
+ * KV head g -- starts at element (b * num_kv_heads + g) * 16 * head_dim.
+ *   K tile: element (t, d) at ((d / X) * 16 + t) * X + d % X, X = 16 / elem_bytes
+ *           (each token's head vector in 16-byte runs, token-major per run).
+ *   V tile: element (t, d) at ((t / 4) * (D / W) + d / W) * 4W + (d % W) * 4 + t % 4,
+ *           W = 4 / elem_bytes (16-byte cells of 4 tokens x W dims, tokens fastest).
+ * Both orders make each 16-lane quarter of a wavefront load 256 contiguous
+ * bytes straight into matrix-core operand registers.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_BLOCK_SIZE 16
+
+typedef enum pa_dtype {
+    PA_F32 = 0,      /* IEEE binary32 */
+    PA_BF16 = 1,     /* bfloat16 */
+    PA_FP8_E4M3 = 2  /* OCP FP8 E4M3FN: bias 7, max 448, no infinities, NaN = S.1111.111 */
+} pa_dtype;
+
+typedef enum pa_status {
+    PA_OK = 0,
+    PA_ERR_NULL = -1,        /* a required pointer is NULL */
+    PA_ERR_DTYPE = -2,       /* unknown dtype or unsupported dtype pairing */
+    PA_ERR_SHAPE = -3,       /* negative/zero size, Hq % Hkv != 0, bad partition size */
+    PA_ERR_UNSUPPORTED = -4, /* block_size != 16 or head_dim not 64 / 128 */
+    PA_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required */
+    PA_ERR_ALIGN = -6,       /* a pointer is not 16-byte aligned */
+    PA_ERR_HIP = -7,         /* the HIP runtime reported an error */
+    PA_ERR_RANGE = -8        /* a scale is not finite and positive */
+} pa_status;
+
+/* The shared KV block pool.  k_scale / v_scale: per-pool dequantisation
+ * scales of an FP8 pool (stored code * scale = value); ignored (use 1) for
+ * 16/32-bit pools. */
+typedef struct pa_pool {
+    void *k_pool;
+    void *v_pool;
+    int32_t num_blocks;
+    int32_t num_kv_heads;
+    int32_t block_size; /* must be 16 */
+    int32_t head_dim;   /* 64 or 128 */
+    int32_t kv_dtype;   /* pa_dtype */
+    float k_scale;
+    float v_scale;
+} pa_pool_t;
+
+/* Bytes of ONE pool (K or V): num_blocks * num_kv_heads * 16 * head_dim * elem. */
+size_t pa_pool_bytes(const pa_pool_t *pool);
+
+/* Partition size (tokens, multiple of 16) that pa_decode uses for these
+ * arguments; `partition_tokens` = 0 asks for the library's choice.  Returns a
+ * negative pa_status on invalid arguments. */
+int32_t pa_decode_partition_tokens(const pa_pool_t *pool, int32_t num_seqs,
+                                   int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                   int32_t partition_tokens);
+
+/* Workspace bytes pa_decode needs for these arguments (0 when every context
+ * fits one partition).  Holds fp32 partial results of the split-K passes. */
+size_t pa_decode_workspace_size(const pa_pool_t *pool, int32_t num_seqs, int32_t num_q_heads,
+                                int32_t max_blocks_per_seq, int32_t partition_tokens);
+
+/*
+ * pa_decode -- paged single-query decode attention.
+ *   q              [num_seqs][num_q_heads][head_dim], q_dtype: PA_F32 with an
+ *                  fp32 pool, PA_BF16 with a bf16 or fp8 pool.
+ *   block_tables   int32 [num_seqs][max_blocks_per_seq]: physical block of each
+ *                  logical block; entries past ceil(ctx / 16) are never read.
+ *   context_lens   int32 [num_seqs]: tokens attended (0 gives a zero row).
+ *   scale          softmax scale applied to q . k.
+ *   out            fp32 [num_seqs][num_q_heads][head_dim].
+ *   partition_tokens  split-K partition length in tokens (multiple of 16),
+ *                  0 = library's choice.  Contexts longer than one partition
+ *                  are processed as independent partitions merged by a
+ *                  second kernel; the result does not depend on the split
+ *                  beyond fp32 rounding.
+ *   workspace      device buffer of >= pa_decode_workspace_size(...) bytes
+ *                  (may be NULL when that size is 0).
+ * Query head h attends with KV head h / (num_q_heads / num_kv_heads).
+ */
+int pa_decode(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t num_seqs,
+              int32_t num_q_heads, const int32_t *block_tables, int32_t max_blocks_per_seq,
+              const int32_t *context_lens, float scale, float *out, int32_t partition_tokens,
+              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * pa_reshape_and_cache -- write num_tokens new tokens into the pool.
+ *   k, v           [num_tokens][num_kv_heads][head_dim] of kv_dtype: the pool's
+ *                  dtype for 16/32-bit pools; PA_BF16 or PA_F32 for an FP8 pool.
+ *   slot_mapping   int32 [num_tokens]: slot = block * 16 + position in block;
+ *                  a negative slot skips the token.
+ * FP8 pools store the E4M3FN code nearest to fp32(x) * fp32(1 / scale)
+ * (round to nearest even, saturating to +-448); other pools store the input
+ * bits unchanged.  Slots must be distinct within one call.
+ */
+int pa_reshape_and_cache(const pa_pool_t *pool, const void *k, const void *v, int32_t kv_dtype,
+                         const int32_t *slot_mapping, int32_t num_tokens, void *stream);
+
+/*
+ * pa_copy_blocks -- copy-on-write block copy.
+ *   src_dst_pairs  int32 [num_pairs][2]: copy every KV head's K and V tile of
+ *                  block src over block dst.  Destinations must be distinct
+ *                  and none may also be a source.  num_pairs = 0 is a no-op.
+ */
+int pa_copy_blocks(const pa_pool_t *pool, const int32_t *src_dst_pairs, int32_t num_pairs,
+                   void *stream);
+
+/* Measurement aid: the next pa_decode call on this host thread records
+ * `before` (a hipEvent_t) just before its partition kernel and `after` just
+ * after it, on the call's stream.  Pass NULLs to clear. */
+int pa_set_profile_events(void *before, void *after);
+
+/* Static description of a status code. */
+const char *pa_strerror(int status);
+
+/* Description of the last error on this host thread ("" if none). */
+const char *pa_last_error(void);
+
+/* Build description: target architecture and kernel variants. */
+const char *pa_build_info(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

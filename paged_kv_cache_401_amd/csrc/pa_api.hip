@@ -1,0 +1,288 @@
+// pa_api.hip -- the C ABI declared in include/pa.h: argument checks,
+// partition and workspace sizing, kernel dispatch and error reporting.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+thread_local hipEvent_t g_ev_before = nullptr;
+thread_local hipEvent_t g_ev_after = nullptr;
+
+int fail(int status, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok() {
+    g_last_error[0] = '\0';
+    return PA_OK;
+}
+
+bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+int check_pool(const pa_pool_t *pool) {
+    if (!pool) return fail(PA_ERR_NULL, "pool descriptor is NULL");
+    if (!pool->k_pool || !pool->v_pool) return fail(PA_ERR_NULL, "k_pool or v_pool is NULL");
+    if (pool->kv_dtype < PA_F32 || pool->kv_dtype > PA_FP8_E4M3)
+        return fail(PA_ERR_DTYPE, "unknown kv_dtype %d", pool->kv_dtype);
+    if (pool->block_size != PA_BLOCK_SIZE)
+        return fail(PA_ERR_UNSUPPORTED, "block_size %d: only 16 is supported", pool->block_size);
+    if (pool->head_dim != 64 && pool->head_dim != 128)
+        return fail(PA_ERR_UNSUPPORTED, "head_dim %d: only 64 and 128 are supported", pool->head_dim);
+    if (pool->num_blocks <= 0 || pool->num_kv_heads <= 0)
+        return fail(PA_ERR_SHAPE, "num_blocks %d and num_kv_heads %d must be positive",
+                    pool->num_blocks, pool->num_kv_heads);
+    if (!aligned16(pool->k_pool) || !aligned16(pool->v_pool))
+        return fail(PA_ERR_ALIGN, "k_pool and v_pool must be 16-byte aligned");
+    if (pool->kv_dtype == PA_FP8_E4M3) {
+        if (!(isfinite(pool->k_scale) && pool->k_scale > 0.f && isfinite(pool->v_scale) &&
+              pool->v_scale > 0.f))
+            return fail(PA_ERR_RANGE, "fp8 pool scales must be finite and positive (k %g, v %g)",
+                        (double)pool->k_scale, (double)pool->v_scale);
+        if (!isfinite(1.0f / pool->k_scale) || !isfinite(1.0f / pool->v_scale))
+            return fail(PA_ERR_RANGE, "fp8 pool scale too small to invert in fp32");
+    }
+    return PA_OK;
+}
+
+int64_t tile_bytes(const pa_pool_t *pool) {
+    return (int64_t)PA_BLOCK_SIZE * pool->head_dim * pa::elem_bytes(pool->kv_dtype);
+}
+
+// Library's partition size: keep at least ~8 workgroups per compute unit in
+// flight (256 CUs), never below 256 tokens, and prefer long partitions
+// otherwise (each split costs a partial-result write and read).
+int32_t auto_partition(const pa_pool_t *pool, int32_t num_seqs, int32_t num_q_heads,
+                       int32_t max_blocks_per_seq) {
+    const bool mfma = pa::mfma_path_supported(pool->kv_dtype, pool->head_dim,
+                                              num_q_heads / pool->num_kv_heads);
+    const int64_t rows = (int64_t)num_seqs * (mfma ? pool->num_kv_heads : num_q_heads);
+    const int64_t max_tokens = (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE;
+    const int64_t target = 256 * 8;
+    int64_t ptok = 256;
+    while (ptok < max_tokens && rows * ((max_tokens + 2 * ptok - 1) / (2 * ptok)) >= target)
+        ptok *= 2;
+    if (ptok > max_tokens) ptok = ((max_tokens + 15) / 16) * 16;
+    return (int32_t)(ptok < 16 ? 16 : ptok);
+}
+
+int resolve_partition(const pa_pool_t *pool, int32_t num_seqs, int32_t num_q_heads,
+                      int32_t max_blocks_per_seq, int32_t partition_tokens, int32_t *out) {
+    if (partition_tokens < 0 || partition_tokens % PA_BLOCK_SIZE != 0)
+        return fail(PA_ERR_SHAPE, "partition_tokens %d must be 0 or a positive multiple of 16",
+                    partition_tokens);
+    *out = partition_tokens ? partition_tokens
+                            : auto_partition(pool, num_seqs, num_q_heads, max_blocks_per_seq);
+    return PA_OK;
+}
+
+int check_heads(const pa_pool_t *pool, int32_t num_seqs, int32_t num_q_heads,
+                int32_t max_blocks_per_seq) {
+    if (num_seqs < 0) return fail(PA_ERR_SHAPE, "num_seqs %d is negative", num_seqs);
+    if (num_q_heads <= 0 || num_q_heads % pool->num_kv_heads != 0)
+        return fail(PA_ERR_SHAPE, "num_q_heads %d must be a positive multiple of num_kv_heads %d",
+                    num_q_heads, pool->num_kv_heads);
+    if (max_blocks_per_seq <= 0 || max_blocks_per_seq > (1 << 26))
+        return fail(PA_ERR_SHAPE, "max_blocks_per_seq %d out of range", max_blocks_per_seq);
+    return PA_OK;
+}
+
+size_t workspace_for(const pa_pool_t *pool, int32_t num_seqs, int32_t num_q_heads,
+                     int32_t max_blocks_per_seq, int32_t ptok, int32_t *nparts_out) {
+    const int64_t max_tokens = (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE;
+    const int64_t np = (max_tokens + ptok - 1) / ptok;
+    if (nparts_out) *nparts_out = (int32_t)np;
+    if (np <= 1) return 0;
+    const int64_t rows = (int64_t)num_seqs * num_q_heads * np;
+    // acc [rows][D] then m [rows] then l [rows], each region 256-byte aligned
+    const int64_t acc = ((rows * pool->head_dim * 4 + 255) / 256) * 256;
+    const int64_t ml = ((rows * 4 + 255) / 256) * 256;
+    return (size_t)(acc + 2 * ml);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pa_pool_bytes(const pa_pool_t *pool) {
+    if (check_pool(pool) != PA_OK) return 0;
+    return (size_t)pool->num_blocks * pool->num_kv_heads * (size_t)tile_bytes(pool);
+}
+
+int32_t pa_decode_partition_tokens(const pa_pool_t *pool, int32_t num_seqs, int32_t num_q_heads,
+                                   int32_t max_blocks_per_seq, int32_t partition_tokens) {
+    int rc = check_pool(pool);
+    if (rc == PA_OK) rc = check_heads(pool, num_seqs, num_q_heads, max_blocks_per_seq);
+    if (rc != PA_OK) return rc;
+    int32_t ptok = 0;
+    rc = resolve_partition(pool, num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens, &ptok);
+    return rc == PA_OK ? ptok : rc;
+}
+
+size_t pa_decode_workspace_size(const pa_pool_t *pool, int32_t num_seqs, int32_t num_q_heads,
+                                int32_t max_blocks_per_seq, int32_t partition_tokens) {
+    const int32_t ptok = pa_decode_partition_tokens(pool, num_seqs, num_q_heads,
+                                                    max_blocks_per_seq, partition_tokens);
+    if (ptok <= 0) return 0;
+    return workspace_for(pool, num_seqs, num_q_heads, max_blocks_per_seq, ptok, nullptr);
+}
+
+int pa_decode(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t num_seqs,
+              int32_t num_q_heads, const int32_t *block_tables, int32_t max_blocks_per_seq,
+              const int32_t *context_lens, float scale, float *out, int32_t partition_tokens,
+              void *workspace, size_t workspace_bytes, void *stream) {
+    int rc = check_pool(pool);
+    if (rc != PA_OK) return rc;
+    rc = check_heads(pool, num_seqs, num_q_heads, max_blocks_per_seq);
+    if (rc != PA_OK) return rc;
+    const int want_q = pool->kv_dtype == PA_F32 ? PA_F32 : PA_BF16;
+    if (q_dtype != want_q)
+        return fail(PA_ERR_DTYPE, "q_dtype %d does not match a kv_dtype %d pool (needs %d)", q_dtype,
+                    pool->kv_dtype, want_q);
+    if (!isfinite(scale)) return fail(PA_ERR_RANGE, "scale is not finite");
+    int32_t ptok = 0;
+    rc = resolve_partition(pool, num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens, &ptok);
+    if (rc != PA_OK) return rc;
+    if (num_seqs == 0) return ok();
+    if (!q || !block_tables || !context_lens || !out)
+        return fail(PA_ERR_NULL, "q, block_tables, context_lens and out must be non-NULL");
+    if (!aligned16(q)) return fail(PA_ERR_ALIGN, "q must be 16-byte aligned");
+    int32_t np = 1;
+    const size_t need = workspace_for(pool, num_seqs, num_q_heads, max_blocks_per_seq, ptok, &np);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (need > 0 && !aligned16(workspace)) return fail(PA_ERR_ALIGN, "workspace must be 16-byte aligned");
+
+    pa::DecodeParams p{};
+    p.k_pool = pool->k_pool;
+    p.v_pool = pool->v_pool;
+    p.q = q;
+    p.out = out;
+    p.block_tables = block_tables;
+    p.context_lens = context_lens;
+    p.num_blocks = pool->num_blocks;
+    p.num_kv_heads = pool->num_kv_heads;
+    p.num_q_heads = num_q_heads;
+    p.group = num_q_heads / pool->num_kv_heads;
+    p.num_seqs = num_seqs;
+    p.max_blocks_per_seq = max_blocks_per_seq;
+    p.partition_tokens = ptok;
+    p.max_partitions = np;
+    const double kscale = pool->kv_dtype == PA_FP8_E4M3 ? (double)pool->k_scale : 1.0;
+    p.qk_scale_log2 = (float)((double)scale * kscale * 1.4426950408889634);
+    p.out_scale = pool->kv_dtype == PA_FP8_E4M3 ? pool->v_scale : 1.0f;
+    if (need > 0) {
+        const int64_t rows = (int64_t)num_seqs * num_q_heads * np;
+        char *ws = static_cast<char *>(workspace);
+        const int64_t acc = ((rows * pool->head_dim * 4 + 255) / 256) * 256;
+        const int64_t ml = ((rows * 4 + 255) / 256) * 256;
+        p.ws_acc = reinterpret_cast<float *>(ws);
+        p.ws_m = reinterpret_cast<float *>(ws + acc);
+        p.ws_l = reinterpret_cast<float *>(ws + acc + ml);
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const bool mfma = pa::mfma_path_supported(pool->kv_dtype, pool->head_dim, p.group);
+    if (g_ev_before) {
+        hipError_t e = hipEventRecord(g_ev_before, st);
+        if (e != hipSuccess) return fail(PA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+    }
+    hipError_t e = mfma ? pa::launch_decode_mfma(pool->kv_dtype, pool->head_dim, p, st)
+                        : pa::launch_decode_valu(pool->kv_dtype, pool->head_dim, p, st);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "decode partition kernel: %s", hipGetErrorString(e));
+    if (g_ev_after) {
+        e = hipEventRecord(g_ev_after, st);
+        if (e != hipSuccess) return fail(PA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+    }
+    g_ev_before = g_ev_after = nullptr;
+    if (np > 1) {
+        e = pa::launch_decode_reduce(pool->head_dim, p, st);
+        if (e != hipSuccess) return fail(PA_ERR_HIP, "decode reduce kernel: %s", hipGetErrorString(e));
+    }
+    return ok();
+}
+
+int pa_reshape_and_cache(const pa_pool_t *pool, const void *k, const void *v, int32_t kv_dtype,
+                         const int32_t *slot_mapping, int32_t num_tokens, void *stream) {
+    int rc = check_pool(pool);
+    if (rc != PA_OK) return rc;
+    const bool dtype_ok = pool->kv_dtype == PA_FP8_E4M3
+                              ? (kv_dtype == PA_BF16 || kv_dtype == PA_F32)
+                              : kv_dtype == pool->kv_dtype;
+    if (!dtype_ok)
+        return fail(PA_ERR_DTYPE, "input dtype %d cannot be written to a kv_dtype %d pool", kv_dtype,
+                    pool->kv_dtype);
+    if (num_tokens < 0) return fail(PA_ERR_SHAPE, "num_tokens %d is negative", num_tokens);
+    if (num_tokens == 0) return ok();
+    if (!k || !v || !slot_mapping) return fail(PA_ERR_NULL, "k, v and slot_mapping must be non-NULL");
+    pa::CacheParams p{};
+    p.k_pool = pool->k_pool;
+    p.v_pool = pool->v_pool;
+    p.k = k;
+    p.v = v;
+    p.slot_mapping = slot_mapping;
+    p.num_tokens = num_tokens;
+    p.num_blocks = pool->num_blocks;
+    p.num_kv_heads = pool->num_kv_heads;
+    p.inv_k_scale = pool->kv_dtype == PA_FP8_E4M3 ? 1.0f / pool->k_scale : 1.0f;
+    p.inv_v_scale = pool->kv_dtype == PA_FP8_E4M3 ? 1.0f / pool->v_scale : 1.0f;
+    hipError_t e = pa::launch_reshape_and_cache(pool->kv_dtype, kv_dtype, pool->head_dim, p,
+                                                static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "reshape_and_cache kernel: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int pa_copy_blocks(const pa_pool_t *pool, const int32_t *src_dst_pairs, int32_t num_pairs,
+                   void *stream) {
+    int rc = check_pool(pool);
+    if (rc != PA_OK) return rc;
+    if (num_pairs < 0) return fail(PA_ERR_SHAPE, "num_pairs %d is negative", num_pairs);
+    if (num_pairs == 0) return ok();
+    if (!src_dst_pairs) return fail(PA_ERR_NULL, "src_dst_pairs is NULL");
+    hipError_t e = pa::launch_copy_blocks(pool->k_pool, pool->v_pool, src_dst_pairs, num_pairs,
+                                          pool->num_blocks, pool->num_kv_heads * tile_bytes(pool),
+                                          static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "copy_blocks kernel: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int pa_set_profile_events(void *before, void *after) {
+    if ((before == nullptr) != (after == nullptr))
+        return fail(PA_ERR_NULL, "pass both events or neither");
+    g_ev_before = static_cast<hipEvent_t>(before);
+    g_ev_after = static_cast<hipEvent_t>(after);
+    return ok();
+}
+
+const char *pa_strerror(int status) {
+    switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "required pointer is NULL";
+    case PA_ERR_DTYPE: return "unsupported dtype or dtype pairing";
+    case PA_ERR_SHAPE: return "invalid shape";
+    case PA_ERR_UNSUPPORTED: return "unsupported block size or head dim";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case PA_ERR_HIP: return "HIP runtime error";
+    case PA_ERR_RANGE: return "scale out of range";
+    default: return "unknown status";
+    }
+}
+
+const char *pa_last_error(void) { return g_last_error; }
+
+const char *pa_build_info(void) {
+    return "libpa gfx950: decode (vector-ALU partition kernel, matrix-core GQA kernel, split-K "
+           "reduce), reshape_and_cache (fp32/bf16/fp8-e4m3), copy_blocks";
+}
+
+}  // extern "C"

@@ -1,0 +1,61 @@
+// pa_internal.h -- launch interfaces shared by the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+enum KvType : int { kF32 = 0, kBF16 = 1, kFP8 = 2 };
+
+constexpr int kBlock = 16;       // tokens per block
+constexpr int kThreads = 256;    // threads per workgroup of every kernel (4 wavefronts)
+
+inline int elem_bytes(int kv) { return kv == kF32 ? 4 : (kv == kBF16 ? 2 : 1); }
+
+struct DecodeParams {
+    const void *k_pool;
+    const void *v_pool;
+    const void *q;             // [S][Hq][D], fp32 for an fp32 pool, bf16 otherwise
+    float *out;                // [S][Hq][D]
+    const int32_t *block_tables;
+    const int32_t *context_lens;
+    float *ws_acc;             // [S][Hq][NP][D] partial numerators
+    float *ws_m;               // [S][Hq][NP]   partial maxima (log2 domain)
+    float *ws_l;               // [S][Hq][NP]   partial denominators
+    int32_t num_blocks;
+    int32_t num_kv_heads;
+    int32_t num_q_heads;
+    int32_t group;             // Hq / Hkv
+    int32_t num_seqs;
+    int32_t max_blocks_per_seq;
+    int32_t partition_tokens;  // multiple of 16
+    int32_t max_partitions;    // ceil(max_blocks_per_seq * 16 / partition_tokens)
+    float qk_scale_log2;       // scale * k_scale * log2(e)
+    float out_scale;           // v_scale (1 for 16/32-bit pools)
+};
+
+struct CacheParams {
+    void *k_pool;
+    void *v_pool;
+    const void *k;
+    const void *v;
+    const int32_t *slot_mapping;
+    int64_t num_tokens;
+    int32_t num_blocks;
+    int32_t num_kv_heads;
+    float inv_k_scale;         // fp32(1 / k_scale), fp8 pools only
+    float inv_v_scale;
+};
+
+// Each launcher enqueues on `stream` and returns the launch status.
+hipError_t launch_decode_valu(int kv, int head_dim, const DecodeParams &p, hipStream_t stream);
+hipError_t launch_decode_mfma(int kv, int head_dim, const DecodeParams &p, hipStream_t stream);
+bool mfma_path_supported(int kv, int head_dim, int group);
+hipError_t launch_decode_reduce(int head_dim, const DecodeParams &p, hipStream_t stream);
+hipError_t launch_reshape_and_cache(int pool_kv, int in_kv, int head_dim, const CacheParams &p,
+                                    hipStream_t stream);
+hipError_t launch_copy_blocks(void *k_pool, void *v_pool, const int32_t *pairs, int32_t num_pairs,
+                              int32_t num_blocks, int64_t block_bytes, hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,202 @@
+"""Python binding of libpa.so (the C ABI in include/pa.h).
+
+Argument marshalling only: torch tensors supply device memory and the current
+HIP stream; every computation runs in the library's HIP kernels.  There is no
+fallback: if libpa.so is missing or a call fails, an exception is raised.
+
+torch is imported before the library is loaded so that libpa.so binds to the
+HIP runtime torch already holds (one runtime per process).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+F32, BF16, FP8 = 0, 1, 2
+ELEM_BYTES = {F32: 4, BF16: 2, FP8: 1}
+BLOCK_SIZE = 16
+TORCH_TO_PA = {torch.float32: F32, torch.bfloat16: BF16}
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
+
+# every symbol include/pa.h declares
+EXPORTS = ("pa_pool_bytes", "pa_decode_partition_tokens", "pa_decode_workspace_size", "pa_decode",
+           "pa_reshape_and_cache", "pa_copy_blocks", "pa_set_profile_events", "pa_strerror",
+           "pa_last_error", "pa_build_info")
+
+
+class PAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("libpa error %d: %s" % (status, message))
+        self.status = status
+
+
+class PoolDesc(ctypes.Structure):
+    _fields_ = [("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
+                ("num_blocks", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("kv_dtype", ctypes.c_int32), ("k_scale", ctypes.c_float),
+                ("v_scale", ctypes.c_float)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libpa.so (built by ``__graft_entry__.build()``); raise if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise PAError(-7, "%s is not built; run __graft_entry__.build()" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+    PD = ctypes.POINTER(PoolDesc)
+    L.pa_pool_bytes.argtypes = [PD]
+    L.pa_pool_bytes.restype = SZ
+    L.pa_decode_partition_tokens.argtypes = [PD, I32, I32, I32, I32]
+    L.pa_decode_partition_tokens.restype = I32
+    L.pa_decode_workspace_size.argtypes = [PD, I32, I32, I32, I32]
+    L.pa_decode_workspace_size.restype = SZ
+    L.pa_decode.argtypes = [PD, P, I32, I32, I32, P, I32, P, F, P, I32, P, SZ, P]
+    L.pa_decode.restype = ctypes.c_int
+    L.pa_reshape_and_cache.argtypes = [PD, P, P, I32, P, I32, P]
+    L.pa_reshape_and_cache.restype = ctypes.c_int
+    L.pa_copy_blocks.argtypes = [PD, P, I32, P]
+    L.pa_copy_blocks.restype = ctypes.c_int
+    L.pa_set_profile_events.argtypes = [P, P]
+    L.pa_set_profile_events.restype = ctypes.c_int
+    L.pa_strerror.argtypes = [ctypes.c_int]
+    L.pa_strerror.restype = ctypes.c_char_p
+    L.pa_last_error.argtypes = []
+    L.pa_last_error.restype = ctypes.c_char_p
+    L.pa_build_info.argtypes = []
+    L.pa_build_info.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise PAError(rc, lib().pa_last_error().decode())
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    return t.data_ptr()
+
+
+class KVPool:
+    """Device K and V pools: num_blocks x num_kv_heads tiles of 16 x head_dim
+    elements of ``dtype`` each, held as raw byte tensors."""
+
+    def __init__(self, num_blocks: int, num_kv_heads: int, head_dim: int, dtype: int,
+                 device="cuda", k_scale: float = 1.0, v_scale: float = 1.0, fill: int | None = None):
+        self.num_blocks, self.num_kv_heads, self.head_dim, self.dtype = (
+            int(num_blocks), int(num_kv_heads), int(head_dim), int(dtype))
+        self.k_scale, self.v_scale = float(k_scale), float(v_scale)
+        nbytes = self.num_blocks * self.num_kv_heads * BLOCK_SIZE * self.head_dim * ELEM_BYTES[dtype]
+        alloc = torch.empty if fill is None else (lambda n, **kw: torch.full((n,), fill, **kw))
+        self.k = alloc(nbytes, dtype=torch.uint8, device=device)
+        self.v = alloc(nbytes, dtype=torch.uint8, device=device)
+        got = lib().pa_pool_bytes(ctypes.byref(self.desc()))
+        if got != nbytes:
+            raise PAError(-3, "pool descriptor rejected: %s" % lib().pa_last_error().decode())
+
+    def desc(self) -> PoolDesc:
+        return PoolDesc(self.k.data_ptr(), self.v.data_ptr(), self.num_blocks, self.num_kv_heads,
+                        BLOCK_SIZE, self.head_dim, self.dtype, self.k_scale, self.v_scale)
+
+    @property
+    def nbytes(self) -> int:
+        return self.k.numel()
+
+
+def reshape_and_cache(pool: KVPool, k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
+                      stream=None) -> None:
+    n = slot_mapping.numel()
+    if k.shape != (n, pool.num_kv_heads, pool.head_dim) or v.shape != k.shape:
+        raise ValueError("k/v must be [num_tokens][num_kv_heads][head_dim]")
+    if k.dtype != v.dtype or k.dtype not in TORCH_TO_PA:
+        raise TypeError("k/v must both be float32 or bfloat16")
+    d = pool.desc()
+    _check(lib().pa_reshape_and_cache(ctypes.byref(d), _dev(k, "k"), _dev(v, "v"),
+                                      TORCH_TO_PA[k.dtype], _dev(slot_mapping, "slot_mapping",
+                                                                 torch.int32), n, _stream(stream)))
+
+
+def copy_blocks(pool: KVPool, pairs: torch.Tensor, stream=None) -> None:
+    n = pairs.numel() // 2
+    ptr = _dev(pairs, "pairs", torch.int32) if n else None
+    d = pool.desc()
+    _check(lib().pa_copy_blocks(ctypes.byref(d), ptr, n, _stream(stream)))
+
+
+def decode_partition_tokens(pool: KVPool, num_seqs, num_q_heads, max_blocks_per_seq,
+                            partition_tokens=0) -> int:
+    d = pool.desc()
+    r = lib().pa_decode_partition_tokens(ctypes.byref(d), num_seqs, num_q_heads,
+                                         max_blocks_per_seq, partition_tokens)
+    if r < 0:
+        raise PAError(r, lib().pa_last_error().decode())
+    return r
+
+
+def decode_workspace_size(pool: KVPool, num_seqs, num_q_heads, max_blocks_per_seq,
+                          partition_tokens=0) -> int:
+    decode_partition_tokens(pool, num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens)
+    d = pool.desc()
+    return int(lib().pa_decode_workspace_size(ctypes.byref(d), num_seqs, num_q_heads,
+                                              max_blocks_per_seq, partition_tokens))
+
+
+def decode(pool: KVPool, q: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+           scale: float, out: torch.Tensor | None = None, partition_tokens: int = 0,
+           workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    S, Hq, D = q.shape
+    if D != pool.head_dim:
+        raise ValueError("q head dim %d differs from the pool's %d" % (D, pool.head_dim))
+    if q.dtype not in TORCH_TO_PA:
+        raise TypeError("q must be float32 or bfloat16")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.numel() != S:
+        raise ValueError("block_tables must be [num_seqs][max_blocks]; context_lens [num_seqs]")
+    mbs = block_tables.shape[1]
+    if out is None:
+        out = torch.empty((S, Hq, D), dtype=torch.float32, device=q.device)
+    need = decode_workspace_size(pool, S, Hq, mbs, partition_tokens)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wptr = workspace.data_ptr() if workspace is not None else None
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    d = pool.desc()
+    _check(lib().pa_decode(ctypes.byref(d), _dev(q, "q"), TORCH_TO_PA[q.dtype], S, Hq,
+                           _dev(block_tables, "block_tables", torch.int32), mbs,
+                           _dev(context_lens, "context_lens", torch.int32), float(scale),
+                           _dev(out, "out", torch.float32), int(partition_tokens), wptr, wbytes,
+                           _stream(stream)))
+    return out
+
+
+def set_profile_events(before, after) -> None:
+    """Record torch.cuda.Event ``before``/``after`` around the next decode's
+    partition kernel (pass None, None to clear)."""
+    b = before.cuda_event if before is not None else None
+    a = after.cuda_event if after is not None else None
+    _check(lib().pa_set_profile_events(b, a))
+
+
+def build_info() -> str:
+    return lib().pa_build_info().decode()

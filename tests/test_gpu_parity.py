@@ -1,0 +1,291 @@
+"""GPU parity: the HIP library through its C ABI against the fp64 CPU oracle.
+
+Bit-exact: pool bytes after cache writes and block copies (with a NaN
+sentinel in every untouched byte), block-table indexing (one-hot probes), and
+invariants (block relabelling, shared vs private prefixes, poisoned tails,
+run-to-run determinism).  Attention outputs: max abs error 2e-3 (bf16/fp32
+inputs) or 3e-2 (fp8 cache) against the oracle.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import gpu_decode, gpu_pool, tolerance
+from oracle_helpers import oracle_decode, oracle_pools
+from paged_kv_cache_401_amd import ops
+from paged_kv_cache_401_amd import workloads as wl
+from paged_kv_cache_401_amd.blocks import BlockManager, blocks_for
+from paged_kv_cache_401_amd.workloads import raw_numpy
+
+pytestmark = pytest.mark.gpu
+
+SMALL = ["tiny", "mha13b", "gqa70b", "sampling_a", "sampling_b", "fp8"]
+
+
+def _pool_bytes(pool):
+    torch.cuda.synchronize()
+    return pool.k.cpu().numpy(), pool.v.cpu().numpy()
+
+
+# ------------------------------------------------------------- cache kernels
+@pytest.mark.parametrize("name", SMALL)
+def test_cache_write_and_copy_bit_exact(name):
+    w = wl.make_workload(name, small=True)
+    kp, vp = oracle_pools(w, fill=0xFF)
+    gk, gv = _pool_bytes(gpu_pool(w, fill=0xFF))
+    assert np.array_equal(gk, kp), "K pool bytes differ"
+    assert np.array_equal(gv, vp), "V pool bytes differ"
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.37])
+def test_fp8_encoder_bit_exact_over_dense_fp32_sweep(scale):
+    """Every fp32 pattern of the form (hi 24 bits, random low 8 bits) plus the
+    rounding midpoints, infinities, NaN and signed zero, through the fp8 cache
+    write: pool bytes equal the oracle's table-search encoder."""
+    rng = np.random.default_rng(5)
+    hi = np.arange(1 << 24, dtype=np.uint32) << np.uint32(8)
+    lo = rng.integers(0, 256, 1 << 24, dtype=np.uint32)
+    vals = oracle.fp8_decode(np.arange(127, dtype=np.uint8))
+    mids = ((vals[1:] + vals[:-1]) / 2).astype(np.float32).view(np.uint32)
+    extra = np.concatenate([mids, mids - 1, mids + 1, mids | 0x80000000,
+                            np.array([0x7f800000, 0xff800000, 0x7fc00000, 0x80000000, 0],
+                                     np.uint32)])
+    bits = np.concatenate([hi | lo, extra]).astype(np.uint32)
+    D, Hkv = 128, 1
+    n_tok = -(-bits.size // D)
+    bits = np.concatenate([bits, np.zeros(n_tok * D - bits.size, np.uint32)])
+    x = bits.view(np.float32).reshape(n_tok, Hkv, D)
+    nb = blocks_for(n_tok)
+    slots = np.arange(n_tok, dtype=np.int32)
+    kp = oracle.new_pool(nb, Hkv, D, oracle.FP8, fill=0xFF)
+    vp = oracle.new_pool(nb, Hkv, D, oracle.FP8, fill=0xFF)
+    oracle.reshape_and_cache(kp, vp, oracle.FP8, nb, Hkv, D, x, x, oracle.F32, slots, scale, scale)
+    pool = ops.KVPool(nb, Hkv, D, ops.FP8, k_scale=scale, v_scale=scale, fill=0xFF)
+    xt = torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    ops.reshape_and_cache(pool, xt, xt, torch.from_numpy(slots).cuda())
+    gk, gv = _pool_bytes(pool)
+    assert np.array_equal(gk, kp) and np.array_equal(gv, vp)
+
+
+# ---------------------------------------------------------------- attention
+@pytest.mark.parametrize("name", SMALL)
+def test_decode_matches_oracle(name):
+    w = wl.make_workload(name, small=True)
+    kp, vp = oracle_pools(w)
+    ref = oracle_decode(w, kp, vp)
+    out = gpu_decode(w, gpu_pool(w))
+    err = float(np.max(np.abs(out - ref)))
+    print("%s: max abs err %.3e (tol %.0e)" % (name, err, tolerance(w)))
+    assert err <= tolerance(w)
+
+
+_ORACLE_CACHE = {}
+
+
+def _small_with_oracle(name):
+    if name not in _ORACLE_CACHE:
+        w = wl.make_workload(name, small=True)
+        kp, vp = oracle_pools(w)
+        _ORACLE_CACHE[name] = (w, oracle_decode(w, kp, vp))
+    return _ORACLE_CACHE[name]
+
+
+@pytest.mark.parametrize("name", ["mha13b", "gqa70b", "sampling_b", "fp8"])
+@pytest.mark.parametrize("ptok", [16, 48, 256, 512, 1024, 4096])
+def test_decode_any_partition_size(name, ptok):
+    w, ref = _small_with_oracle(name)
+    out = gpu_decode(w, gpu_pool(w), partition_tokens=ptok)
+    assert float(np.max(np.abs(out - ref))) <= tolerance(w)
+
+
+def _one_hot(S, Hq, Hkv, D, ctx, pool_dt, targets, seed=0):
+    """K is zero except K[target_s][:, 0] = c; q = e_0; so the output of every
+    head is exactly that token's V row (times v_scale)."""
+    rng = np.random.default_rng(seed)
+    in_dt = oracle.F32 if pool_dt == oracle.F32 else oracle.BF16
+    w = wl._simple("one_hot", S, Hq, Hkv, D, ctx, pool_dt, in_dt, in_dt, 0.5, seed, "cpu", rng)
+    _, k, v, slots = w.ops[0]
+    c = 448.0 if pool_dt == oracle.FP8 else 1000.0
+    k = torch.zeros_like(k)
+    off = np.concatenate([[0], np.cumsum(w.context_lens)[:-1]])
+    for s in range(S):
+        k[off[s] + targets[s], :, 0] = c
+    q = torch.zeros_like(w.q)
+    q[:, :, 0] = 1.0
+    w.ops = [("write", k, v, slots)]
+    w.q = q
+    w.k_scale = w.v_scale = 1.0
+    vals = [v[off[s] + targets[s]] for s in range(S)]
+    return w, vals
+
+
+ONE_HOT_CASES = {
+    "fp32_mha_d64": (3, 1, 1, 64, oracle.F32),
+    "bf16_mha": (4, 8, 8, 128, oracle.BF16),
+    "bf16_gqa8": (4, 64, 8, 128, oracle.BF16),
+    "bf16_gqa5": (4, 40, 8, 128, oracle.BF16),
+    "bf16_gqa8_d64": (4, 16, 2, 64, oracle.BF16),
+    "fp8_gqa8": (4, 64, 8, 128, oracle.FP8),
+    "fp8_mha": (4, 4, 4, 128, oracle.FP8),
+}
+
+
+@pytest.mark.parametrize("case", sorted(ONE_HOT_CASES))
+@pytest.mark.parametrize("ptok", [0, 16, 512])
+def test_one_hot_probe_is_bit_exact(case, ptok):
+    """Block-table indexing, bit for bit, through every path including split-K:
+    targets at the first token, the last token, partition edges and random."""
+    S, Hq, Hkv, D, dt = ONE_HOT_CASES[case]
+    ctx = [1, 1037, 4096, 700][:S]
+    rng = np.random.default_rng(1)
+    for targets in ([0] * S, [n - 1 for n in ctx], [min(n - 1, 511) for n in ctx],
+                    [min(n - 1, 512) for n in ctx], [int(rng.integers(0, n)) for n in ctx]):
+        w, vals = _one_hot(S, Hq, Hkv, D, ctx, dt, targets)
+        out = gpu_decode(w, gpu_pool(w, fill=0xFF), partition_tokens=ptok)
+        for s in range(S):
+            v = vals[s].float().numpy().astype(np.float64)  # [Hkv][D]
+            if dt == oracle.FP8:
+                codes = oracle.fp8_encode(v.astype(np.float32))
+                v = oracle.fp8_decode(codes.ravel()).reshape(v.shape)
+            for h in range(Hq):
+                assert np.array_equal(out[s, h], v[h // (Hq // Hkv)]), (case, s, h, targets[s])
+
+
+def test_fp8_decode_all_codes_through_attention():
+    """A one-hot probe on tokens whose V rows hold all 256 E4M3FN codes: the
+    output is each code's value (NaN where the code is NaN)."""
+    D = 128
+    codes = np.arange(256, dtype=np.uint8).reshape(2, D)
+    vals = oracle.fp8_decode(codes.ravel()).reshape(2, D)
+    for tgt in (0, 1):
+        w, _ = _one_hot(1, 1, 1, D, [2], oracle.FP8, [tgt])
+        _, k, v, slots = w.ops[0]
+        v = torch.from_numpy(vals.astype(np.float32)).reshape(2, 1, D).to(torch.bfloat16)
+        w.ops = [("write", k, v, slots)]
+        out = gpu_decode(w, gpu_pool(w))
+        want = vals[tgt]
+        assert np.array_equal(np.isnan(out[0, 0]), np.isnan(want))
+        ok = ~np.isnan(want)
+        assert np.array_equal(out[0, 0][ok], want[ok])
+
+
+# --------------------------------------------------------------- invariants
+def test_block_relabelling_is_bit_exact():
+    w = wl.make_workload("gqa70b", small=True)
+    ref = gpu_decode(w, gpu_pool(w))
+    perm = np.random.default_rng(11).permutation(w.num_blocks).astype(np.int32)
+    _, k, v, slots = w.ops[0]
+    w2 = wl.make_workload("gqa70b", small=True)
+    w2.ops = [("write", k, v, (perm[slots // 16] * 16 + slots % 16).astype(np.int32))]
+    tables = np.where(w.block_tables >= 0, perm[np.maximum(w.block_tables, 0)], -1)
+    out = gpu_decode(w2, gpu_pool(w2), tables=tables.astype(np.int32))
+    assert out.tobytes() == ref.tobytes()
+
+
+@pytest.mark.parametrize("name", ["sampling_a", "sampling_b"])
+def test_shared_prefix_equals_private_copies_on_gpu(name):
+    w = wl.make_workload(name, small=True)
+    shared = gpu_decode(w, gpu_pool(w))
+    kp, vp = oracle_pools(w)
+    ref = oracle_decode(w, kp, vp)
+    assert float(np.max(np.abs(shared - ref))) <= tolerance(w)
+    # private copies: every sequence's logical tokens written to its own blocks
+    import test_oracle_pins as pins
+    logical = pins._logical_tokens(w)
+    mgr = BlockManager(sum(blocks_for(n) for n in w.context_lens))
+    ks, vs, slots = [], [], []
+    for s in range(w.S):
+        mgr.add_sequence(s)
+        sl, _ = mgr.append_tokens(s, int(w.context_lens[s]))
+        slots += sl
+        ks.append(logical[s][0])
+        vs.append(logical[s][1])
+    wp = wl.make_workload(name, small=True)
+    wp.num_blocks = mgr.num_blocks
+    wp.ops = [("write", torch.cat(ks), torch.cat(vs), np.asarray(slots, np.int32))]
+    tables = np.full((w.S, max(blocks_for(n) for n in w.context_lens)), -1, np.int32)
+    for s in range(w.S):
+        t = mgr.block_table(s)
+        tables[s, :len(t)] = t
+    private = gpu_decode(wp, gpu_pool(wp), tables=tables)
+    assert private.tobytes() == shared.tobytes()
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_poisoned_pool_gives_identical_output(name):
+    """Unused tail slots and unreferenced blocks hold NaN (0xFF bytes); they
+    must not change a single output bit."""
+    w = wl.make_workload(name, small=True)
+    clean = gpu_decode(w, gpu_pool(w, fill=0))
+    poisoned = gpu_decode(w, gpu_pool(w, fill=0xFF))
+    assert poisoned.tobytes() == clean.tobytes()
+    assert not np.isnan(clean).any()
+
+
+@pytest.mark.parametrize("name", ["mha13b", "gqa70b", "fp8"])
+def test_run_to_run_deterministic(name):
+    w = wl.make_workload(name, small=True)
+    pool = gpu_pool(w)
+    a = gpu_decode(w, pool)
+    b = gpu_decode(w, pool)
+    assert a.tobytes() == b.tobytes()
+
+
+def test_empty_and_overlong_contexts():
+    w = wl.make_workload("gqa70b", small=True)
+    pool = gpu_pool(w)
+    ctx = w.context_lens.copy()
+    ctx[0] = 0
+    out = gpu_decode(w, pool, ctx=ctx)
+    assert (out[0] == 0).all()
+    ctx2 = w.context_lens.copy()
+    ctx2[1] = ctx2[1] + 100  # beyond the table: clamped to max_blocks_per_seq * 16
+    out2 = gpu_decode(w, pool, ctx=ctx2)
+    ref = gpu_decode(w, pool)
+    assert out2[1].tobytes() == ref[1].tobytes()
+
+
+# --------------------------------------------------------- full-size configs
+def _sampled_rows(w, seqs):
+    return [(s, h) for s in seqs for h in range(w.Hq)]
+
+
+@pytest.mark.parametrize("name", ["mha13b", "gqa70b", "fp8", "sampling_b"])
+def test_full_size_sampled_rows(name):
+    """The full-size workload in the launch configuration the benchmark uses,
+    checked on sampled sequences (every head) against the oracle, and pool
+    bytes of those sequences' blocks bit-exact."""
+    torch.manual_seed(0)
+    w = wl.make_workload(name, small=False, device="cuda")
+    pool = gpu_pool(w)
+    out = gpu_decode(w, pool)
+    ctx = w.context_lens
+    seqs = sorted({int(np.argmax(ctx)), int(np.argmin(ctx)), 0, w.S - 1, w.S // 2, w.S // 3})
+    if name.startswith("sampling"):
+        kp, vp = oracle_pools(w)
+    else:
+        _, k, v, slots = w.ops[0]
+        off = np.concatenate([[0], np.cumsum(ctx.astype(np.int64))])
+        idx = np.concatenate([np.arange(off[s], off[s + 1]) for s in seqs])
+        kp = oracle.new_pool(w.num_blocks, w.Hkv, w.D, w.pool_dtype)
+        vp = oracle.new_pool(w.num_blocks, w.Hkv, w.D, w.pool_dtype)
+        it = torch.as_tensor(idx, device=k.device)
+        oracle.reshape_and_cache(kp, vp, w.pool_dtype, w.num_blocks, w.Hkv, w.D,
+                                 raw_numpy(k.index_select(0, it)),
+                                 raw_numpy(v.index_select(0, it)), w.kv_in_dtype,
+                                 slots[idx], w.k_scale, w.v_scale)
+        gk, gv = _pool_bytes(pool)
+        tile = 16 * w.D * oracle.ELEM_BYTES[w.pool_dtype] * w.Hkv
+        for s in seqs:
+            for b in w.block_tables[s][:blocks_for(ctx[s])]:
+                sl = slice(int(b) * tile, (int(b) + 1) * tile)
+                assert np.array_equal(gk[sl], kp[sl]) and np.array_equal(gv[sl], vp[sl])
+    rows = _sampled_rows(w, seqs)
+    ref = oracle_decode(w, kp, vp, rows=rows)
+    got = np.stack([out[s, h] for s, h in rows])
+    err = float(np.max(np.abs(got - ref)))
+    print("%s full size: %d rows, max abs err %.3e" % (name, len(rows), err))
+    assert err <= tolerance(w)
