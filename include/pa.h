@@ -147,6 +147,12 @@ int pa_reshape_and_cache(const pa_pool_t *pool, const void *k, const void *v, in
 int pa_copy_blocks(const pa_pool_t *pool, const int32_t *src_dst_pairs, int32_t num_pairs,
                    void *stream);
 
+/* Which partition kernel pa_decode launches for this pool and head count:
+ * 0 = vector-ALU kernel (one workgroup per query head), 1 = matrix-core
+ * kernel (one workgroup per KV head and its group of query heads).  Returns a
+ * negative pa_status on invalid arguments. */
+int pa_decode_variant(const pa_pool_t *pool, int32_t num_q_heads);
+
 /* Measurement aid: the next pa_decode call on this host thread records
  * `before` (a hipEvent_t) just before its partition kernel and `after` just
  * after it, on the call's stream.  Pass NULLs to clear. */

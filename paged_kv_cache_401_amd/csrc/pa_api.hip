@@ -255,6 +255,14 @@ int pa_copy_blocks(const pa_pool_t *pool, const int32_t *src_dst_pairs, int32_t 
     return ok();
 }
 
+int pa_decode_variant(const pa_pool_t *pool, int32_t num_q_heads) {
+    int rc = check_pool(pool);
+    if (rc == PA_OK) rc = check_heads(pool, 0, num_q_heads, 1);
+    if (rc != PA_OK) return rc;
+    return pa::mfma_path_supported(pool->kv_dtype, pool->head_dim,
+                                   num_q_heads / pool->num_kv_heads) ? 1 : 0;
+}
+
 int pa_set_profile_events(void *before, void *after) {
     if ((before == nullptr) != (after == nullptr))
         return fail(PA_ERR_NULL, "pass both events or neither");

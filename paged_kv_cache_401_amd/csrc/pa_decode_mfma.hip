@@ -1,12 +1,289 @@
 // pa_decode_mfma.hip -- matrix-core decode kernel for grouped-query attention.
+//
+// When G = Hq / Hkv query heads share one KV head (grouped-query attention,
+// "PagedAttention" glossary page, related techniques), each 16-token block
+// read through the block table ("how paging works") serves G queries, and the
+// two products of decode attention become small dense contractions:
+//     S^T[16 tokens][16 heads]  = K[16][D] . Q^T[D][16]           (heads >= G are zero)
+//     O^T[D][16 heads]         += V^T[D][16 tokens] . P^T[16][16]
+// Both run on gfx950's v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  An
+// fp8 (E4M3FN) pool is widened to bf16 in registers, which is exact.
+//
+// Work split: one workgroup per (sequence, KV head, partition of
+// partition_tokens tokens); its four wavefronts take every fourth block and
+// keep their own online-softmax state (running max m and sum l per head,
+// base-2 exponent domain), merged through LDS at the end.  Longer contexts
+// leave per-partition (m, l, O) in the workspace for the reduce kernel.
+//
+// Operand layouts (lane = 16 c + n, n = lane % 16):
+//   K (A operand, rows = tokens): the pool's K tile stores each token's head
+//     vector in 16-byte runs, token-major per run, so lane (n, c) loads run
+//     c + 4u of token n with one 16-byte load; all 64 lanes read 1 KiB of
+//     contiguous memory.  Contraction index (c, r) of step u is head dim
+//     8 (4u + c) + r for bf16, 16 (c + 4j) + 8 h + r for fp8 (run c + 4j,
+//     half h); Q^T uses the same mapping.
+//   S^T (result): lane (n, c) holds tokens 4c..4c+3 of head n, which is
+//     exactly the P^T operand layout of the second product, so probabilities
+//     never leave their lane.
+//   V (A operand, rows = head dims): the pool's V tile stores 16-byte cells of
+//     4 consecutive tokens x W head dims, so lane (n, c) loads the cell of
+//     tokens 4c..4c+3 and head dims W (16 jj + n) .. +W-1 with one load.
+//   P^T is split into bf16 high and low parts (p = hi + lo to 16 significant
+//     bits); the 32-deep contraction takes [hi | lo] against [V | V], so one
+//     MFMA per 16 x 16 output tile carries P at ~16-bit precision.
+//   Tokens past the context are excluded by selection: their scores are set
+//     to -inf and their V operand elements to zero before the product.
 #include "pa_internal.h"
 
 namespace pa {
+namespace {
 
-bool mfma_path_supported(int, int, int) { return false; }
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-hipError_t launch_decode_mfma(int, int, const DecodeParams &, hipStream_t) {
-    return hipErrorNotSupported;
+constexpr float kNegInf = -__builtin_inff();
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// four fp8 codes (one 32-bit word) -> four bf16 in two words (exact)
+__device__ __forceinline__ void e4m3x4_to_bf16(uint32_t w, uint32_t &lo, uint32_t &hi) {
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+    lo = __builtin_bit_cast(uint32_t, a);
+    hi = __builtin_bit_cast(uint32_t, b);
+}
+
+// p = hi + lo with hi = p truncated to bf16 and lo = the remainder truncated to bf16
+__device__ __forceinline__ void split_bf16(float p, uint32_t &hi, uint32_t &lo) {
+    const uint32_t u = __float_as_uint(p);
+    hi = u >> 16;
+    lo = __float_as_uint(p - __uint_as_float(u & 0xffff0000u)) >> 16;
+}
+
+template <int KV, int D>
+__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
+    constexpr int EB = KV == kBF16 ? 2 : 1;
+    constexpr int TILE_BYTES = kBlock * D * EB;
+    constexpr int NQK = D / 32;                   // QK steps (32-deep) per block
+    constexpr int NKL = KV == kBF16 ? NQK : NQK / 2;  // 16-byte K loads per lane per block
+    constexpr int W = 4 / EB;                     // V: head dims per 16-byte cell
+    constexpr int NVL = D / W / 16;               // 16-byte V loads per lane per block
+    constexpr int NT = D / 16;                    // 16 x 16 output tiles (= NVL * W)
+    constexpr int LDS_STRIDE = 17;                // [wave][d][head] with padding
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int n = lane & 15;
+    const int c = lane >> 4;
+
+    int bid = blockIdx.x;
+    const int part = bid % p.max_partitions;
+    bid /= p.max_partitions;
+    const int g = bid % p.num_kv_heads;
+    const int s = bid / p.num_kv_heads;
+    const int G = p.group;
+
+    int ctx = p.context_lens[s];
+    ctx = ctx < 0 ? 0 : (ctx > p.max_blocks_per_seq * kBlock ? p.max_blocks_per_seq * kBlock : ctx);
+    const int nparts = (ctx + p.partition_tokens - 1) / p.partition_tokens;
+    if (part >= (nparts > 1 ? nparts : 1)) return;
+    const int tok0 = part * p.partition_tokens;
+    const int tok1 = min(ctx, tok0 + p.partition_tokens);
+    const int blk0 = tok0 / kBlock;
+    const int blk1 = (tok1 + kBlock - 1) / kBlock;
+
+    // Q^T operands: head g*G + n (zero for n >= G), head dims per the K mapping
+    bf16x8 qop[NQK];
+    {
+        const uint16_t *qrow = reinterpret_cast<const uint16_t *>(p.q) +
+                               ((int64_t)s * p.num_q_heads + (int64_t)g * G + n) * D;
+#pragma unroll
+        for (int u = 0; u < NQK; ++u) {
+            int d0;
+            if constexpr (KV == kBF16)
+                d0 = 8 * (4 * u + c);
+            else
+                d0 = 16 * (c + 4 * (u >> 1)) + 8 * (u & 1);
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (n < G) v = *reinterpret_cast<const u32x4 *>(qrow + d0);
+            qop[u] = as_bf16x8(v);
+        }
+    }
+
+    float m = kNegInf;
+    float l = 0.f;
+    floatx4 acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    const int32_t *table = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
+    const char *kbase = static_cast<const char *>(p.k_pool);
+    const char *vbase = static_cast<const char *>(p.v_pool);
+    const int koff = (c * kBlock + n) * 16;        // run c, token n
+    const int voff = (c * (D / W) + n) * 16;       // cell (tokens 4c.., dims W*n..)
+
+    for (int j = blk0 + wave; j < blk1; j += 4) {
+        const int32_t b = table[j];
+        if (b < 0 || b >= p.num_blocks) continue;
+        const int64_t tile = ((int64_t)b * p.num_kv_heads + g) * TILE_BYTES;
+        const char *kt = kbase + tile + koff;
+        const char *vt = vbase + tile + voff;
+        u32x4 kr[NKL], vr[NVL];
+#pragma unroll
+        for (int i = 0; i < NKL; ++i) kr[i] = *reinterpret_cast<const u32x4 *>(kt + i * 4 * kBlock * 16);
+#pragma unroll
+        for (int i = 0; i < NVL; ++i) vr[i] = *reinterpret_cast<const u32x4 *>(vt + i * 16 * 16);
+
+        // S^T = K . Q^T
+        floatx4 sacc = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (KV == kBF16) {
+#pragma unroll
+            for (int u = 0; u < NQK; ++u)
+                sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[u]), qop[u], sacc, 0, 0, 0);
+        } else {
+#pragma unroll
+            for (int i = 0; i < NKL; ++i) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    uint32_t a0, a1, a2, a3;
+                    e4m3x4_to_bf16(kr[i][2 * h], a0, a1);
+                    e4m3x4_to_bf16(kr[i][2 * h + 1], a2, a3);
+                    const u32x4 a = {a0, a1, a2, a3};
+                    sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), qop[2 * i + h], sacc,
+                                                                   0, 0, 0);
+                }
+            }
+        }
+
+        // online softmax over this block (tokens 4c..4c+3 of head n in this lane)
+        const int nvalid = tok1 - j * kBlock;       // >= 1
+        float sc[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sc[i] = sacc[i] * p.qk_scale_log2;
+            if (4 * c + i >= nvalid) sc[i] = kNegInf;
+        }
+        float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+        bm = fmaxf(bm, __shfl_xor(bm, 16));
+        bm = fmaxf(bm, __shfl_xor(bm, 32));
+        const float m_new = fmaxf(m, bm);
+        const float alpha = exp2f(m - m_new);
+        float pr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pr[i] = exp2f(sc[i] - m_new);
+        m = m_new;
+        l = l * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+
+        // P^T operand: [hi(p0..p3) | lo(p0..p3)]
+        u32x4 pw;
+        {
+            uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
+            split_bf16(pr[0], h0, l0);
+            split_bf16(pr[1], h1, l1);
+            split_bf16(pr[2], h2, l2);
+            split_bf16(pr[3], h3, l3);
+            pw[0] = h0 | (h1 << 16);
+            pw[1] = h2 | (h3 << 16);
+            pw[2] = l0 | (l1 << 16);
+            pw[3] = l2 | (l3 << 16);
+        }
+        const bf16x8 pop = as_bf16x8(pw);
+
+        // zero the V elements of tokens past the context (last block only)
+        uint32_t keep01 = 0xffffffffu, keep23 = 0xffffffffu;
+        if (nvalid < kBlock) {
+            keep01 = (4 * c + 0 < nvalid ? 0x0000ffffu : 0u) | (4 * c + 1 < nvalid ? 0xffff0000u : 0u);
+            keep23 = (4 * c + 2 < nvalid ? 0x0000ffffu : 0u) | (4 * c + 3 < nvalid ? 0xffff0000u : 0u);
+        }
+
+        // O^T += V^T . P^T, one MFMA per 16 x 16 tile
+#pragma unroll
+        for (int jj = 0; jj < NVL; ++jj) {
+#pragma unroll
+            for (int w = 0; w < W; ++w) {
+                uint32_t v01, v23;
+                if constexpr (KV == kBF16) {
+                    v01 = vr[jj][2 * w];
+                    v23 = vr[jj][2 * w + 1];
+                } else {
+                    e4m3x4_to_bf16(vr[jj][w], v01, v23);
+                }
+                v01 &= keep01;
+                v23 &= keep23;
+                const u32x4 a = {v01, v23, v01, v23};
+                floatx4 &o = acc[jj * W + w];
+                o *= alpha;
+                o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), pop, o, 0, 0, 0);
+            }
+        }
+    }
+
+    // per-head totals of the lane-partial sums
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+
+    __shared__ float sm_m[4][16], sm_l[4][16];
+    __shared__ float sm_acc[4][D * LDS_STRIDE];
+    if (c == 0) {
+        sm_m[wave][n] = m;
+        sm_l[wave][n] = l;
+    }
+#pragma unroll
+    for (int jj = 0; jj < NVL; ++jj)
+#pragma unroll
+        for (int w = 0; w < W; ++w)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int d = W * (16 * jj + 4 * c + i) + w;
+                sm_acc[wave][d * LDS_STRIDE + n] = acc[jj * W + w][i];
+            }
+    __syncthreads();
+
+    for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+        const int hh = idx / D;
+        const int d = idx % D;
+        const float M = fmaxf(fmaxf(sm_m[0][hh], sm_m[1][hh]), fmaxf(sm_m[2][hh], sm_m[3][hh]));
+        float L = 0.f, O = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float f = sm_m[w][hh] == kNegInf ? 0.f : exp2f(sm_m[w][hh] - M);
+            L += sm_l[w][hh] * f;
+            O += sm_acc[w][d * LDS_STRIDE + hh] * f;
+        }
+        const int64_t row = (int64_t)s * p.num_q_heads + (int64_t)g * G + hh;
+        if (nparts <= 1) {
+            p.out[row * D + d] = L > 0.f ? (O / L) * p.out_scale : 0.f;
+        } else {
+            const int64_t pr = row * p.max_partitions + part;
+            p.ws_acc[pr * D + d] = O;
+            if (d == 0) {
+                p.ws_m[pr] = M;
+                p.ws_l[pr] = L;
+            }
+        }
+    }
+}
+
+template <int KV, int D>
+hipError_t launch(const DecodeParams &p, hipStream_t stream) {
+    const int64_t grid = (int64_t)p.num_seqs * p.num_kv_heads * p.max_partitions;
+    if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+    decode_mfma_kernel<KV, D><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool mfma_path_supported(int kv, int head_dim, int group) {
+    return (kv == kBF16 || kv == kFP8) && (head_dim == 64 || head_dim == 128) && group >= 2 &&
+           group <= 16;
+}
+
+hipError_t launch_decode_mfma(int kv, int head_dim, const DecodeParams &p, hipStream_t stream) {
+    if (kv == kBF16) return head_dim == 64 ? launch<kBF16, 64>(p, stream) : launch<kBF16, 128>(p, stream);
+    return head_dim == 64 ? launch<kFP8, 64>(p, stream) : launch<kFP8, 128>(p, stream);
 }
 
 }  // namespace pa

@@ -23,7 +23,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 
 # every symbol include/pa.h declares
 EXPORTS = ("pa_pool_bytes", "pa_decode_partition_tokens", "pa_decode_workspace_size", "pa_decode",
-           "pa_reshape_and_cache", "pa_copy_blocks", "pa_set_profile_events", "pa_strerror",
+           "pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_variant", "pa_set_profile_events",
+           "pa_strerror",
            "pa_last_error", "pa_build_info")
 
 
@@ -66,6 +67,8 @@ def lib() -> ctypes.CDLL:
     L.pa_reshape_and_cache.restype = ctypes.c_int
     L.pa_copy_blocks.argtypes = [PD, P, I32, P]
     L.pa_copy_blocks.restype = ctypes.c_int
+    L.pa_decode_variant.argtypes = [PD, I32]
+    L.pa_decode_variant.restype = ctypes.c_int
     L.pa_set_profile_events.argtypes = [P, P]
     L.pa_set_profile_events.restype = ctypes.c_int
     L.pa_strerror.argtypes = [ctypes.c_int]
@@ -188,6 +191,15 @@ def decode(pool: KVPool, q: torch.Tensor, block_tables: torch.Tensor, context_le
                            _dev(out, "out", torch.float32), int(partition_tokens), wptr, wbytes,
                            _stream(stream)))
     return out
+
+
+def decode_variant(pool: KVPool, num_q_heads: int) -> str:
+    """Name of the partition kernel pa_decode launches for this pool."""
+    d = pool.desc()
+    r = lib().pa_decode_variant(ctypes.byref(d), num_q_heads)
+    if r < 0:
+        raise PAError(r, lib().pa_last_error().decode())
+    return "decode_mfma_kernel" if r == 1 else "decode_valu_kernel"
 
 
 def set_profile_events(before, after) -> None:

@@ -105,6 +105,13 @@ def test_cache_and_copy_argument_rules():
     assert L.pa_copy_blocks(ctypes.byref(d), 16, -3, None) == -3
 
 
+def test_decode_variant():
+    L = ops.lib()
+    assert L.pa_decode_variant(ctypes.byref(desc(kv_dtype=ops.F32)), 8) == 0
+    assert L.pa_decode_variant(ctypes.byref(desc()), 12) == -3
+    assert L.pa_decode_variant(ctypes.byref(desc()), 8) in (0, 1)
+
+
 def test_strerror_and_profile_events():
     L = ops.lib()
     for s in (0, -1, -2, -3, -4, -5, -6, -7, -8):

@@ -154,22 +154,25 @@ def test_one_hot_probe_is_bit_exact(case, ptok):
                 assert np.array_equal(out[s, h], v[h // (Hq // Hkv)]), (case, s, h, targets[s])
 
 
-def test_fp8_decode_all_codes_through_attention():
+@pytest.mark.parametrize("Hq", [1, 2])
+def test_fp8_decode_all_codes_through_attention(Hq):
     """A one-hot probe on tokens whose V rows hold all 256 E4M3FN codes: the
-    output is each code's value (NaN where the code is NaN)."""
+    output is each code's value (NaN where the code is NaN), through the
+    vector-ALU path (one head) and the matrix-core path (two heads on one KV head)."""
     D = 128
     codes = np.arange(256, dtype=np.uint8).reshape(2, D)
     vals = oracle.fp8_decode(codes.ravel()).reshape(2, D)
     for tgt in (0, 1):
-        w, _ = _one_hot(1, 1, 1, D, [2], oracle.FP8, [tgt])
+        w, _ = _one_hot(1, Hq, 1, D, [2], oracle.FP8, [tgt])
         _, k, v, slots = w.ops[0]
         v = torch.from_numpy(vals.astype(np.float32)).reshape(2, 1, D).to(torch.bfloat16)
         w.ops = [("write", k, v, slots)]
         out = gpu_decode(w, gpu_pool(w))
         want = vals[tgt]
-        assert np.array_equal(np.isnan(out[0, 0]), np.isnan(want))
-        ok = ~np.isnan(want)
-        assert np.array_equal(out[0, 0][ok], want[ok])
+        for h in range(Hq):
+            assert np.array_equal(np.isnan(out[0, h]), np.isnan(want))
+            ok = ~np.isnan(want)
+            assert np.array_equal(out[0, h][ok], want[ok])
 
 
 # --------------------------------------------------------------- invariants
