@@ -55,7 +55,27 @@ def parse():
     ap.add_argument("--cpu-seqs", type=int, default=None,
                     help="sequences in the CPU-oracle sample (default: ~10-30 s of CPU work)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="instead of the benchmark, run a plain device copy of BYTES bytes "
+                         "--steps times (reference for hardware byte counters)")
     return ap.parse_args()
+
+
+def copy_probe(nbytes: int, steps: int) -> None:
+    """A plain copy kernel of known size: reads and writes `nbytes` per launch."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    print(json.dumps({"copy_probe_bytes": src.numel() * 4, "launches": steps,
+                      "ms_per_copy": round(dt * 1e3, 4),
+                      "read_plus_write_GBps": round(2 * src.numel() * 4 / dt / 1e9, 1)}), flush=True)
 
 
 def source_digest() -> str:
@@ -79,6 +99,9 @@ def traffic_for(workload: str, kernel: str, launches_bytes: float):
 
 def main():
     args = parse()
+    if args.copy_probe:
+        copy_probe(args.copy_probe, args.steps)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "

@@ -63,7 +63,7 @@ __device__ __forceinline__ void split_bf16(float p, uint32_t &hi, uint32_t &lo) 
 }
 
 template <int KV, int D>
-__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void decode_mfma_kernel(DecodeParams p) {
     constexpr int EB = KV == kBF16 ? 2 : 1;
     constexpr int TILE_BYTES = kBlock * D * EB;
     constexpr int NQK = D / 32;                   // QK steps (32-deep) per block
@@ -124,18 +124,17 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     const int koff = (c * kBlock + n) * 16;        // run c, token n
     const int voff = (c * (D / W) + n) * 16;       // cell (tokens 4c.., dims W*n..)
 
-    for (int j = blk0 + wave; j < blk1; j += 4) {
-        const int32_t b = table[j];
-        if (b < 0 || b >= p.num_blocks) continue;
+    auto load_block = [&](int32_t b, u32x4 (&kr)[NKL], u32x4 (&vr)[NVL]) {
         const int64_t tile = ((int64_t)b * p.num_kv_heads + g) * TILE_BYTES;
         const char *kt = kbase + tile + koff;
         const char *vt = vbase + tile + voff;
-        u32x4 kr[NKL], vr[NVL];
 #pragma unroll
         for (int i = 0; i < NKL; ++i) kr[i] = *reinterpret_cast<const u32x4 *>(kt + i * 4 * kBlock * 16);
 #pragma unroll
         for (int i = 0; i < NVL; ++i) vr[i] = *reinterpret_cast<const u32x4 *>(vt + i * 16 * 16);
+    };
 
+    auto compute_block = [&](const u32x4 (&kr)[NKL], const u32x4 (&vr)[NVL], int j) {
         // S^T = K . Q^T
         floatx4 sacc = {0.f, 0.f, 0.f, 0.f};
         if constexpr (KV == kBF16) {
@@ -169,12 +168,17 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
         bm = fmaxf(bm, __shfl_xor(bm, 16));
         bm = fmaxf(bm, __shfl_xor(bm, 32));
         const float m_new = fmaxf(m, bm);
-        const float alpha = exp2f(m - m_new);
+        const float alpha = __builtin_amdgcn_exp2f(m - m_new);
         float pr[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pr[i] = exp2f(sc[i] - m_new);
+        for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(sc[i] - m_new);
         m = m_new;
         l = l * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+        // rescale the numerators only when some real head's maximum moved
+        if (__builtin_amdgcn_ballot_w64(n < G && alpha != 1.f) != 0) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) acc[t] *= alpha;
+        }
 
         // P^T operand: [hi(p0..p3) | lo(p0..p3)]
         u32x4 pw;
@@ -213,10 +217,48 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
                 v01 &= keep01;
                 v23 &= keep23;
                 const u32x4 a = {v01, v23, v01, v23};
-                floatx4 &o = acc[jj * W + w];
-                o *= alpha;
-                o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), pop, o, 0, 0, 0);
+                acc[jj * W + w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), pop,
+                                                                          acc[jj * W + w], 0, 0, 0);
             }
+        }
+    };
+
+    // This wavefront's blocks are j = blk0 + wave + 4k, k = 0..nk-1.  Their ids
+    // are fetched 64 at a time into one VGPR (lane i holds block k0 + i), and
+    // the K/V loads of block k+1 are issued before block k is computed (two
+    // register buffers, A and B, used alternately).
+    const int nk = blk1 - blk0 > wave ? (blk1 - blk0 - wave + 3) / 4 : 0;
+    for (int k0 = 0; k0 < nk; k0 += 64) {
+        const int kend = min(nk, k0 + 64);
+        int32_t ids = -1;
+        if (k0 + lane < kend) ids = table[blk0 + wave + 4 * (k0 + lane)];
+        auto block_id = [&](int k) { return __builtin_amdgcn_readlane(ids, k - k0); };
+        auto valid = [&](int32_t b) { return b >= 0 && b < p.num_blocks; };
+        u32x4 kA[NKL], vA[NVL], kB[NKL], vB[NVL];
+        int k = k0;
+        int32_t bA = block_id(k);
+        bool okA = valid(bA);
+        if (okA) load_block(bA, kA, vA);
+        while (true) {
+            const int k1 = k + 1;
+            bool okB = false;
+            if (k1 < kend) {
+                const int32_t bB = block_id(k1);
+                okB = valid(bB);
+                if (okB) load_block(bB, kB, vB);
+            }
+            if (okA) compute_block(kA, vA, blk0 + wave + 4 * k);
+            if (k1 >= kend) break;
+            const int k2 = k1 + 1;
+            okA = false;
+            if (k2 < kend) {
+                bA = block_id(k2);
+                okA = valid(bA);
+                if (okA) load_block(bA, kA, vA);
+            }
+            if (okB) compute_block(kB, vB, blk0 + wave + 4 * k1);
+            if (k2 >= kend) break;
+            k = k2;
         }
     }
 
