@@ -187,6 +187,18 @@ def main():
     kernel_name = ops.decode_variant(pool, w.Hq)
     traffic = traffic_for(args.workload, kernel_name, kv_bytes)
 
+    # the read bandwidth this GPU sustains on a plain streaming read of the K pool
+    sink = torch.zeros(16, dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        ops.probe_read(pool.k, sink)
+    pb, pe = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    pb.record(stream)
+    for _ in range(10):
+        ops.probe_read(pool.k, sink)
+    pe.record(stream)
+    torch.cuda.synchronize()
+    probe_gbps = pool.k.numel() / (pb.elapsed_time(pe) / 10 * 1e-3) / 1e9
+
     rec = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -210,6 +222,10 @@ def main():
         "decode_kernel_ms": round(kern_avg_ms, 5),
         "decode_kernel_ms_min": round(float(np.min(kern_ms)), 5),
         "wall_ms_per_step": round(1e3 * wall_s / args.steps, 5),
+        "unique_kv_bytes": w.unique_kv_bytes(),
+        "decode_unique_GBps": round(w.unique_kv_bytes() / (kern_avg_ms * 1e-3) / 1e9, 2),
+        "read_probe_GBps": round(probe_gbps, 1),
+        "decode_pct_of_read_probe": round(100.0 * achieved / probe_gbps, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "kernel": kernel_name,

@@ -158,6 +158,12 @@ int pa_decode_variant(const pa_pool_t *pool, int32_t num_q_heads);
  * after it, on the call's stream.  Pass NULLs to clear. */
 int pa_set_profile_events(void *before, void *after);
 
+/* Measurement aid: enqueue one streaming read of `bytes` bytes (rounded down
+ * to 16) of device buffer `buf` (16-byte aligned) by a grid-stride kernel, to
+ * time the read bandwidth the GPU sustains.  `sink` is a device buffer of at
+ * least 16 bytes that the kernel may write.  Returns a pa_status. */
+int pa_probe_read(const void *buf, size_t bytes, void *sink, void *stream);
+
 /* Static description of a status code. */
 const char *pa_strerror(int status);
 

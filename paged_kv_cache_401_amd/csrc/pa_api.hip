@@ -58,20 +58,20 @@ int64_t tile_bytes(const pa_pool_t *pool) {
     return (int64_t)PA_BLOCK_SIZE * pool->head_dim * pa::elem_bytes(pool->kv_dtype);
 }
 
-// Library's partition size: keep at least ~8 workgroups per compute unit in
-// flight (256 CUs), never below 256 tokens, and prefer long partitions
-// otherwise (each split costs a partial-result write and read).
+// Library's partition size.  Measured on MI355X: splitting a context costs a
+// partial-result write and read plus a second launch, and does not pay for
+// contexts up to 4096 tokens; longer contexts are cut into 2048-token
+// partitions so that no workgroup walks an unbounded chain of blocks.  Small
+// batches split further (down to 256 tokens) until ~1024 workgroups exist.
 int32_t auto_partition(const pa_pool_t *pool, int32_t num_seqs, int32_t num_q_heads,
                        int32_t max_blocks_per_seq) {
     const bool mfma = pa::mfma_path_supported(pool->kv_dtype, pool->head_dim,
                                               num_q_heads / pool->num_kv_heads);
     const int64_t rows = (int64_t)num_seqs * (mfma ? pool->num_kv_heads : num_q_heads);
     const int64_t max_tokens = (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE;
-    const int64_t target = 256 * 8;
-    int64_t ptok = 256;
-    while (ptok < max_tokens && rows * ((max_tokens + 2 * ptok - 1) / (2 * ptok)) >= target)
-        ptok *= 2;
-    if (ptok > max_tokens) ptok = ((max_tokens + 15) / 16) * 16;
+    int64_t ptok = max_tokens <= 4096 ? max_tokens : 2048;
+    while (ptok > 256 && rows * ((max_tokens + ptok - 1) / ptok) < 1024)
+        ptok = ((ptok / 2 + 15) / 16) * 16;
     return (int32_t)(ptok < 16 ? 16 : ptok);
 }
 

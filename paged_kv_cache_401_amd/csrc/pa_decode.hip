@@ -125,20 +125,19 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
     const char *kbase = static_cast<const char *>(p.k_pool);
     const char *vbase = static_cast<const char *>(p.v_pool);
 
-    for (int j = blk0 + wave; j < blk1; j += 4) {
-        const int32_t b = table[j];
-        if (b < 0 || b >= p.num_blocks) continue;
+    auto load_block = [&](int32_t b, uint4 (&kc)[NKL], uint4 (&vc)[NVL]) {
         const int64_t tile = ((int64_t)b * p.num_kv_heads + g) * TILE_BYTES;
         const char *kt = kbase + tile;
         const char *vt = vbase + tile;
-        uint4 kc[NKL], vc[NVL];
 #pragma unroll
         for (int jk = 0; jk < NKL; ++jk)
             kc[jk] = *reinterpret_cast<const uint4 *>(kt + ((c + 4 * jk) * kBlock + t) * 16);
 #pragma unroll
         for (int jj = 0; jj < NVL; ++jj)
             vc[jj] = *reinterpret_cast<const uint4 *>(vt + (c * (D / W) + 16 * jj + t) * 16);
+    };
 
+    auto compute_block = [&](const uint4 (&kc)[NKL], const uint4 (&vc)[NVL], int j) {
         float part_dot = 0.f;
 #pragma unroll
         for (int jk = 0; jk < NKL; ++jk)
@@ -150,8 +149,8 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
         float sc = part_dot * p.qk_scale_log2;
         if (j * kBlock + t >= tok1) sc = kNegInf;
         const float m_new = fmaxf(m, wave_max16(sc));
-        const float alpha = exp2f(m - m_new);
-        const float pt = exp2f(sc - m_new);
+        const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+        const float pt = __builtin_amdgcn_exp2f(sc - m_new);
         m = m_new;
 
         // probabilities of tokens 4c..4c+3; tokens past the context are left
@@ -165,6 +164,12 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
             live[i] = 4 * c + i < nvalid;
         }
         l = l * alpha + ((pw[0] + pw[1]) + (pw[2] + pw[3]));
+        if (alpha != 1.f) {  // alpha is the same in every lane
+#pragma unroll
+            for (int jj = 0; jj < NVL; ++jj)
+#pragma unroll
+                for (int w = 0; w < W; ++w) acc[jj][w] *= alpha;
+        }
 #pragma unroll
         for (int jj = 0; jj < NVL; ++jj) {
 #pragma unroll
@@ -175,8 +180,46 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
                     const float term = pw[i] * chunk_elem<KV>(vc[jj], 4 * w + i);
                     sum += live[i] ? term : 0.f;
                 }
-                acc[jj][w] = acc[jj][w] * alpha + sum;
+                acc[jj][w] += sum;
             }
+        }
+    };
+
+    // This wavefront's blocks are j = blk0 + wave + 4k, k = 0..nk-1; ids are
+    // fetched 64 at a time into one VGPR, and block k+1's loads are issued
+    // before block k is computed (register buffers A and B in turn).
+    const int nk = blk1 - blk0 > wave ? (blk1 - blk0 - wave + 3) / 4 : 0;
+    for (int k0 = 0; k0 < nk; k0 += 64) {
+        const int kend = min(nk, k0 + 64);
+        int32_t ids = -1;
+        if (k0 + lane < kend) ids = table[blk0 + wave + 4 * (k0 + lane)];
+        auto block_id = [&](int k) { return __builtin_amdgcn_readlane(ids, k - k0); };
+        auto valid = [&](int32_t b) { return b >= 0 && b < p.num_blocks; };
+        uint4 kA[NKL], vA[NVL], kB[NKL], vB[NVL];
+        int k = k0;
+        int32_t bA = block_id(k);
+        bool okA = valid(bA);
+        if (okA) load_block(bA, kA, vA);
+        while (true) {
+            const int k1 = k + 1;
+            bool okB = false;
+            if (k1 < kend) {
+                const int32_t bB = block_id(k1);
+                okB = valid(bB);
+                if (okB) load_block(bB, kB, vB);
+            }
+            if (okA) compute_block(kA, vA, blk0 + wave + 4 * k);
+            if (k1 >= kend) break;
+            const int k2 = k1 + 1;
+            okA = false;
+            if (k2 < kend) {
+                bA = block_id(k2);
+                okA = valid(bA);
+                if (okA) load_block(bA, kA, vA);
+            }
+            if (okB) compute_block(kB, vB, blk0 + wave + 4 * k1);
+            if (k2 >= kend) break;
+            k = k2;
         }
     }
 

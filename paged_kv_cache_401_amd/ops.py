@@ -24,8 +24,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 # every symbol include/pa.h declares
 EXPORTS = ("pa_pool_bytes", "pa_decode_partition_tokens", "pa_decode_workspace_size", "pa_decode",
            "pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_variant", "pa_set_profile_events",
-           "pa_strerror",
-           "pa_last_error", "pa_build_info")
+           "pa_probe_read", "pa_strerror", "pa_last_error", "pa_build_info")
 
 
 class PAError(RuntimeError):
@@ -71,6 +70,8 @@ def lib() -> ctypes.CDLL:
     L.pa_decode_variant.restype = ctypes.c_int
     L.pa_set_profile_events.argtypes = [P, P]
     L.pa_set_profile_events.restype = ctypes.c_int
+    L.pa_probe_read.argtypes = [P, SZ, P, P]
+    L.pa_probe_read.restype = ctypes.c_int
     L.pa_strerror.argtypes = [ctypes.c_int]
     L.pa_strerror.restype = ctypes.c_char_p
     L.pa_last_error.argtypes = []
@@ -208,6 +209,14 @@ def set_profile_events(before, after) -> None:
     b = before.cuda_event if before is not None else None
     a = after.cuda_event if after is not None else None
     _check(lib().pa_set_profile_events(b, a))
+
+
+def probe_read(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Enqueue one streaming read of ``buf`` (measurement aid)."""
+    rc = lib().pa_probe_read(_dev(buf, "buf"), buf.numel() * buf.element_size(),
+                             _dev(sink, "sink"), _stream(stream))
+    if rc != 0:
+        raise PAError(rc, lib().pa_strerror(rc).decode())
 
 
 def build_info() -> str:

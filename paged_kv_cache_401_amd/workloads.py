@@ -86,6 +86,18 @@ class Workload:
         eb = {F32: 4, BF16: 2, FP8: 1}[self.pool_dtype]
         return int(self.context_lens.astype(np.int64).sum()) * self.Hkv * self.D * 2 * eb
 
+    def unique_kv_bytes(self) -> int:
+        """K+V bytes of distinct physical token slots one decode pass reads (shared
+        prompt blocks counted once)."""
+        eb = {F32: 4, BF16: 2, FP8: 1}[self.pool_dtype]
+        used = {}
+        for s in range(self.S):
+            n = int(self.context_lens[s])
+            for i in range(-(-n // 16)):
+                b = int(self.block_tables[s, i])
+                used[b] = max(used.get(b, 0), min(16, n - 16 * i))
+        return sum(used.values()) * self.Hkv * self.D * 2 * eb
+
 
 def _f32(x: float) -> float:
     """The nearest fp32 value: the entry points take the softmax scale as fp32."""

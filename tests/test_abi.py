@@ -119,3 +119,6 @@ def test_strerror_and_profile_events():
     assert L.pa_set_profile_events(16, None) == -1
     assert L.pa_set_profile_events(None, None) == 0
     assert b"gfx950" in L.pa_build_info()
+    assert L.pa_probe_read(None, 64, 16, None) == -1
+    assert L.pa_probe_read(17, 64, 16, None) == -6
+    assert L.pa_probe_read(16, 8, 16, None) == -3
