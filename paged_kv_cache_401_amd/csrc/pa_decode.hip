@@ -33,29 +33,35 @@ namespace {
 
 constexpr float kNegInf = -__builtin_inff();
 
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-// OCP E4M3FN code -> fp32, exact: the code's exponent and mantissa fields are
-// placed in an fp32 pattern (a value 2^-120 times too small; subnormal codes
-// land on fp32 subnormals) and multiplied by 2^120.  S.1111.111 is NaN.
-__device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
-    const uint32_t mag = code & 0x7fu;
-    const float f = __uint_as_float(((code & 0x80u) << 24) | (mag << 20)) * 0x1p120f;
-    return mag == 0x7fu ? __uint_as_float(0x7fc00000u) : f;
+// Element e of a 16-byte chunk of fp32 values.
+__device__ __forceinline__ float chunk_f32(const uint4 &v, int e) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    return __uint_as_float(w[e]);
 }
 
-// Element e of a 16-byte chunk holding elements of type KV.
-template <int KV>
-__device__ __forceinline__ float chunk_elem(const uint4 &v, int e) {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    if constexpr (KV == kF32) {
-        return __uint_as_float(w[e]);
-    } else if constexpr (KV == kBF16) {
-        return (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]);
-    } else {
-        return e4m3_to_f32((w[e >> 2] >> (8 * (e & 3))) & 0xffu);
-    }
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// a.lo * b.lo + a.hi * b.hi + acc for two packed bf16 pairs (v_dot2_f32_bf16;
+// the bf16 products are exact in fp32)
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                           __builtin_bit_cast(bf16x2, b), acc, false);
+}
+
+// four fp8 codes (one word) -> bf16 pairs (codes 0,1) and (codes 2,3), exact
+__device__ __forceinline__ void e4m3x4_to_bf16(uint32_t w, uint32_t &lo, uint32_t &hi) {
+    lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+    hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+}
+
+// p0, p1 -> bf16 pairs hi = (trunc(p0), trunc(p1)) and lo = the remainders,
+// truncated: hi + lo carries each p to 16 significant bits
+__device__ __forceinline__ void split_pair(float p0, float p1, uint32_t &hi, uint32_t &lo) {
+    const uint32_t u0 = __float_as_uint(p0), u1 = __float_as_uint(p1);
+    const uint32_t r0 = __float_as_uint(p0 - __uint_as_float(u0 & 0xffff0000u));
+    const uint32_t r1 = __float_as_uint(p1 - __uint_as_float(u1 & 0xffff0000u));
+    hi = (u0 >> 16) | (u1 & 0xffff0000u);
+    lo = (r0 >> 16) | (r1 & 0xffff0000u);
 }
 
 __device__ __forceinline__ float wave_max16(float x) {
@@ -97,18 +103,29 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
     const int blk0 = tok0 / kBlock;
     const int blk1 = (tok1 + kBlock - 1) / kBlock;
 
-    // q elements matching this lane's K runs
-    float qv[NKL][X];
+    // q elements matching this lane's K runs: fp32 values for an fp32 pool,
+    // else the raw bf16 pairs (dims 2i, 2i+1 of run c + 4j in word i), which
+    // line up with the K run's bf16 pairs (fp8 runs are widened pairwise)
+    constexpr int QW = KV == kF32 ? 1 : X / 2;  // bf16 pairs per run
     const int64_t qrow = ((int64_t)s * p.num_q_heads + h) * D;
+    float qv[KV == kF32 ? NKL : 1][KV == kF32 ? X : 1];
+    uint32_t qw[KV == kF32 ? 1 : NKL][QW];
 #pragma unroll
     for (int j = 0; j < NKL; ++j) {
+        const int d0 = (c + 4 * j) * X;
+        if constexpr (KV == kF32) {
 #pragma unroll
-        for (int x = 0; x < X; ++x) {
-            const int d = (c + 4 * j) * X + x;
-            if constexpr (KV == kF32) {
-                qv[j][x] = reinterpret_cast<const float *>(p.q)[qrow + d];
-            } else {
-                qv[j][x] = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(p.q)[qrow + d] << 16);
+            for (int x = 0; x < X; ++x) qv[j][x] = reinterpret_cast<const float *>(p.q)[qrow + d0 + x];
+        } else {
+            const uint4 *src = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(p.q) +
+                                                               qrow + d0);
+#pragma unroll
+            for (int i = 0; i < QW / 4; ++i) {
+                const uint4 v = src[i];
+                qw[j][4 * i + 0] = v.x;
+                qw[j][4 * i + 1] = v.y;
+                qw[j][4 * i + 2] = v.z;
+                qw[j][4 * i + 3] = v.w;
             }
         }
     }
@@ -140,9 +157,26 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
     auto compute_block = [&](const uint4 (&kc)[NKL], const uint4 (&vc)[NVL], int j) {
         float part_dot = 0.f;
 #pragma unroll
-        for (int jk = 0; jk < NKL; ++jk)
+        for (int jk = 0; jk < NKL; ++jk) {
+            if constexpr (KV == kF32) {
 #pragma unroll
-            for (int x = 0; x < X; ++x) part_dot += qv[jk][x] * chunk_elem<KV>(kc[jk], x);
+                for (int x = 0; x < X; ++x) part_dot += qv[jk][x] * chunk_f32(kc[jk], x);
+            } else if constexpr (KV == kBF16) {
+                part_dot = dot2(kc[jk].x, qw[jk][0], part_dot);
+                part_dot = dot2(kc[jk].y, qw[jk][1], part_dot);
+                part_dot = dot2(kc[jk].z, qw[jk][2], part_dot);
+                part_dot = dot2(kc[jk].w, qw[jk][3], part_dot);
+            } else {
+                const uint32_t kw[4] = {kc[jk].x, kc[jk].y, kc[jk].z, kc[jk].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    uint32_t lo, hi;
+                    e4m3x4_to_bf16(kw[i], lo, hi);
+                    part_dot = dot2(lo, qw[jk][2 * i], part_dot);
+                    part_dot = dot2(hi, qw[jk][2 * i + 1], part_dot);
+                }
+            }
+        }
         part_dot += __shfl_xor(part_dot, 16);
         part_dot += __shfl_xor(part_dot, 32);
 
@@ -170,17 +204,49 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
 #pragma unroll
                 for (int w = 0; w < W; ++w) acc[jj][w] *= alpha;
         }
+        if constexpr (KV == kF32) {
 #pragma unroll
-        for (int jj = 0; jj < NVL; ++jj) {
+            for (int jj = 0; jj < NVL; ++jj) {
 #pragma unroll
-            for (int w = 0; w < W; ++w) {
-                float sum = 0.f;
+                for (int w = 0; w < W; ++w) {
+                    float sum = 0.f;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float term = pw[i] * chunk_elem<KV>(vc[jj], 4 * w + i);
-                    sum += live[i] ? term : 0.f;
+                    for (int i = 0; i < 4; ++i) {
+                        const float term = pw[i] * chunk_f32(vc[jj], 4 * w + i);
+                        sum += live[i] ? term : 0.f;
+                    }
+                    acc[jj][w] += sum;
                 }
-                acc[jj][w] += sum;
+            }
+        } else {
+            // P as bf16 hi + lo pairs against the V cell's bf16 token pairs;
+            // V elements of tokens past the context are zeroed first
+            uint32_t p01h, p01l, p23h, p23l;
+            split_pair(pw[0], pw[1], p01h, p01l);
+            split_pair(pw[2], pw[3], p23h, p23l);
+            const uint32_t keep01 = (live[0] ? 0x0000ffffu : 0u) | (live[1] ? 0xffff0000u : 0u);
+            const uint32_t keep23 = (live[2] ? 0x0000ffffu : 0u) | (live[3] ? 0xffff0000u : 0u);
+#pragma unroll
+            for (int jj = 0; jj < NVL; ++jj) {
+                const uint32_t vw[4] = {vc[jj].x, vc[jj].y, vc[jj].z, vc[jj].w};
+#pragma unroll
+                for (int w = 0; w < W; ++w) {
+                    uint32_t v01, v23;
+                    if constexpr (KV == kBF16) {
+                        v01 = vw[2 * w];
+                        v23 = vw[2 * w + 1];
+                    } else {
+                        e4m3x4_to_bf16(vw[w], v01, v23);
+                    }
+                    v01 &= keep01;
+                    v23 &= keep23;
+                    float a = acc[jj][w];
+                    a = dot2(v01, p01h, a);
+                    a = dot2(v23, p23h, a);
+                    a = dot2(v01, p01l, a);
+                    a = dot2(v23, p23l, a);
+                    acc[jj][w] = a;
+                }
             }
         }
     };
@@ -274,30 +340,64 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
 
 // Merge the partitions of one (sequence, query head) row, in partition order:
 // M = max_p m_p, out = sum_p acc_p 2^(m_p - M) / sum_p l_p 2^(m_p - M).
+// One wavefront per row (four rows per workgroup); lane i holds head dims
+// E*i .. E*i+E-1.  The partition weights are computed 64 at a time, one per
+// lane, and broadcast with readlane, so the partial numerators of eight
+// partitions are in flight at once.
 template <int D>
 __global__ __launch_bounds__(kThreads) void decode_reduce_kernel(DecodeParams p) {
-    const int64_t row = blockIdx.x;  // s * Hq + h
+    constexpr int E = D / 64;
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);  // s * Hq + h
+    if (row >= (int64_t)p.num_seqs * p.num_q_heads) return;
     const int s = (int)(row / p.num_q_heads);
     int ctx = p.context_lens[s];
     ctx = ctx < 0 ? 0 : (ctx > p.max_blocks_per_seq * kBlock ? p.max_blocks_per_seq * kBlock : ctx);
     const int nparts = (ctx + p.partition_tokens - 1) / p.partition_tokens;
     if (nparts <= 1) return;  // written by the partition kernel
-    const int d = threadIdx.x;
-    if (d >= D) return;
     const float *ms = p.ws_m + row * p.max_partitions;
     const float *ls = p.ws_l + row * p.max_partitions;
-    const float *as = p.ws_acc + row * p.max_partitions * D;
+    const float *as = p.ws_acc + row * p.max_partitions * D + E * lane;
+
     float M = kNegInf;
-    for (int i = 0; i < nparts; ++i) M = fmaxf(M, ms[i]);
-    float L = 0.f, O = 0.f;
+    for (int i = lane; i < nparts; i += 64) M = fmaxf(M, ms[i]);
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
+
+    float L = 0.f;
+    float O[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) O[e] = 0.f;
     if (M != kNegInf) {
-        for (int i = 0; i < nparts; ++i) {
-            const float f = exp2f(ms[i] - M);
-            L += ls[i] * f;
-            O += as[(int64_t)i * D + d] * f;
+        for (int base = 0; base < nparts; base += 64) {
+            const int i = base + lane;
+            const float f = i < nparts ? exp2f(ms[i] - M) : 0.f;
+            L += i < nparts ? ls[i] * f : 0.f;
+            const int cnt = min(64, nparts - base);
+            auto add = [&](int j) {
+                const float fj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), j));
+                const float *a = as + (int64_t)(base + j) * D;
+                if constexpr (E == 2) {
+                    const float2 v = *reinterpret_cast<const float2 *>(a);
+                    O[0] += v.x * fj;
+                    O[1] += v.y * fj;
+                } else {
+                    O[0] += a[0] * fj;
+                }
+            };
+            int j = 0;
+            for (; j + 8 <= cnt; j += 8) {
+#pragma unroll
+                for (int u = 0; u < 8; ++u) add(j + u);
+            }
+            for (; j < cnt; ++j) add(j);
         }
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) L += __shfl_xor(L, o);
     }
-    p.out[row * D + d] = L > 0.f ? (O / L) * p.out_scale : 0.f;
+    float *dst = p.out + row * D + E * lane;
+#pragma unroll
+    for (int e = 0; e < E; ++e) dst[e] = L > 0.f ? (O[e] / L) * p.out_scale : 0.f;
 }
 
 template <int KV, int D>
@@ -322,7 +422,8 @@ hipError_t launch_decode_valu(int kv, int head_dim, const DecodeParams &p, hipSt
 }
 
 hipError_t launch_decode_reduce(int head_dim, const DecodeParams &p, hipStream_t stream) {
-    const int64_t grid = (int64_t)p.num_seqs * p.num_q_heads;
+    const int64_t rows = (int64_t)p.num_seqs * p.num_q_heads;
+    const int64_t grid = (rows + kThreads / 64 - 1) / (kThreads / 64);
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
     if (head_dim == 64)
         decode_reduce_kernel<64><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(p);
