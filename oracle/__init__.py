@@ -1,5 +1,5 @@
-"""fp64 CPU oracle for paged decode attention, the paged cache write and the
-copy-on-write block copy.
+"""fp64 CPU oracle for paged decode attention, paged (chunked) prefill
+attention, the paged cache write and the copy-on-write block copy.
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may import this package.  It shares no code
@@ -62,6 +62,9 @@ def bind(L: ctypes.CDLL) -> ctypes.CDLL:
     L.orc_paged_attention.argtypes = [P, P, I, F, F, I, I, P, I, I, I, P, I, P, F,
                                       P, P, I64, I]
     L.orc_paged_attention.restype = I
+    L.orc_prefill_attention.argtypes = [P, P, I, F, F, I, I, P, I, I, I, P, P, I, P, F,
+                                        P, P, I64, I]
+    L.orc_prefill_attention.restype = I
     L.orc_max_threads.argtypes = []
     L.orc_max_threads.restype = I
     return L
@@ -172,6 +175,35 @@ def paged_attention(k_pool, v_pool, pool_dt, Hkv, D, q, q_dt, S, Hq, block_table
     return out
 
 
+def prefill_attention(k_pool, v_pool, pool_dt, Hkv, D, q, q_dt, S, Hq, query_start, block_tables,
+                      context_lens, scale, k_scale=1.0, v_scale=1.0, rows=None,
+                      threads=0) -> np.ndarray:
+    """fp64 causal attention of each sequence's chunk of new tokens (the last
+    ``query_start[s+1] - query_start[s]`` tokens of its context) over its
+    paged context.  q is [total][Hq][D]; returns [total][Hq][D], or
+    [len(rows)][D] when ``rows`` lists (chunk token, head) pairs."""
+    qb = _bytes(q)
+    qs = np.ascontiguousarray(query_start, dtype=np.int32)
+    assert qs.size == S + 1
+    tables = np.ascontiguousarray(block_tables, dtype=np.int32)
+    MBS = tables.shape[1] if tables.ndim == 2 else tables.size // max(S, 1)
+    ctx = np.ascontiguousarray(context_lens, dtype=np.int32)
+    if rows is not None:
+        rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int32).reshape(-1, 2))
+        out = np.zeros((rows.shape[0], D), dtype=np.float64)
+        nrows = rows.shape[0]
+    else:
+        out = np.zeros((int(qs[-1]), Hq, D), dtype=np.float64)
+        nrows = 0
+    rc = lib().orc_prefill_attention(_ptr(k_pool), _ptr(v_pool), pool_dt, float(k_scale),
+                                     float(v_scale), Hkv, D, _ptr(qb), q_dt, S, Hq, _ptr(qs),
+                                     _ptr(tables), MBS, _ptr(ctx), float(scale), _ptr(out),
+                                     _ptr(rows), nrows, int(threads))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments (rc=%d)" % rc)
+    return out
+
+
 # ------------------------------------------------------- library restatement
 def dense_attention(q, K, V, scale) -> np.ndarray:
     """softmax(scale * q K^T) V for contiguous K/V, via scipy's softmax and
@@ -182,3 +214,17 @@ def dense_attention(q, K, V, scale) -> np.ndarray:
     V = np.asarray(V, dtype=np.float64)
     w = softmax(np.float64(scale) * (K @ q), axis=-1)
     return w @ V
+
+
+def dense_causal_attention(Q, K, V, scale, first_pos) -> np.ndarray:
+    """Rows of Q [n][D] at positions first_pos .. first_pos + n - 1 over K/V
+    [ctx][D]: scipy softmax of scale * Q K^T with every key after a row's
+    position masked to -inf, then times V (fp64 library restatement)."""
+    from scipy.special import softmax
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    s = np.float64(scale) * (Q @ K.T)
+    pos = first_pos + np.arange(Q.shape[0])[:, None]
+    s = np.where(np.arange(K.shape[0])[None, :] <= pos, s, -np.inf)
+    return softmax(s, axis=-1) @ V

@@ -278,25 +278,24 @@ void orc_gather(const uint8_t *pool, int is_v, int pool_dt, int Hkv, int D,
 
 /* ------------------------------------------------------ decode attention */
 
-/* One output row: query head h of sequence s against the ctx[s] tokens of KV
- * head g = h / (Hq / Hkv), gathered through the sequence's block table. */
-static void orc_attend_one(const uint8_t *k_pool, const uint8_t *v_pool, int pool_dt,
+/* One output row: the query row stored at q[qrow][0..D) (query head h)
+ * against tokens 0..n-1 of KV head g = h / (Hq / Hkv), gathered through the
+ * sequence's block table `table` in logical order.  n <= 0 gives a zero row. */
+static void orc_attend_row(const uint8_t *k_pool, const uint8_t *v_pool, int pool_dt,
                            double k_scale, double v_scale, int Hkv, int D,
-                           const uint8_t *q, int q_dt, int Hq, const int32_t *tables,
-                           int MBS, const int32_t *ctx, double scale, int s, int h,
+                           const uint8_t *q, int q_dt, int64_t qrow, int Hq, int h,
+                           const int32_t *table, int64_t n, double scale,
                            double *out_row, double *score, double *kbuf)
 {
     int eb = orc_elem_bytes(pool_dt);
     int group = Hq / Hkv;
     int g = h / group;
-    int64_t n = ctx[s];
     for (int d = 0; d < D; d++)
         out_row[d] = 0.0;
     if (n <= 0)
         return;
-    const int32_t *table = tables + (int64_t)s * MBS;
     for (int d = 0; d < D; d++)
-        kbuf[d] = orc_load(q, ((int64_t)s * Hq + h) * D + d, q_dt, 1.0);
+        kbuf[d] = orc_load(q, qrow * D + d, q_dt, 1.0);
     double m = -INFINITY;
     for (int64_t t = 0; t < n; t++) {
         int64_t b = table[t / 16];
@@ -319,6 +318,19 @@ static void orc_attend_one(const uint8_t *k_pool, const uint8_t *v_pool, int poo
     }
     for (int d = 0; d < D; d++)
         out_row[d] /= denom;
+}
+
+/* Decode row: the one query of sequence s (q laid out [S][Hq][D]), head h,
+ * against all ctx[s] tokens of its context. */
+static void orc_attend_one(const uint8_t *k_pool, const uint8_t *v_pool, int pool_dt,
+                           double k_scale, double v_scale, int Hkv, int D,
+                           const uint8_t *q, int q_dt, int Hq, const int32_t *tables,
+                           int MBS, const int32_t *ctx, double scale, int s, int h,
+                           double *out_row, double *score, double *kbuf)
+{
+    int64_t qrow = (int64_t)s * Hq + h;
+    orc_attend_row(k_pool, v_pool, pool_dt, k_scale, v_scale, Hkv, D, q, q_dt, qrow, Hq, h,
+                   tables + (int64_t)s * MBS, ctx[s], scale, out_row, score, kbuf);
 }
 
 /* Decode attention for all (s, h) rows, or for the `num_rows` rows listed in
@@ -365,6 +377,77 @@ int orc_paged_attention(const uint8_t *k_pool, const uint8_t *v_pool, int pool_d
                 orc_attend_one(k_pool, v_pool, pool_dt, (double)k_scale, (double)v_scale,
                                Hkv, D, q, q_dt, Hq, tables, MBS, ctx, (double)scale, s, h,
                                out + r * D, score, kbuf);
+        }
+        free(score);
+        free(kbuf);
+    }
+    return failed ? -2 : 0;
+}
+
+/* ------------------------------------------------ prefill (chunked) attention */
+
+/* Prefill of a chunk of new tokens per sequence.  The chunk of sequence s is
+ * the last n_s = query_start[s+1] - query_start[s] tokens of its ctx[s]-token
+ * context, already written to the pool (the page on the KV cache: the
+ * prompt's K/V is stored first; the Russian page: memory for the input is
+ * allocated first).  Chunk token i sits at position p = ctx[s] - n_s + i and,
+ * as in generation, sees the K/V of itself and every earlier token
+ * (positions 0..p) -- the same attention a decode step with ctx = p + 1
+ * would compute for it.  q and out are [query_start[S]][Hq][D]; a row with
+ * p < 0 (a chunk longer than its context) is zero.
+ * With `rows`, only the listed (chunk row, head) pairs are computed, rows[2i]
+ * being the global chunk-token index and rows[2i+1] the head, and out holds
+ * num_rows x D values.  Each row is computed serially. */
+int orc_prefill_attention(const uint8_t *k_pool, const uint8_t *v_pool, int pool_dt,
+                          float k_scale, float v_scale, int Hkv, int D,
+                          const uint8_t *q, int q_dt, int S, int Hq,
+                          const int32_t *query_start, const int32_t *tables, int MBS,
+                          const int32_t *ctx, float scale, double *out,
+                          const int32_t *rows, int64_t num_rows, int threads)
+{
+    if (Hkv <= 0 || Hq % Hkv != 0 || S < 0)
+        return -1;
+    int64_t total_q = query_start[S];
+    int64_t total = rows ? num_rows : total_q * Hq;
+    int64_t max_n = 1;
+    for (int s = 0; s < S; s++)
+        if (ctx[s] > max_n)
+            max_n = ctx[s];
+#ifdef _OPENMP
+    if (threads > 0)
+        omp_set_num_threads(threads);
+#endif
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *score = (double *)malloc(sizeof(double) * (size_t)max_n);
+        double *kbuf = (double *)malloc(sizeof(double) * (size_t)D);
+        if (!score || !kbuf) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t r = 0; r < total; r++) {
+            int64_t qi;
+            int h;
+            if (rows) {
+                qi = rows[2 * r];
+                h = rows[2 * r + 1];
+            } else {
+                qi = r / Hq;
+                h = (int)(r % Hq);
+            }
+            /* the sequence whose chunk holds global chunk token qi */
+            int s = 0;
+            while (s < S - 1 && query_start[s + 1] <= qi)
+                s++;
+            int64_t n_new = query_start[s + 1] - query_start[s];
+            int64_t i = qi - query_start[s];
+            int64_t pos = (int64_t)ctx[s] - n_new + i;
+            if (score && kbuf)
+                orc_attend_row(k_pool, v_pool, pool_dt, (double)k_scale, (double)v_scale, Hkv, D,
+                               q, q_dt, qi * Hq + h, Hq, h, tables + (int64_t)s * MBS, pos + 1,
+                               (double)scale, out + r * D, score, kbuf);
         }
         free(score);
         free(kbuf);

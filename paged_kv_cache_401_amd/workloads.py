@@ -43,7 +43,9 @@ from .blocks import BlockManager, blocks_for
 F32, BF16, FP8 = 0, 1, 2
 TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16}
 CONFIG_IDS = ("tiny", "mha13b", "gqa70b", "sampling_a", "sampling_b", "fp8")
-SEEDS = {"tiny": 0, "mha13b": 1, "gqa70b": 2, "sampling_a": 3, "sampling_b": 3, "fp8": 4}
+PREFILL_IDS = ("prefill_gqa70b", "prefill_mha13b", "chunked_gqa70b", "chunked_fp8")
+SEEDS = {"tiny": 0, "mha13b": 1, "gqa70b": 2, "sampling_a": 3, "sampling_b": 3, "fp8": 4,
+         "prefill_gqa70b": 5, "prefill_mha13b": 6, "chunked_gqa70b": 7, "chunked_fp8": 8}
 
 
 @dataclass
@@ -71,6 +73,11 @@ class Workload:
     step_k: torch.Tensor | None = None
     step_v: torch.Tensor | None = None
     step_slots: np.ndarray | None = None
+    # prefill: each sequence's chunk of new tokens is the last
+    # query_start[s+1] - query_start[s] tokens of its context; prefill_q holds
+    # their queries, [query_start[S]][Hq][D]
+    query_start: np.ndarray | None = None
+    prefill_q: torch.Tensor | None = None
     info: dict = field(default_factory=dict)
 
     @property
@@ -85,6 +92,23 @@ class Workload:
         """Algorithmic K+V bytes one decode pass reads: sum ctx * Hkv * D * 2 * elem."""
         eb = {F32: 4, BF16: 2, FP8: 1}[self.pool_dtype]
         return int(self.context_lens.astype(np.int64).sum()) * self.Hkv * self.D * 2 * eb
+
+    def prefill_flops(self) -> int:
+        """Algorithmic flops of one causal prefill pass: every (chunk token,
+        query head) row does 2 D flops for q.K and 2 D for P.V per token it
+        sees (positions 0..p)."""
+        total = 0
+        for s in range(self.S):
+            n = int(self.query_start[s + 1] - self.query_start[s])
+            c = int(self.context_lens[s])
+            first = c - n + 1   # tokens seen by the chunk's first row
+            total += n * first + n * (n - 1) // 2
+        return total * self.Hq * 4 * self.D
+
+    def prefill_kv_bytes(self) -> int:
+        """K+V bytes of every context token of every sequence (each read at
+        least once by a prefill pass)."""
+        return self.kv_bytes()
 
     def unique_kv_bytes(self) -> int:
         """K+V bytes of distinct physical token slots one decode pass reads (shared
@@ -189,6 +213,56 @@ def make_workload(name: str, small: bool = False, device="cpu", seed: int | None
     if name in ("sampling_a", "sampling_b"):
         return _sampling(name, small, device, seed, rng, num_seqs)
     raise KeyError(name)
+
+
+def make_prefill_workload(name: str, small: bool = False, device="cpu",
+                          seed: int | None = None) -> Workload:
+    """Prefill workloads: every sequence's context is in the pool (one bulk
+    write) and its last ``n_new`` tokens form the chunk whose queries attend
+    causally over the context.
+
+    - ``prefill_gqa70b``: whole prompts (chunk = context) with the 70B-like
+      heads (64 q / 8 KV, head dim 128, bf16): 8 prompts of 4096 tokens,
+      the French page's per-user sequence length.
+    - ``prefill_mha13b``: whole prompts with LLaMA-13B heads (40 / 40): 8
+      prompts of 2048 tokens.
+    - ``chunked_gqa70b``: chunked prefill, 70B-like heads: 32 sequences with
+      a cached prefix uniform in [0, 3584] tokens and a 512-token chunk.
+    - ``chunked_fp8``: the same with an E4M3 cache (per-pool scales).
+    ``small`` keeps the heads but uses 2-3 short, ragged sequences.
+    """
+    if seed is None:
+        seed = SEEDS[name]
+    rng = np.random.default_rng(seed)
+    scale = _f32(1.0 / math.sqrt(128))
+    if name == "prefill_gqa70b":
+        Hq, Hkv, pool_dt = 64, 8, BF16
+        n_new = np.array([77, 300, 16]) if small else np.full(8, 4096)
+        prefix = np.zeros_like(n_new)
+    elif name == "prefill_mha13b":
+        Hq, Hkv, pool_dt = 40, 40, BF16
+        n_new = np.array([150, 33]) if small else np.full(8, 2048)
+        prefix = np.zeros_like(n_new)
+    elif name in ("chunked_gqa70b", "chunked_fp8"):
+        Hq, Hkv = 64, 8
+        pool_dt = FP8 if name == "chunked_fp8" else BF16
+        S = 3 if small else 32
+        n_new = np.full(S, 40 if small else 512)
+        prefix = rng.integers(0, 200 if small else 3585, size=S)
+        if small:
+            prefix[0] = 0
+    else:
+        raise KeyError(name)
+    ctx = (prefix + n_new).astype(np.int32)
+    w = _simple(name, len(ctx), Hq, Hkv, 128, ctx, pool_dt, BF16, BF16, scale, seed, device,
+                rng, fp8_scales=pool_dt == FP8)
+    qs = np.zeros(len(ctx) + 1, dtype=np.int32)
+    qs[1:] = np.cumsum(n_new)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed + 1000)
+    w.query_start = qs
+    w.prefill_q = _randn(gen, (int(qs[-1]), Hq, 128), torch.bfloat16, device)
+    return w
 
 
 def _sampling(name, small, device, seed, rng, num_prompts=None) -> Workload:

@@ -12,6 +12,7 @@ import pytest
 
 import oracle
 import test_oracle_pins as pins
+import test_oracle_prefill_pins as prefill_pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "pa_oracle.c")
 
@@ -22,13 +23,20 @@ MUTATIONS = {
     "wrong_slot_in_block": ("int o = (int)(t % 16);\n        double dot", "int o = (int)((t + 1) % 16);\n        double dot"),
     "wrong_value_row": ("out_row[d] += w * orc_load(v_pool, orc_v_offset(b, g, o, d,",
                         "out_row[d] += w * orc_load(v_pool, orc_v_offset(b, g, (o + 1) % 16, d,"),
-    "query_index_transposed": ("kbuf[d] = orc_load(q, ((int64_t)s * Hq + h) * D + d",
-                               "kbuf[d] = orc_load(q, ((int64_t)h * 1 + s) * D + d"),
+    "query_index_transposed": ("int64_t qrow = (int64_t)s * Hq + h;",
+                               "int64_t qrow = (int64_t)h * 1 + s;"),
     "fp8_ties_up": ("c = (lo % 2 == 0) ? lo : hi;", "c = hi;"),
     "fp8_subnormal_exponent": ("mag = ldexp((double)m, -9);", "mag = ldexp((double)m, -10);"),
     "fp8_no_saturation": ("if (a >= orc_fp8_mag[126])\n        return (uint8_t)(sign | 0x7E);",
                           "if (a >= orc_fp8_mag[126])\n        return (uint8_t)(sign | 0x7F);"),
     "scatter_skips_offset": ("int t = slot % 16;", "int t = slot % 15;"),
+    "prefill_excludes_own_token": ("tables + (int64_t)s * MBS, pos + 1,",
+                                   "tables + (int64_t)s * MBS, pos,"),
+    "prefill_not_causal": ("tables + (int64_t)s * MBS, pos + 1,",
+                           "tables + (int64_t)s * MBS, (int64_t)ctx[s],"),
+    "prefill_ignores_cached_prefix": ("int64_t pos = (int64_t)ctx[s] - n_new + i;",
+                                      "int64_t pos = i;"),
+    "prefill_query_rows_transposed": ("q, q_dt, qi * Hq + h, Hq, h,", "q, q_dt, qi + h * Hq, Hq, h,"),
 }
 
 PIN_TESTS = [
@@ -44,6 +52,9 @@ PIN_TESTS = [
     pins.test_fp8_encode_matches_torch_cast_below_overflow,
     pins.test_fp8_encode_saturates_and_keeps_nan,
     pins.test_fp8_scatter_encodes_scaled_values,
+    lambda: prefill_pins.test_prefill_equals_dense_causal_library_softmax("chunked_gqa70b"),
+    lambda: prefill_pins.test_each_chunk_row_equals_decode_at_its_position("chunked_gqa70b"),
+    prefill_pins.test_causality_future_tokens_do_not_matter,
 ]
 
 
