@@ -1,7 +1,7 @@
 /*
  * pa.h -- C ABI of the MI355X (gfx950) paged KV cache library (libpa.so).
  *
- * Three operations on a pool of fixed-size KV blocks, as the source pages
+ * Four operations on a pool of fixed-size KV blocks, as the source pages
  * state the problem:
  *   - pa_reshape_and_cache: write new tokens' K/V into their slots
  *     ("PagedAttention" glossary page (Ultralytics), how paging works, and the
@@ -18,6 +18,10 @@
  *     placement), with query heads grouped over shared KV heads (glossary
  *     page, related techniques: grouped-query attention).  The pages print no
  *     formula; the operation is softmax(scale * q K^T) V over the ctx tokens.
+ *   - pa_prefill: the same attention for a chunk of new tokens per sequence,
+ *     each attending causally to itself and every earlier token (glossary
+ *     page, related techniques: FlashAttention-style kernels that read paged
+ *     blocks).
  *
  * Conventions for every entry point
  *   - Pointers are device pointers unless stated; the caller owns every
@@ -126,6 +130,36 @@ int pa_decode(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t num
               void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * pa_prefill -- causal (chunked) prefill attention over the paged pool.
+ * Each sequence's chunk of new tokens is the last
+ * n_s = query_start[s+1] - query_start[s] tokens of its context; their K/V
+ * must already be in the pool (pa_reshape_and_cache), as the pages describe
+ * the prompt's K/V being stored before generation continues (French page,
+ * second article, "what is the KV cache"; Russian page: memory for the input
+ * is allocated first).  Chunk token i of sequence s sits at position
+ * p = context_lens[s] - n_s + i and attends to tokens 0..p of its context,
+ * read through its block table -- the FlashAttention-style kernel reading
+ * paged blocks of the glossary page's related techniques.  Row (token, h)
+ * equals what pa_decode computes for that token's query over a context of
+ * p + 1 tokens.
+ *   q              bf16 [query_start[num_seqs]][num_q_heads][head_dim]
+ *                  (16-byte aligned).
+ *   query_start    int32 [num_seqs + 1], non-decreasing, query_start[0] = 0.
+ *   max_query_len  host-side upper bound of every n_s (sizes the grid);
+ *                  chunk tokens beyond it are not computed.  0 is a no-op.
+ *   block_tables, max_blocks_per_seq, context_lens, scale: as for pa_decode.
+ *   out            fp32 [query_start[num_seqs]][num_q_heads][head_dim]
+ *                  (16-byte aligned).  A row whose position is negative (a
+ *                  chunk longer than its context) is written as zeros.
+ * Pools: PA_BF16 or PA_FP8_E4M3 (PA_ERR_UNSUPPORTED for fp32); q_dtype must
+ * be PA_BF16.  Cache entries inside each context must be finite.
+ */
+int pa_prefill(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t num_seqs,
+               int32_t num_q_heads, const int32_t *query_start, int32_t max_query_len,
+               const int32_t *block_tables, int32_t max_blocks_per_seq,
+               const int32_t *context_lens, float scale, float *out, void *stream);
+
+/*
  * pa_reshape_and_cache -- write num_tokens new tokens into the pool.
  *   k, v           [num_tokens][num_kv_heads][head_dim] of kv_dtype: the pool's
  *                  dtype for 16/32-bit pools; PA_BF16 or PA_F32 for an FP8 pool.
@@ -153,9 +187,10 @@ int pa_copy_blocks(const pa_pool_t *pool, const int32_t *src_dst_pairs, int32_t 
  * negative pa_status on invalid arguments. */
 int pa_decode_variant(const pa_pool_t *pool, int32_t num_q_heads);
 
-/* Measurement aid: the next pa_decode call on this host thread records
- * `before` (a hipEvent_t) just before its partition kernel and `after` just
- * after it, on the call's stream.  Pass NULLs to clear. */
+/* Measurement aid: the next pa_decode or pa_prefill call on this host
+ * thread records `before` (a hipEvent_t) just before its partition (or
+ * prefill) kernel and `after` just after it, on the call's stream.  Pass
+ * NULLs to clear. */
 int pa_set_profile_events(void *before, void *after);
 
 /* Measurement aid: enqueue one streaming read of `bytes` bytes (rounded down

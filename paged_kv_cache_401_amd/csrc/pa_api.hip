@@ -211,6 +211,62 @@ int pa_decode(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t num
     return ok();
 }
 
+int pa_prefill(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t num_seqs,
+               int32_t num_q_heads, const int32_t *query_start, int32_t max_query_len,
+               const int32_t *block_tables, int32_t max_blocks_per_seq,
+               const int32_t *context_lens, float scale, float *out, void *stream) {
+    int rc = check_pool(pool);
+    if (rc != PA_OK) return rc;
+    rc = check_heads(pool, num_seqs, num_q_heads, max_blocks_per_seq);
+    if (rc != PA_OK) return rc;
+    const int group = num_q_heads / pool->num_kv_heads;
+    if (!pa::prefill_supported(pool->kv_dtype, pool->head_dim, group))
+        return fail(PA_ERR_UNSUPPORTED,
+                    "prefill needs a bf16 or fp8 pool and a query group the kernel tiles (kv_dtype %d, group %d)",
+                    pool->kv_dtype, group);
+    if (q_dtype != PA_BF16) return fail(PA_ERR_DTYPE, "prefill q_dtype must be PA_BF16, got %d", q_dtype);
+    if (!isfinite(scale)) return fail(PA_ERR_RANGE, "scale is not finite");
+    if (max_query_len < 0) return fail(PA_ERR_SHAPE, "max_query_len %d is negative", max_query_len);
+    if (num_seqs == 0 || max_query_len == 0) return ok();
+    if (!q || !query_start || !block_tables || !context_lens || !out)
+        return fail(PA_ERR_NULL, "q, query_start, block_tables, context_lens and out must be non-NULL");
+    if (!aligned16(q) || !aligned16(out)) return fail(PA_ERR_ALIGN, "q and out must be 16-byte aligned");
+
+    pa::PrefillParams p{};
+    p.k_pool = pool->k_pool;
+    p.v_pool = pool->v_pool;
+    p.q = q;
+    p.out = out;
+    p.block_tables = block_tables;
+    p.context_lens = context_lens;
+    p.query_start = query_start;
+    p.num_blocks = pool->num_blocks;
+    p.num_kv_heads = pool->num_kv_heads;
+    p.num_q_heads = num_q_heads;
+    p.group = group;
+    p.num_seqs = num_seqs;
+    p.max_blocks_per_seq = max_blocks_per_seq;
+    p.max_query_len = max_query_len;
+    const int tile = pa::prefill_tile_tokens(pool->head_dim, group);
+    p.num_tiles = (max_query_len + tile - 1) / tile;
+    const double kscale = pool->kv_dtype == PA_FP8_E4M3 ? (double)pool->k_scale : 1.0;
+    p.qk_scale_log2 = (float)((double)scale * kscale * 1.4426950408889634);
+    p.out_scale = pool->kv_dtype == PA_FP8_E4M3 ? pool->v_scale : 1.0f;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (g_ev_before) {
+        hipError_t e = hipEventRecord(g_ev_before, st);
+        if (e != hipSuccess) return fail(PA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+    }
+    hipError_t e = pa::launch_prefill(pool->kv_dtype, pool->head_dim, p, st);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "prefill kernel: %s", hipGetErrorString(e));
+    if (g_ev_after) {
+        e = hipEventRecord(g_ev_after, st);
+        if (e != hipSuccess) return fail(PA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+    }
+    g_ev_before = g_ev_after = nullptr;
+    return ok();
+}
+
 int pa_reshape_and_cache(const pa_pool_t *pool, const void *k, const void *v, int32_t kv_dtype,
                          const int32_t *slot_mapping, int32_t num_tokens, void *stream) {
     int rc = check_pool(pool);
@@ -290,7 +346,8 @@ const char *pa_last_error(void) { return g_last_error; }
 
 const char *pa_build_info(void) {
     return "libpa gfx950: decode (vector-ALU partition kernel, matrix-core GQA kernel, split-K "
-           "reduce), reshape_and_cache (fp32/bf16/fp8-e4m3), copy_blocks";
+           "reduce), causal chunked prefill (matrix-core), reshape_and_cache (fp32/bf16/fp8-e4m3), "
+           "copy_blocks";
 }
 
 }  // extern "C"

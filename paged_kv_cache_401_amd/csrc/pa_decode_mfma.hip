@@ -34,33 +34,12 @@
 //   Tokens past the context are excluded by selection: their scores are set
 //     to -inf and their V operand elements to zero before the product.
 #include "pa_internal.h"
+#include "pa_mfma_util.h"
 
 namespace pa {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-constexpr float kNegInf = -__builtin_inff();
-
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
-
-// four fp8 codes (one 32-bit word) -> four bf16 in two words (exact)
-__device__ __forceinline__ void e4m3x4_to_bf16(uint32_t w, uint32_t &lo, uint32_t &hi) {
-    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
-    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
-    lo = __builtin_bit_cast(uint32_t, a);
-    hi = __builtin_bit_cast(uint32_t, b);
-}
-
-// p = hi + lo with hi = p truncated to bf16 and lo = the remainder truncated to bf16
-__device__ __forceinline__ void split_bf16(float p, uint32_t &hi, uint32_t &lo) {
-    const uint32_t u = __float_as_uint(p);
-    hi = u >> 16;
-    lo = __float_as_uint(p - __uint_as_float(u & 0xffff0000u)) >> 16;
-}
+constexpr float kNegInf = kNegInfF;
 
 template <int KV, int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void decode_mfma_kernel(DecodeParams p) {
@@ -181,26 +160,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         }
 
         // P^T operand: [hi(p0..p3) | lo(p0..p3)]
-        u32x4 pw;
-        {
-            uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
-            split_bf16(pr[0], h0, l0);
-            split_bf16(pr[1], h1, l1);
-            split_bf16(pr[2], h2, l2);
-            split_bf16(pr[3], h3, l3);
-            pw[0] = h0 | (h1 << 16);
-            pw[1] = h2 | (h3 << 16);
-            pw[2] = l0 | (l1 << 16);
-            pw[3] = l2 | (l3 << 16);
-        }
-        const bf16x8 pop = as_bf16x8(pw);
+        const bf16x8 pop = p_operand_hi_lo(pr);
 
         // zero the V elements of tokens past the context (last block only)
         uint32_t keep01 = 0xffffffffu, keep23 = 0xffffffffu;
-        if (nvalid < kBlock) {
-            keep01 = (4 * c + 0 < nvalid ? 0x0000ffffu : 0u) | (4 * c + 1 < nvalid ? 0xffff0000u : 0u);
-            keep23 = (4 * c + 2 < nvalid ? 0x0000ffffu : 0u) | (4 * c + 3 < nvalid ? 0xffff0000u : 0u);
-        }
+        if (nvalid < kBlock) v_keep_masks(c, nvalid, keep01, keep23);
 
         // O^T += V^T . P^T, one MFMA per 16 x 16 tile
 #pragma unroll

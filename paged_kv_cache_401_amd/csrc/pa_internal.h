@@ -35,6 +35,26 @@ struct DecodeParams {
     float out_scale;           // v_scale (1 for 16/32-bit pools)
 };
 
+struct PrefillParams {
+    const void *k_pool;
+    const void *v_pool;
+    const void *q;             // bf16 [total chunk tokens][Hq][D]
+    float *out;                // [total chunk tokens][Hq][D]
+    const int32_t *block_tables;
+    const int32_t *context_lens;
+    const int32_t *query_start;  // [S + 1]
+    int32_t num_blocks;
+    int32_t num_kv_heads;
+    int32_t num_q_heads;
+    int32_t group;
+    int32_t num_seqs;
+    int32_t max_blocks_per_seq;
+    int32_t max_query_len;
+    int32_t num_tiles;         // ceil(max_query_len / tile tokens)
+    float qk_scale_log2;
+    float out_scale;
+};
+
 struct CacheParams {
     void *k_pool;
     void *v_pool;
@@ -53,6 +73,9 @@ hipError_t launch_decode_valu(int kv, int head_dim, const DecodeParams &p, hipSt
 hipError_t launch_decode_mfma(int kv, int head_dim, const DecodeParams &p, hipStream_t stream);
 bool mfma_path_supported(int kv, int head_dim, int group);
 hipError_t launch_decode_reduce(int head_dim, const DecodeParams &p, hipStream_t stream);
+bool prefill_supported(int kv, int head_dim, int group);
+int prefill_tile_tokens(int head_dim, int group);  // chunk tokens per prefill workgroup
+hipError_t launch_prefill(int kv, int head_dim, const PrefillParams &p, hipStream_t stream);
 hipError_t launch_reshape_and_cache(int pool_kv, int in_kv, int head_dim, const CacheParams &p,
                                     hipStream_t stream);
 hipError_t launch_copy_blocks(void *k_pool, void *v_pool, const int32_t *pairs, int32_t num_pairs,

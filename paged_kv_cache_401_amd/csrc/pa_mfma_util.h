@@ -1,0 +1,64 @@
+// pa_mfma_util.h -- operand helpers shared by the matrix-core kernels
+// (grouped-query decode and prefill) for gfx950's v_mfma_f32_16x16x32_bf16.
+//
+// Operand layouts of that instruction (lane = 16 c + n):
+//   A (16 x 32): lane holds A[row n][8 c .. 8 c + 7]
+//   B (32 x 16): lane holds B[8 c .. 8 c + 7][column n]
+//   C (16 x 16): lane holds C[4 c .. 4 c + 3][column n]
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kNegInfF = -__builtin_inff();
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// four fp8 E4M3FN codes (one word) -> four bf16 in two words (exact):
+// lo = codes 0, 1 and hi = codes 2, 3
+__device__ __forceinline__ void e4m3x4_to_bf16(uint32_t w, uint32_t &lo, uint32_t &hi) {
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+    lo = __builtin_bit_cast(uint32_t, a);
+    hi = __builtin_bit_cast(uint32_t, b);
+}
+
+// p = hi + lo with hi = p truncated to bf16 and lo = the remainder truncated
+// to bf16: together they carry p to 16 significant bits
+__device__ __forceinline__ void split_bf16(float p, uint32_t &hi, uint32_t &lo) {
+    const uint32_t u = __float_as_uint(p);
+    hi = u >> 16;
+    lo = __float_as_uint(p - __uint_as_float(u & 0xffff0000u)) >> 16;
+}
+
+// The P^T operand [hi(p0..p3) | lo(p0..p3)] of a 32-deep contraction that
+// multiplies it against [V | V] (tokens 4c..4c+3 twice)
+__device__ __forceinline__ bf16x8 p_operand_hi_lo(const float (&pr)[4]) {
+    uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
+    split_bf16(pr[0], h0, l0);
+    split_bf16(pr[1], h1, l1);
+    split_bf16(pr[2], h2, l2);
+    split_bf16(pr[3], h3, l3);
+    u32x4 pw;
+    pw[0] = h0 | (h1 << 16);
+    pw[1] = h2 | (h3 << 16);
+    pw[2] = l0 | (l1 << 16);
+    pw[3] = l2 | (l3 << 16);
+    return as_bf16x8(pw);
+}
+
+// Keep masks for the bf16 pairs (tokens 4c, 4c+1) and (4c+2, 4c+3) of a V
+// cell: all ones for tokens below `nvalid`, zero above
+__device__ __forceinline__ void v_keep_masks(int c, int nvalid, uint32_t &keep01, uint32_t &keep23) {
+    keep01 = (4 * c + 0 < nvalid ? 0x0000ffffu : 0u) | (4 * c + 1 < nvalid ? 0xffff0000u : 0u);
+    keep23 = (4 * c + 2 < nvalid ? 0x0000ffffu : 0u) | (4 * c + 3 < nvalid ? 0xffff0000u : 0u);
+}
+
+}  // namespace pa

@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 
 # every symbol include/pa.h declares
 EXPORTS = ("pa_pool_bytes", "pa_decode_partition_tokens", "pa_decode_workspace_size", "pa_decode",
-           "pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_variant", "pa_set_profile_events",
+           "pa_prefill", "pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_variant", "pa_set_profile_events",
            "pa_probe_read", "pa_strerror", "pa_last_error", "pa_build_info")
 
 
@@ -62,6 +62,8 @@ def lib() -> ctypes.CDLL:
     L.pa_decode_workspace_size.restype = SZ
     L.pa_decode.argtypes = [PD, P, I32, I32, I32, P, I32, P, F, P, I32, P, SZ, P]
     L.pa_decode.restype = ctypes.c_int
+    L.pa_prefill.argtypes = [PD, P, I32, I32, I32, P, I32, P, I32, P, F, P, P]
+    L.pa_prefill.restype = ctypes.c_int
     L.pa_reshape_and_cache.argtypes = [PD, P, P, I32, P, I32, P]
     L.pa_reshape_and_cache.restype = ctypes.c_int
     L.pa_copy_blocks.argtypes = [PD, P, I32, P]
@@ -191,6 +193,32 @@ def decode(pool: KVPool, q: torch.Tensor, block_tables: torch.Tensor, context_le
                            _dev(context_lens, "context_lens", torch.int32), float(scale),
                            _dev(out, "out", torch.float32), int(partition_tokens), wptr, wbytes,
                            _stream(stream)))
+    return out
+
+
+def prefill(pool: KVPool, q: torch.Tensor, query_start: torch.Tensor, max_query_len: int,
+            block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+            out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Causal prefill of each sequence's chunk (its last query_start[s+1] -
+    query_start[s] context tokens); q is bf16 [total][Hq][D]."""
+    T, Hq, D = q.shape
+    if D != pool.head_dim:
+        raise ValueError("q head dim %d differs from the pool's %d" % (D, pool.head_dim))
+    S = context_lens.numel()
+    if query_start.numel() != S + 1:
+        raise ValueError("query_start must hold num_seqs + 1 offsets")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError("block_tables must be [num_seqs][max_blocks]")
+    if q.dtype != torch.bfloat16:
+        raise TypeError("prefill q must be bfloat16")
+    if out is None:
+        out = torch.empty((T, Hq, D), dtype=torch.float32, device=q.device)
+    d = pool.desc()
+    _check(lib().pa_prefill(ctypes.byref(d), _dev(q, "q"), BF16, S, Hq,
+                            _dev(query_start, "query_start", torch.int32), int(max_query_len),
+                            _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+                            _dev(context_lens, "context_lens", torch.int32), float(scale),
+                            _dev(out, "out", torch.float32), _stream(stream)))
     return out
 
 

@@ -122,3 +122,25 @@ def test_strerror_and_profile_events():
     assert L.pa_probe_read(None, 64, 16, None) == -1
     assert L.pa_probe_read(17, 64, 16, None) == -6
     assert L.pa_probe_read(16, 8, 16, None) == -3
+
+
+def test_prefill_argument_rules():
+    L = ops.lib()
+    d = desc()
+    args = lambda **kw: dict(dict(q=16, qdt=ops.BF16, S=1, Hq=8, qs=16, mql=4, bt=16, mbs=4,
+                                  ctx=16, scale=0.1, out=16), **kw)
+
+    def call(pool=d, **kw):
+        a = args(**kw)
+        return L.pa_prefill(ctypes.byref(pool), a["q"], a["qdt"], a["S"], a["Hq"], a["qs"],
+                            a["mql"], a["bt"], a["mbs"], a["ctx"], a["scale"], a["out"], None)
+
+    assert call(pool=desc(kv_dtype=ops.F32)) == -4          # fp32 pool: no matrix-core prefill
+    assert call(qdt=ops.F32) == -2                           # q must be bf16
+    assert call(Hq=12) == -3                                 # Hq % Hkv != 0
+    assert call(mql=-1) == -3
+    assert call(q=None) == -1
+    assert call(out=17) == -6                                # misaligned out
+    assert call(scale=float("inf")) == -8
+    assert call(mql=0, q=None, qs=None, bt=None, ctx=None, out=None) == 0   # nothing to do
+    assert call(S=0, q=None, qs=None, bt=None, ctx=None, out=None) == 0
