@@ -40,7 +40,26 @@ WORKLOAD_TEXT = {
     "sampling_b": "parallel sampling with copy-on-write: 64 prompts x 3 samples, 1016-token shared "
                   "prompts + 0..512 private tokens, 40 q / 8 KV heads, head_dim 128, bf16",
     "tiny": "worked example: 1 seq x 40 tokens, 1 head, head_dim 64, fp32, 3 random blocks of 64",
+    "prefill_gqa70b": "causal prefill of 8 whole 4096-token prompts, 64 q / 8 KV heads, head_dim 128, "
+                      "bf16 KV in scattered 16-token blocks",
+    "prefill_mha13b": "causal prefill of 8 whole 2048-token prompts, 40 heads, head_dim 128, bf16 KV",
+    "chunked_gqa70b": "chunked prefill: 32 seqs, cached prefix uniform [0, 3584] + 512-token chunk, "
+                      "64 q / 8 KV heads, head_dim 128, bf16 KV",
+    "chunked_fp8": "chunked prefill: 32 seqs, cached prefix uniform [0, 3584] + 512-token chunk, "
+                   "64 q / 8 KV heads, head_dim 128, e4m3 KV, bf16 q",
 }
+WORKLOAD_TEXT["beam"] = ("beam search: 64 requests x 8 beams over shared 1000-token prompts after 40 "
+                         "steps of forks and copy-on-write, 64 q / 8 KV heads, head_dim 128, bf16; "
+                         "a step copies the last step's ~176 shared partial blocks")
+WORKLOAD_TEXT["swap"] = ("block swap: 16 of 64 sequences x 4096 tokens (70B-like: 8 KV heads, head_dim "
+                         "128, bf16) moved block by block to pinned host memory and back: 4096 "
+                         "blocks x 32 KiB for K and for V")
+WORKLOAD_TEXT["prefix"] = ("prefix caching by full-block hashing: 128 requests over 8 system prompts "
+                           "(64..2048 tokens) + 16..512 private tokens, 64 q / 8 KV heads, head_dim "
+                           "128, bf16; prompt processing = cache write + causal prefill of each "
+                           "request's uncached tokens over its (partly cached) context")
+PREFILL = ("prefill_gqa70b", "prefill_mha13b", "chunked_gqa70b", "chunked_fp8")
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 DTYPE_NAME = {0: "f32", 1: "bf16", 2: "fp8e4m3"}
 
 
@@ -49,7 +68,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="gqa70b", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--workload", default="gqa70b", choices=sorted(WORKLOAD_TEXT),
+                    help="decode workload (default: the 70B-like GQA layer) or a prefill one")
     ap.add_argument("--partition-tokens", type=int, default=None,
                     help="split-K partition length (default: the workload's, else auto)")
     ap.add_argument("--cpu-seqs", type=int, default=None,
@@ -108,6 +128,15 @@ def main():
               "(the decode hot path shards by sequence or KV head with no exchange; "
               "see the design notes).", file=sys.stderr)
         sys.exit(2)
+    if args.workload in PREFILL:
+        run_prefill(args)
+        return
+    if args.workload == "swap":
+        run_swap(args)
+        return
+    if args.workload == "prefix":
+        run_prefix(args)
+        return
 
     import numpy as np
     import torch
@@ -141,12 +170,15 @@ def main():
         step_slots = torch.as_tensor(w.step_slots, dtype=torch.int32, device=dev)
     else:
         step_k = step_v = step_slots = None
-    no_pairs = torch.zeros((0, 2), dtype=torch.int32, device=dev)
+    # the step's copy-on-write pairs (beam search: the last step's; else none)
+    sp = w.info.get("step_pairs")
+    step_pairs = torch.as_tensor(np.zeros((0, 2), np.int32) if sp is None else sp,
+                                 dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
     setup_s = time.time() - t0
 
     def step():
-        ops.copy_blocks(pool, no_pairs)
+        ops.copy_blocks(pool, step_pairs)
         if step_slots is not None:
             ops.reshape_and_cache(pool, step_k, step_v, step_slots)
         ops.decode(pool, q, tables, ctx, w.scale, out=out, partition_tokens=ptok,
@@ -168,7 +200,7 @@ def main():
     wall0 = time.perf_counter()
     step_begin.record(stream)
     for i in range(args.steps):
-        ops.copy_blocks(pool, no_pairs)
+        ops.copy_blocks(pool, step_pairs)
         if step_slots is not None:
             ops.reshape_and_cache(pool, step_k, step_v, step_slots)
         ops.set_profile_events(evs[2 * i], evs[2 * i + 1])
@@ -186,6 +218,21 @@ def main():
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
     kernel_name = ops.decode_variant(pool, w.Hq)
     traffic = traffic_for(args.workload, kernel_name, kv_bytes)
+
+    copy_rec = None
+    if step_pairs.shape[0]:
+        # the copy-on-write kernel alone: read + write bytes of K and V blocks
+        cb, ce = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        cb.record(stream)
+        for _ in range(args.steps):
+            ops.copy_blocks(pool, step_pairs)
+        ce.record(stream)
+        torch.cuda.synchronize()
+        copy_ms = cb.elapsed_time(ce) / args.steps
+        block_bytes = pool.nbytes // w.num_blocks
+        moved = 2 * 2 * int(step_pairs.shape[0]) * block_bytes
+        copy_rec = {"pairs": int(step_pairs.shape[0]), "block_bytes_per_pool": block_bytes,
+                    "ms": round(copy_ms, 5), "read_plus_write_GBps": round(moved / copy_ms / 1e6, 1)}
 
     # the read bandwidth this GPU sustains on a plain streaming read of the K pool
     sink = torch.zeros(16, dtype=torch.uint8, device=dev)
@@ -232,10 +279,336 @@ def main():
                      "algorithmic_bytes_per_launch": kv_bytes},
         "setup_s": round(setup_s, 2),
     }
+    if copy_rec is not None:
+        rec["copy_blocks"] = copy_rec
     if not args.no_cpu_baseline:
         rec["cpu_baseline"], rec["max_abs_err_vs_oracle_sample"] = cpu_baseline(
             w, args, out, pool)
     print(json.dumps(rec), flush=True)
+
+
+def run_prefill(args):
+    """One prefill step: write every sequence's chunk of new tokens into its
+    slots, then causal prefill attention of the chunks over their contexts.
+    ``value`` is algorithmic TFLOP/s of the step (sum over chunk rows and
+    heads of 4 D flops per token seen); ``roofline`` is the prefill kernel
+    alone against the bf16 matrix-core peak."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_401_amd import ops
+    from paged_kv_cache_401_amd import workloads as wl
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    t0 = time.time()
+    w = wl.make_prefill_workload(args.workload, small=False, device=dev)
+    pool = ops.KVPool(w.num_blocks, w.Hkv, w.D, w.pool_dtype, device=dev, k_scale=w.k_scale,
+                      v_scale=w.v_scale, fill=0)
+    _, k, v, slots = w.ops[0]
+    slots_t = torch.as_tensor(slots, dtype=torch.int32, device=dev)
+    ops.reshape_and_cache(pool, k, v, slots_t)          # the cached prefixes (and chunks)
+    # the step's cache write: the chunk tokens, the last n of each context
+    off = np.concatenate([[0], np.cumsum(w.context_lens.astype(np.int64))])
+    n_new = np.diff(w.query_start)
+    idx = np.concatenate([np.arange(off[s + 1] - n_new[s], off[s + 1]) for s in range(w.S)])
+    it = torch.as_tensor(idx, device=dev)
+    ck, cv = k.index_select(0, it), v.index_select(0, it)
+    cslots = slots_t.index_select(0, it)
+    q = w.prefill_q
+    qs = torch.as_tensor(w.query_start, dtype=torch.int32, device=dev)
+    bt = torch.as_tensor(w.block_tables, dtype=torch.int32, device=dev)
+    ctx = torch.as_tensor(w.context_lens, dtype=torch.int32, device=dev)
+    mql = int(n_new.max())
+    out = torch.empty((q.shape[0], w.Hq, w.D), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    setup_s = time.time() - t0
+
+    for _ in range(args.warmup):
+        ops.reshape_and_cache(pool, ck, cv, cslots)
+        ops.prefill(pool, q, qs, mql, bt, ctx, w.scale, out=out)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+    for e in evs:
+        e.record(stream)
+    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    b0.record(stream)
+    for i in range(args.steps):
+        ops.reshape_and_cache(pool, ck, cv, cslots)
+        ops.set_profile_events(evs[2 * i], evs[2 * i + 1])
+        ops.prefill(pool, q, qs, mql, bt, ctx, w.scale, out=out)
+    b1.record(stream)
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - wall0
+    ms_step = b0.elapsed_time(b1) / args.steps
+    kern = [evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(args.steps)]
+    kern_ms = float(np.mean(kern))
+    flops = w.prefill_flops()
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    value = flops / (ms_step * 1e-3) / 1e12
+    tokens = int(w.query_start[-1])
+    rec = {
+        "metric": "pa_prefill TFLOP/s (algorithmic, causal) at 1 MI355X",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": DTYPE_NAME[w.pool_dtype],
+        "data": "synthetic (seeded N(0,1) q/K/V, scattered 16-token blocks)",
+        "config": {"workload": WORKLOAD_TEXT[args.workload], "num_seqs": w.S,
+                   "num_q_heads": w.Hq, "num_kv_heads": w.Hkv, "head_dim": w.D,
+                   "chunk_tokens": tokens, "total_context_tokens": int(w.context_lens.sum()),
+                   "algorithmic_flops": flops, "parallelism": "single GPU"},
+        "prefill_tokens_per_s": round(tokens / (ms_step * 1e-3), 1),
+        "prefill_kernel_ms": round(kern_ms, 5),
+        "prefill_kernel_ms_min": round(float(np.min(kern)), 5),
+        "wall_ms_per_step": round(1e3 * wall_s / args.steps, 5),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "prefill_mfma_kernel", "algorithmic_flops_per_launch": flops},
+        "setup_s": round(setup_s, 2),
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"], rec["max_abs_err_vs_oracle_sample"] = prefill_cpu_baseline(
+            w, args, out)
+    print(json.dumps(rec), flush=True)
+
+
+def run_prefix(args):
+    """Prompt processing of the request stream with prefix caching (only the
+    uncached tokens are written and prefilled, over contexts whose cached
+    prefixes are shared blocks) against the same requests without caching
+    (every token written and prefilled).  ``value`` is prompt tokens per
+    second with caching."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_401_amd import ops
+    from paged_kv_cache_401_amd import workloads as wl
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    runs = {}
+    for caching in (True, False):
+        w = wl.make_prefix_workload(small=False, device=dev, caching=caching)
+        pool = ops.KVPool(w.num_blocks, w.Hkv, w.D, w.pool_dtype, device=dev, fill=0)
+        _, k, v, slots = w.ops[0]
+        slots_t = torch.as_tensor(slots, dtype=torch.int32, device=dev)
+        qs = torch.as_tensor(w.query_start, dtype=torch.int32, device=dev)
+        bt = torch.as_tensor(w.block_tables, dtype=torch.int32, device=dev)
+        ctx = torch.as_tensor(w.context_lens, dtype=torch.int32, device=dev)
+        mql = int(np.diff(w.query_start).max())
+        out = torch.empty((w.prefill_q.shape[0], w.Hq, w.D), dtype=torch.float32, device=dev)
+
+        def step():
+            ops.reshape_and_cache(pool, k, v, slots_t)
+            ops.prefill(pool, w.prefill_q, qs, mql, bt, ctx, w.scale, out=out)
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+        for e in evs:  # materialise the HIP events before handing them to the library
+            e.record(stream)
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        b0.record(stream)
+        for i in range(args.steps):
+            ops.reshape_and_cache(pool, k, v, slots_t)
+            ops.set_profile_events(evs[2 * i], evs[2 * i + 1])
+            ops.prefill(pool, w.prefill_q, qs, mql, bt, ctx, w.scale, out=out)
+        b1.record(stream)
+        torch.cuda.synchronize()
+        kern = float(np.mean([evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(args.steps)]))
+        runs[caching] = (w, b0.elapsed_time(b1) / args.steps, kern)
+    w, ms, kern = runs[True]
+    w0, ms0, _ = runs[False]
+    prompt_tokens = int(w.context_lens.sum())
+    flops = w.prefill_flops()
+    rec = {
+        "metric": "prefix-cached prompt processing: prompt tokens/s at 1 MI355X",
+        "value": round(prompt_tokens / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded token ids and N(0,1) K/V; K/V of a system prompt depends "
+                "only on (prompt, position))",
+        "config": {"workload": WORKLOAD_TEXT["prefix"], "requests": w.S,
+                   "prompt_tokens": prompt_tokens,
+                   "cached_tokens": int(w.info["cached_tokens"].sum()),
+                   "physical_blocks": w.info["physical_blocks"],
+                   "logical_blocks": w.info["logical_blocks"], "parallelism": "single GPU"},
+        "no_cache_ms_per_step": round(ms0, 5),
+        "speedup_vs_no_cache": round(ms0 / ms, 3),
+        "blocks_saved_frac": round(1 - w.info["physical_blocks"] / w0.info["physical_blocks"], 4),
+        "roofline": {"bound": "mfma", "achieved": round(flops / (kern * 1e-3) / 1e12, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(flops / (kern * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "kernel": "prefill_mfma_kernel",
+                     "algorithmic_flops_per_launch": flops},
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def run_swap(args):
+    """Swap-out then swap-in of the same 4096 blocks per step; ``value`` is the
+    bytes moved over the host link per second (both directions); a plain
+    pinned-host DMA copy of the same byte count is timed as the reference."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from paged_kv_cache_401_amd import ops
+    from paged_kv_cache_401_amd import workloads as wl
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    w = wl.make_workload("gqa70b", small=False, num_seqs=64, device=dev)
+    pool = ops.KVPool(w.num_blocks, w.Hkv, w.D, w.pool_dtype, device=dev, fill=0)
+    _, k, v, slots = w.ops[0]
+    ops.reshape_and_cache(pool, k, v, torch.as_tensor(slots, dtype=torch.int32, device=dev))
+    mgr = w.info["manager"]
+    blocks = [b for s in range(16) for b in mgr.block_table(s)]
+    host = ops.HostPool(pool, len(blocks))
+    pairs = torch.as_tensor(np.stack([blocks, np.arange(len(blocks))], 1), dtype=torch.int32,
+                            device=dev)
+    moved = 2 * len(blocks) * host.slot_bytes           # K and V, one direction
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        ops.swap_blocks(pool, host, pairs, ops.SWAP_OUT)
+        ops.swap_blocks(pool, host, pairs, ops.SWAP_IN)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[3 * i].record(stream)
+        ops.swap_blocks(pool, host, pairs, ops.SWAP_OUT)
+        ev[3 * i + 1].record(stream)
+        ops.swap_blocks(pool, host, pairs, ops.SWAP_IN)
+        ev[3 * i + 2].record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    out_ms = float(np.mean([ev[3 * i].elapsed_time(ev[3 * i + 1]) for i in range(args.steps)]))
+    in_ms = float(np.mean([ev[3 * i + 1].elapsed_time(ev[3 * i + 2]) for i in range(args.steps)]))
+    # reference: DMA copies of the same byte count between HBM and pinned host memory
+    dbuf = torch.empty(moved // 2, dtype=torch.uint8, device=dev)
+    hbuf = torch.empty(moved // 2, dtype=torch.uint8, pin_memory=True)
+    hbuf.copy_(dbuf, non_blocking=True)
+    torch.cuda.synchronize()
+    a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    a.record(stream)
+    for _ in range(args.steps):
+        hbuf.copy_(dbuf, non_blocking=True)
+        hbuf.copy_(dbuf, non_blocking=True)
+    b.record(stream)
+    for _ in range(args.steps):
+        dbuf.copy_(hbuf, non_blocking=True)
+        dbuf.copy_(hbuf, non_blocking=True)
+    c.record(stream)
+    torch.cuda.synchronize()
+    dma_d2h = moved / (a.elapsed_time(b) / args.steps) / 1e6
+    dma_h2d = moved / (b.elapsed_time(c) / args.steps) / 1e6
+    step_ms = out_ms + in_ms
+    # CPU baseline: the oracle's swap (memcpy of the same blocks) on host pools
+    kp = np.zeros(pool.nbytes, np.uint8)
+    vp = np.zeros(pool.nbytes, np.uint8)
+    hk = np.zeros(host.k.numel(), np.uint8)
+    hv = np.zeros(host.v.numel(), np.uint8)
+    pr = pairs.cpu().numpy()
+    c0 = time.perf_counter()
+    reps = 5
+    for _ in range(reps):
+        oracle.swap_blocks(kp, vp, hk, hv, w.pool_dtype, w.Hkv, w.D, w.num_blocks, len(blocks),
+                           pr, 0)
+        oracle.swap_blocks(kp, vp, hk, hv, w.pool_dtype, w.Hkv, w.D, w.num_blocks, len(blocks),
+                           pr, 1)
+    cpu_s = (time.perf_counter() - c0) / reps
+    rec = {
+        "metric": "pa_swap_blocks host-link GB/s (swap-out + swap-in) at 1 MI355X",
+        "value": round(2 * moved / step_ms / 1e6, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": DTYPE_NAME[w.pool_dtype],
+        "data": "synthetic (seeded N(0,1) K/V, scattered 16-token blocks)",
+        "config": {"workload": WORKLOAD_TEXT["swap"], "blocks": len(blocks),
+                   "block_bytes_per_pool": host.slot_bytes, "bytes_each_direction": moved,
+                   "parallelism": "single GPU"},
+        "swap_out_ms": round(out_ms, 4), "swap_out_GBps": round(moved / out_ms / 1e6, 2),
+        "swap_in_ms": round(in_ms, 4), "swap_in_GBps": round(moved / in_ms / 1e6, 2),
+        "dma_copy_d2h_GBps": round(dma_d2h, 2), "dma_copy_h2d_GBps": round(dma_h2d, 2),
+        "wall_ms_per_step": round(1e3 * wall, 4),
+        "roofline": {"bound": "host-link", "achieved": round(2 * moved / step_ms / 1e6, 2),
+                     "peak": round((dma_d2h + dma_h2d) / 2, 2), "unit": "GB/s",
+                     "frac": round((2 * moved / step_ms / 1e6) / ((dma_d2h + dma_h2d) / 2), 4),
+                     "traffic": None, "kernel": "swap_blocks_kernel",
+                     "peak_note": "measured pinned-host DMA copy rate of the same bytes"},
+        "cpu_baseline": {"value": round(2 * moved / cpu_s / 1e9, 3), "unit": "GB/s", "cores": 1,
+                         "kind": "oracle",
+                         "sample": "the same 4096-block swap-out + swap-in as host memcpy"},
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def prefill_cpu_baseline(w, args, gpu_out):
+    """Time the fp64 oracle on a bounded sample of chunk rows (all heads of
+    every n-th chunk token of every sequence) and compare them with the GPU."""
+    import numpy as np
+
+    import oracle
+    from paged_kv_cache_401_amd.workloads import raw_numpy
+
+    threads = len(os.sched_getaffinity(0))
+    _, k, v, slots = w.ops[0]
+    kp = oracle.new_pool(w.num_blocks, w.Hkv, w.D, w.pool_dtype)
+    vp = oracle.new_pool(w.num_blocks, w.Hkv, w.D, w.pool_dtype)
+    oracle.reshape_and_cache(kp, vp, w.pool_dtype, w.num_blocks, w.Hkv, w.D, raw_numpy(k),
+                             raw_numpy(v), w.kv_in_dtype, slots, w.k_scale, w.v_scale)
+    # ~9 ns per (row, token seen, head dim) on one core; aim at ~15 s of CPU work
+    per_row_s = float(np.mean(w.context_lens)) * w.D * 9e-9
+    want_rows = max(w.Hq, int(15.0 * threads / max(per_row_s, 1e-9)))
+    total = int(w.query_start[-1])
+    stride = max(1, total * w.Hq // want_rows)
+    toks = np.arange(0, total, stride)
+    rows = np.array([(t, h) for t in toks for h in range(w.Hq)], np.int32)
+    t0 = time.perf_counter()
+    ref = oracle.prefill_attention(kp, vp, w.pool_dtype, w.Hkv, w.D, raw_numpy(w.prefill_q),
+                                   w.q_dtype, w.S, w.Hq, w.query_start, w.block_tables,
+                                   w.context_lens, w.scale, w.k_scale, w.v_scale, rows=rows,
+                                   threads=threads)
+    dt = time.perf_counter() - t0
+    got = gpu_out.cpu().numpy()[rows[:, 0], rows[:, 1]].astype(np.float64)
+    err = float(np.max(np.abs(got - ref)))
+    # algorithmic flops of the sampled rows
+    seq = np.searchsorted(w.query_start, rows[:, 0], side="right") - 1
+    pos = w.context_lens[seq] - np.diff(w.query_start)[seq] + (rows[:, 0] - w.query_start[seq])
+    flops = float(np.sum(pos + 1)) * 4 * w.D
+    return ({"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+             "kind": "oracle",
+             "sample": "%d chunk rows (every %d-th chunk token, all %d heads), fp64 C oracle"
+                       % (rows.shape[0], stride, w.Hq),
+             "seconds": round(dt, 3)}, err)
 
 
 def cpu_baseline(w, args, gpu_out, pool):
@@ -247,13 +620,14 @@ def cpu_baseline(w, args, gpu_out, pool):
     from paged_kv_cache_401_amd.workloads import raw_numpy
 
     threads = len(os.sched_getaffinity(0))
-    # the oracle takes ~9 ns per (query head, token, head dim) on one core
+    # the oracle takes ~9 ns per (query head, token, head dim) on one core;
+    # aim at ~15 s of CPU work over `threads` cores, at most the whole batch
     per_seq_cpu_s = w.Hq * float(np.mean(w.context_lens)) * w.D * 9e-9
-    n = args.cpu_seqs or max(1, min(w.S, int(20.0 / max(per_seq_cpu_s, 1e-6))))
+    n = args.cpu_seqs or max(1, min(w.S, int(15.0 * threads / max(per_seq_cpu_s, 1e-6))))
     seqs = list(range(n))
     kp = oracle.new_pool(w.num_blocks, w.Hkv, w.D, w.pool_dtype)
     vp = oracle.new_pool(w.num_blocks, w.Hkv, w.D, w.pool_dtype)
-    if w.name.startswith("sampling"):
+    if w.name.startswith("sampling") or w.name == "beam":
         for op in w.ops:
             if op[0] == "write":
                 oracle.reshape_and_cache(kp, vp, w.pool_dtype, w.num_blocks, w.Hkv, w.D,

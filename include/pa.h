@@ -1,8 +1,8 @@
 /*
  * pa.h -- C ABI of the MI355X (gfx950) paged KV cache library (libpa.so).
  *
- * Four operations on a pool of fixed-size KV blocks, as the source pages
- * state the problem:
+ * Operations on a pool of fixed-size KV blocks, as the source pages state
+ * the problem:
  *   - pa_reshape_and_cache: write new tokens' K/V into their slots
  *     ("PagedAttention" glossary page (Ultralytics), how paging works, and the
  *     French page's second article, "what is the KV cache": only the new
@@ -22,6 +22,9 @@
  *     each attending causally to itself and every earlier token (glossary
  *     page, related techniques: FlashAttention-style kernels that read paged
  *     blocks).
+ *   - pa_swap_blocks: move whole blocks between the device pool and pinned
+ *     host memory (French page: fine-grained eviction of small pages to the
+ *     CPU instead of whole sequences).
  *
  * Conventions for every entry point
  *   - Pointers are device pointers unless stated; the caller owns every
@@ -179,6 +182,35 @@ int pa_reshape_and_cache(const pa_pool_t *pool, const void *k, const void *v, in
  *                  and none may also be a source.  num_pairs = 0 is a no-op.
  */
 int pa_copy_blocks(const pa_pool_t *pool, const int32_t *src_dst_pairs, int32_t num_pairs,
+                   void *stream);
+
+/* Directions of pa_swap_blocks. */
+#define PA_SWAP_OUT 0 /* device pool -> host pool */
+#define PA_SWAP_IN 1  /* host pool -> device pool */
+
+/*
+ * pa_swap_blocks -- move whole blocks between the device pool and a host
+ * pool: the fine-grained eviction of the French page ("how PagedAttention
+ * solves this problem": when memory is full, small pages move to the CPU
+ * instead of whole sequences).
+ *   host_k, host_v  the host pool: num_host_slots slots, each holding one
+ *                   whole block's K (resp. V) bytes for every KV head in the
+ *                   device pool's tile order (num_kv_heads * 16 * head_dim
+ *                   elements of kv_dtype).  Must be pinned host memory
+ *                   (hipHostMalloc, or a pinned torch tensor) that the
+ *                   device can map; PA_ERR_HIP otherwise.  16-byte aligned.
+ *                   Owned by the caller.
+ *   block_slot_pairs  int32 [num_pairs][2] in device memory: (device block,
+ *                   host slot).  PA_SWAP_OUT copies each block's bytes into
+ *                   its slot; PA_SWAP_IN copies each slot's bytes into its
+ *                   block.  Blocks must be distinct, slots must be distinct.
+ *                   Pairs with an id out of range are skipped.
+ * The copy is asynchronous on `stream`: host memory may be read only after
+ * the stream reaches this point (swap-out), and a swapped-in block may be
+ * attended by work enqueued after it.  num_pairs = 0 is a no-op.
+ */
+int pa_swap_blocks(const pa_pool_t *pool, void *host_k, void *host_v, int32_t num_host_slots,
+                   const int32_t *block_slot_pairs, int32_t num_pairs, int32_t direction,
                    void *stream);
 
 /* Which partition kernel pa_decode launches for this pool and head count:

@@ -57,6 +57,8 @@ def bind(L: ctypes.CDLL) -> ctypes.CDLL:
     L.orc_reshape_and_cache.restype = None
     L.orc_copy_blocks.argtypes = [P, P, I, I, I, P, I64]
     L.orc_copy_blocks.restype = None
+    L.orc_swap_blocks.argtypes = [P, P, P, P, I, I, I, I64, I64, P, I64, I]
+    L.orc_swap_blocks.restype = None
     L.orc_gather.argtypes = [P, I, I, I, I, P, I64, I, P]
     L.orc_gather.restype = None
     L.orc_paged_attention.argtypes = [P, P, I, F, F, I, I, P, I, I, I, P, I, P, F,
@@ -138,6 +140,16 @@ def copy_blocks(k_pool, v_pool, pool_dt, Hkv, D, pairs):
     pairs = np.ascontiguousarray(np.asarray(pairs, dtype=np.int32).reshape(-1, 2))
     lib().orc_copy_blocks(_ptr(k_pool), _ptr(v_pool), pool_dt, Hkv, D, _ptr(pairs),
                           pairs.shape[0])
+
+
+def swap_blocks(k_pool, v_pool, host_k, host_v, pool_dt, Hkv, D, num_blocks, num_slots, pairs,
+                direction):
+    """Copy whole blocks between the pools and host slots: direction 0 =
+    device block -> host slot, 1 = host slot -> device block; pairs are
+    (device block, host slot)."""
+    pairs = np.ascontiguousarray(np.asarray(pairs, dtype=np.int32).reshape(-1, 2))
+    lib().orc_swap_blocks(_ptr(k_pool), _ptr(v_pool), _ptr(host_k), _ptr(host_v), pool_dt, Hkv,
+                          D, num_blocks, num_slots, _ptr(pairs), pairs.shape[0], int(direction))
 
 
 def gather(pool, is_v, pool_dt, Hkv, D, table, n, g) -> np.ndarray:

@@ -257,6 +257,32 @@ void orc_copy_blocks(uint8_t *k_pool, uint8_t *v_pool, int pool_dt, int Hkv, int
     }
 }
 
+/* --------------------------------------------------- swap to / from host */
+
+/* For each pair (device block, host slot), in order: direction 0 copies
+ * every KV head's K and V tile of the block into the slot of the host pools
+ * (a slot holds one whole block), direction 1 copies the slot back into the
+ * block (the French page: when memory is full, small pages move to the CPU).
+ * Pairs with an id outside [0, num_blocks) or [0, num_slots) are skipped. */
+void orc_swap_blocks(uint8_t *k_pool, uint8_t *v_pool, uint8_t *host_k, uint8_t *host_v,
+                     int pool_dt, int Hkv, int D, int64_t num_blocks, int64_t num_slots,
+                     const int32_t *pairs, int64_t num_pairs, int direction)
+{
+    size_t bytes = (size_t)Hkv * 16 * (size_t)D * (size_t)orc_elem_bytes(pool_dt);
+    for (int64_t p = 0; p < num_pairs; p++) {
+        int64_t b = pairs[2 * p], h = pairs[2 * p + 1];
+        if (b < 0 || b >= num_blocks || h < 0 || h >= num_slots)
+            continue;
+        if (direction == 0) {
+            memcpy(host_k + h * bytes, k_pool + b * bytes, bytes);
+            memcpy(host_v + h * bytes, v_pool + b * bytes, bytes);
+        } else {
+            memcpy(k_pool + b * bytes, host_k + h * bytes, bytes);
+            memcpy(v_pool + b * bytes, host_v + h * bytes, bytes);
+        }
+    }
+}
+
 /* ------------------------------------------------------ gather (read back) */
 
 /* Copy the raw elements of tokens 0..n-1 of KV head g, read through `table`

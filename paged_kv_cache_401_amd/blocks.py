@@ -37,10 +37,12 @@ class NoFreeBlock(RuntimeError):
 class _Seq:
     table: list = field(default_factory=list)
     length: int = 0
+    on_host: bool = False   # table lists host slots while swapped out
 
 
 class BlockManager:
-    def __init__(self, num_blocks: int, free_list=None, block_size: int = BLOCK_SIZE):
+    def __init__(self, num_blocks: int, free_list=None, block_size: int = BLOCK_SIZE,
+                 num_host_slots: int = 0):
         if block_size != BLOCK_SIZE:
             raise ValueError("block size is fixed at 16 tokens")
         self.num_blocks = int(num_blocks)
@@ -51,6 +53,10 @@ class BlockManager:
             raise ValueError("free list must hold distinct block ids inside the pool")
         self.refcount = [0] * self.num_blocks
         self.seqs: dict = {}
+        # host slots for swapped-out blocks, with their reference counts
+        self.num_host_slots = int(num_host_slots)
+        self.host_free = list(range(self.num_host_slots))
+        self.host_refcount = [0] * self.num_host_slots
         # event counters (allocations, copies, frees) for accounting reports
         self.n_alloc = 0
         self.n_cow = 0
@@ -77,6 +83,8 @@ class BlockManager:
         (src, dst) block copies that must run before those tokens are written.
         """
         seq = self.seqs[seq_id]
+        if seq.on_host:
+            raise RuntimeError("sequence %r is swapped out" % (seq_id,))
         slots, pairs = [], []
         for _ in range(int(n)):
             pos = seq.length
@@ -98,6 +106,8 @@ class BlockManager:
     def fork(self, parent, child) -> None:
         """``child`` starts as a copy of ``parent``'s table, sharing every block."""
         p = self.seqs[parent]
+        if p.on_host:
+            raise RuntimeError("sequence %r is swapped out" % (parent,))
         self.add_sequence(child)
         c = self.seqs[child]
         c.table = list(p.table)
@@ -107,11 +117,75 @@ class BlockManager:
 
     def free_sequence(self, seq_id) -> None:
         seq = self.seqs.pop(seq_id)
+        if seq.on_host:
+            for h in seq.table:
+                self.host_refcount[h] -= 1
+                if self.host_refcount[h] == 0:
+                    self.host_free.append(h)
+            return
         for b in seq.table:
             self.refcount[b] -= 1
             if self.refcount[b] == 0:
                 self.free.append(b)
                 self.n_freed += 1
+
+    # ------------------------------------------------------------- swapping
+    def swap_out(self, seq_ids):
+        """Move every block of the sequences ``seq_ids`` to host slots, block by
+        block (the French page: small pages move to the CPU instead of whole
+        sequences).  The group must hold every reference to its blocks, so
+        shared blocks move once and stay shared.  Returns the
+        (device block, host slot) pairs to copy before the freed blocks are
+        reused."""
+        group = [self.seqs[s] for s in seq_ids]
+        if any(sq.on_host for sq in group):
+            raise RuntimeError("a sequence of the group is already swapped out")
+        refs, order = {}, []
+        for sq in group:
+            for b in sq.table:
+                if b not in refs:
+                    order.append(b)
+                refs[b] = refs.get(b, 0) + 1
+        if any(self.refcount[b] != refs[b] for b in order):
+            raise RuntimeError("a block of the group is shared with a sequence outside it")
+        if len(order) > len(self.host_free):
+            raise NoFreeBlock("no free host slot for %d blocks" % len(order))
+        slot_of = {b: self.host_free.pop(0) for b in order}
+        for b in order:
+            h = slot_of[b]
+            self.host_refcount[h] = self.refcount[b]
+            self.refcount[b] = 0
+            self.free.append(b)
+        for sq in group:
+            sq.table = [slot_of[b] for b in sq.table]
+            sq.on_host = True
+        return [(b, slot_of[b]) for b in order]
+
+    def swap_in(self, seq_ids):
+        """Bring the swapped-out sequences ``seq_ids`` back into free device
+        blocks (any free location, as for new blocks).  Returns the
+        (device block, host slot) pairs to copy before they are attended."""
+        group = [self.seqs[s] for s in seq_ids]
+        if not all(sq.on_host for sq in group):
+            raise RuntimeError("a sequence of the group is not swapped out")
+        order = []
+        for sq in group:
+            for h in sq.table:
+                if h not in order:
+                    order.append(h)
+        if len(order) > len(self.free):
+            raise NoFreeBlock("no free device block for %d slots" % len(order))
+        block_of = {}
+        for h in order:
+            b = self.free.pop(0)
+            block_of[h] = b
+            self.refcount[b] = self.host_refcount[h]
+            self.host_refcount[h] = 0
+            self.host_free.append(h)
+        for sq in group:
+            sq.table = [block_of[h] for h in sq.table]
+            sq.on_host = False
+        return [(block_of[h], h) for h in order]
 
     # -------------------------------------------------------------- queries
     def block_table(self, seq_id) -> list:
@@ -122,6 +196,9 @@ class BlockManager:
 
     def physical_blocks_in_use(self) -> int:
         return sum(1 for r in self.refcount if r > 0)
+
+    def host_slots_in_use(self) -> int:
+        return sum(1 for r in self.host_refcount if r > 0)
 
     def logical_blocks(self) -> int:
         return sum(len(s.table) for s in self.seqs.values())

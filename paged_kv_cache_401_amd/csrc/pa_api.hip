@@ -311,6 +311,36 @@ int pa_copy_blocks(const pa_pool_t *pool, const int32_t *src_dst_pairs, int32_t 
     return ok();
 }
 
+int pa_swap_blocks(const pa_pool_t *pool, void *host_k, void *host_v, int32_t num_host_slots,
+                   const int32_t *block_slot_pairs, int32_t num_pairs, int32_t direction,
+                   void *stream) {
+    int rc = check_pool(pool);
+    if (rc != PA_OK) return rc;
+    if (direction != PA_SWAP_OUT && direction != PA_SWAP_IN)
+        return fail(PA_ERR_SHAPE, "direction %d must be PA_SWAP_OUT or PA_SWAP_IN", direction);
+    if (num_pairs < 0 || num_host_slots < 0)
+        return fail(PA_ERR_SHAPE, "num_pairs %d and num_host_slots %d must be >= 0", num_pairs,
+                    num_host_slots);
+    if (num_pairs == 0) return ok();
+    if (!host_k || !host_v || !block_slot_pairs)
+        return fail(PA_ERR_NULL, "host_k, host_v and block_slot_pairs must be non-NULL");
+    if (!aligned16(host_k) || !aligned16(host_v))
+        return fail(PA_ERR_ALIGN, "host_k and host_v must be 16-byte aligned");
+    // the device-side addresses of the pinned host pools (fails for pageable memory)
+    void *dk = nullptr, *dv = nullptr;
+    hipError_t e = hipHostGetDevicePointer(&dk, host_k, 0);
+    if (e == hipSuccess) e = hipHostGetDevicePointer(&dv, host_v, 0);
+    if (e != hipSuccess)
+        return fail(PA_ERR_HIP, "host pools must be pinned, device-mapped host memory: %s",
+                    hipGetErrorString(e));
+    e = pa::launch_swap_blocks(pool->k_pool, pool->v_pool, dk, dv, block_slot_pairs, num_pairs,
+                               pool->num_blocks, num_host_slots,
+                               pool->num_kv_heads * tile_bytes(pool), direction == PA_SWAP_OUT,
+                               static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "swap_blocks kernel: %s", hipGetErrorString(e));
+    return ok();
+}
+
 int pa_decode_variant(const pa_pool_t *pool, int32_t num_q_heads) {
     int rc = check_pool(pool);
     if (rc == PA_OK) rc = check_heads(pool, 0, num_q_heads, 1);

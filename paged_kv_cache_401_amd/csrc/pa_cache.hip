@@ -1,4 +1,5 @@
-// pa_cache.hip -- the two kernels that keep the paged pool consistent.
+// pa_cache.hip -- the kernels that keep the paged pool consistent, and the
+// block swap between the device pool and host memory.
 //
 // reshape_and_cache: each new token's K/V goes to slot `slot % 16` of block
 // `slot / 16` (the slot rule of the worked example on the "PagedAttention"
@@ -6,6 +7,9 @@
 // the French page's second article, "what is the KV cache", describes).
 // copy_blocks: the copy-on-write step of the same glossary page's section on
 // sharing blocks between sequences.
+// swap_blocks: fine-grained eviction -- when memory runs short, small blocks
+// move to CPU memory instead of whole sequences (French page, "how
+// PagedAttention solves this problem").
 #include "pa_internal.h"
 
 namespace pa {
@@ -86,7 +90,13 @@ __global__ __launch_bounds__(kThreads) void reshape_and_cache_kernel(CacheParams
     }
 }
 
-// One workgroup per (pair, pool): 16-byte copies of the whole block (all KV heads).
+// Workgroup (pair, pool, part): 16-byte copies of one part of the whole block
+// (all KV heads), U x 4 KiB per part; each thread issues its U loads before
+// its stores.  Source and destination never overlap (destinations are
+// distinct and none is a source).  Measured on MI355X: whole 32 KiB blocks
+// per workgroup (U = 8) are fastest for a few hundred pairs, 16 KiB parts
+// (U = 4) once thousands of pairs fill the chip.
+template <int U>
 __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(char *k_pool, char *v_pool,
                                                                const int32_t *pairs,
                                                                int32_t num_blocks,
@@ -95,10 +105,68 @@ __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(char *k_pool, cha
     const int32_t dst = pairs[2 * blockIdx.x + 1];
     if (src < 0 || dst < 0 || src >= num_blocks || dst >= num_blocks) return;
     char *base = blockIdx.y ? v_pool : k_pool;
-    const uint4 *s = reinterpret_cast<const uint4 *>(base + (int64_t)src * block_bytes);
-    uint4 *d = reinterpret_cast<uint4 *>(base + (int64_t)dst * block_bytes);
+    const uint4 *__restrict__ s = reinterpret_cast<const uint4 *>(base + (int64_t)src * block_bytes);
+    uint4 *__restrict__ d = reinterpret_cast<uint4 *>(base + (int64_t)dst * block_bytes);
     const int64_t n = block_bytes / 16;
-    for (int64_t i = threadIdx.x; i < n; i += kThreads) d[i] = s[i];
+    const int64_t i0 = (int64_t)blockIdx.z * kThreads * U;
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t i = i0 + (int64_t)u * kThreads + threadIdx.x;
+        if (i < n) v[u] = s[i];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t i = i0 + (int64_t)u * kThreads + threadIdx.x;
+        if (i < n) d[i] = v[u];
+    }
+}
+
+template <int U>
+hipError_t launch_copy(void *k_pool, void *v_pool, const int32_t *pairs, int32_t num_pairs,
+                       int32_t num_blocks, int64_t block_bytes, hipStream_t stream) {
+    const int64_t part = (int64_t)kThreads * U * 16;
+    const int64_t parts = (block_bytes + part - 1) / part;
+    if (parts > 65535) return hipErrorInvalidValue;
+    copy_blocks_kernel<U><<<dim3((unsigned)num_pairs, 2, (unsigned)parts), dim3(kThreads), 0, stream>>>(
+        static_cast<char *>(k_pool), static_cast<char *>(v_pool), pairs, num_blocks, block_bytes);
+    return hipGetLastError();
+}
+
+// Workgroup (pair, pool, part) of a block swap: one 8 KiB part of a whole
+// block (all KV heads) between the device pool and the host pool.  Swap-out
+// reads the device block and writes host slot bytes over the host link;
+// swap-in reads host slot bytes and writes the device block.  Each thread
+// issues all its loads before its stores: host reads are long round trips.
+constexpr int kSwapUnroll = 4;
+constexpr int64_t kSwapPartBytes = (int64_t)kThreads * kSwapUnroll * 16;  // 16 KiB
+
+__global__ __launch_bounds__(kThreads) void swap_blocks_kernel(char *k_pool, char *v_pool,
+                                                               char *host_k, char *host_v,
+                                                               const int32_t *pairs,
+                                                               int32_t num_blocks,
+                                                               int32_t num_host_slots,
+                                                               int64_t block_bytes, int to_host) {
+    const int32_t b = pairs[2 * blockIdx.x];
+    const int32_t h = pairs[2 * blockIdx.x + 1];
+    if (b < 0 || h < 0 || b >= num_blocks || h >= num_host_slots) return;
+    char *dev = (blockIdx.y ? v_pool : k_pool) + (int64_t)b * block_bytes;
+    char *hst = (blockIdx.y ? host_v : host_k) + (int64_t)h * block_bytes;
+    const uint4 *__restrict__ s = reinterpret_cast<const uint4 *>(to_host ? dev : hst);
+    uint4 *__restrict__ d = reinterpret_cast<uint4 *>(to_host ? hst : dev);
+    const int64_t n = block_bytes / 16;
+    const int64_t i0 = (int64_t)blockIdx.z * (kSwapPartBytes / 16);
+    uint4 v[kSwapUnroll];
+#pragma unroll
+    for (int u = 0; u < kSwapUnroll; ++u) {
+        const int64_t i = i0 + (int64_t)u * kThreads + threadIdx.x;
+        if (i < n) v[u] = s[i];
+    }
+#pragma unroll
+    for (int u = 0; u < kSwapUnroll; ++u) {
+        const int64_t i = i0 + (int64_t)u * kThreads + threadIdx.x;
+        if (i < n) d[i] = v[u];
+    }
 }
 
 template <int POOL, int IN, int D>
@@ -127,8 +195,20 @@ hipError_t launch_reshape_and_cache(int pool_kv, int in_kv, int head_dim, const 
 
 hipError_t launch_copy_blocks(void *k_pool, void *v_pool, const int32_t *pairs, int32_t num_pairs,
                               int32_t num_blocks, int64_t block_bytes, hipStream_t stream) {
-    copy_blocks_kernel<<<dim3((unsigned)num_pairs, 2), dim3(kThreads), 0, stream>>>(
-        static_cast<char *>(k_pool), static_cast<char *>(v_pool), pairs, num_blocks, block_bytes);
+    if (num_pairs < 1024)
+        return launch_copy<8>(k_pool, v_pool, pairs, num_pairs, num_blocks, block_bytes, stream);
+    return launch_copy<4>(k_pool, v_pool, pairs, num_pairs, num_blocks, block_bytes, stream);
+}
+
+hipError_t launch_swap_blocks(void *k_pool, void *v_pool, void *host_k, void *host_v,
+                              const int32_t *pairs, int32_t num_pairs, int32_t num_blocks,
+                              int32_t num_host_slots, int64_t block_bytes, bool to_host,
+                              hipStream_t stream) {
+    const int64_t parts = (block_bytes + kSwapPartBytes - 1) / kSwapPartBytes;
+    if (parts > 65535) return hipErrorInvalidValue;
+    swap_blocks_kernel<<<dim3((unsigned)num_pairs, 2, (unsigned)parts), dim3(kThreads), 0, stream>>>(
+        static_cast<char *>(k_pool), static_cast<char *>(v_pool), static_cast<char *>(host_k),
+        static_cast<char *>(host_v), pairs, num_blocks, num_host_slots, block_bytes, to_host ? 1 : 0);
     return hipGetLastError();
 }
 

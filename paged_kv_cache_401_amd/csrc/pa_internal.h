@@ -81,4 +81,9 @@ hipError_t launch_reshape_and_cache(int pool_kv, int in_kv, int head_dim, const 
 hipError_t launch_copy_blocks(void *k_pool, void *v_pool, const int32_t *pairs, int32_t num_pairs,
                               int32_t num_blocks, int64_t block_bytes, hipStream_t stream);
 
+hipError_t launch_swap_blocks(void *k_pool, void *v_pool, void *host_k, void *host_v,
+                              const int32_t *pairs, int32_t num_pairs, int32_t num_blocks,
+                              int32_t num_host_slots, int64_t block_bytes, bool to_host,
+                              hipStream_t stream);
+
 }  // namespace pa

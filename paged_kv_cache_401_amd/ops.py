@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 
 # every symbol include/pa.h declares
 EXPORTS = ("pa_pool_bytes", "pa_decode_partition_tokens", "pa_decode_workspace_size", "pa_decode",
-           "pa_prefill", "pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_variant", "pa_set_profile_events",
+           "pa_prefill", "pa_reshape_and_cache", "pa_swap_blocks", "pa_copy_blocks", "pa_decode_variant", "pa_set_profile_events",
            "pa_probe_read", "pa_strerror", "pa_last_error", "pa_build_info")
 
 
@@ -66,6 +66,8 @@ def lib() -> ctypes.CDLL:
     L.pa_prefill.restype = ctypes.c_int
     L.pa_reshape_and_cache.argtypes = [PD, P, P, I32, P, I32, P]
     L.pa_reshape_and_cache.restype = ctypes.c_int
+    L.pa_swap_blocks.argtypes = [PD, P, P, I32, P, I32, I32, P]
+    L.pa_swap_blocks.restype = ctypes.c_int
     L.pa_copy_blocks.argtypes = [PD, P, I32, P]
     L.pa_copy_blocks.restype = ctypes.c_int
     L.pa_decode_variant.argtypes = [PD, I32]
@@ -149,6 +151,34 @@ def copy_blocks(pool: KVPool, pairs: torch.Tensor, stream=None) -> None:
     ptr = _dev(pairs, "pairs", torch.int32) if n else None
     d = pool.desc()
     _check(lib().pa_copy_blocks(ctypes.byref(d), ptr, n, _stream(stream)))
+
+
+SWAP_OUT, SWAP_IN = 0, 1
+
+
+class HostPool:
+    """Pinned host memory for swapped-out blocks: num_slots slots, each one
+    whole block of the device pool (every KV head) for K and for V."""
+
+    def __init__(self, pool: KVPool, num_slots: int):
+        self.num_slots = int(num_slots)
+        self.slot_bytes = pool.nbytes // pool.num_blocks
+        n = max(1, self.num_slots) * self.slot_bytes
+        self.k = torch.empty(n, dtype=torch.uint8, pin_memory=True)
+        self.v = torch.empty(n, dtype=torch.uint8, pin_memory=True)
+
+
+def swap_blocks(pool: KVPool, host: HostPool, pairs: torch.Tensor, direction: int,
+                stream=None) -> None:
+    """Move whole blocks: pairs is int32 [P][2] (device block, host slot) on the
+    GPU; direction SWAP_OUT (device -> host) or SWAP_IN (host -> device)."""
+    n = pairs.numel() // 2
+    ptr = _dev(pairs, "pairs", torch.int32) if n else None
+    if not host.k.is_pinned() or not host.v.is_pinned():
+        raise ValueError("host pools must be pinned")
+    d = pool.desc()
+    _check(lib().pa_swap_blocks(ctypes.byref(d), host.k.data_ptr(), host.v.data_ptr(),
+                                host.num_slots, ptr, n, int(direction), _stream(stream)))
 
 
 def decode_partition_tokens(pool: KVPool, num_seqs, num_q_heads, max_blocks_per_seq,

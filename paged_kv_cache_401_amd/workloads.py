@@ -44,8 +44,11 @@ F32, BF16, FP8 = 0, 1, 2
 TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16}
 CONFIG_IDS = ("tiny", "mha13b", "gqa70b", "sampling_a", "sampling_b", "fp8")
 PREFILL_IDS = ("prefill_gqa70b", "prefill_mha13b", "chunked_gqa70b", "chunked_fp8")
+BEAM_IDS = ("beam",)
+PREFIX_IDS = ("prefix",)
 SEEDS = {"tiny": 0, "mha13b": 1, "gqa70b": 2, "sampling_a": 3, "sampling_b": 3, "fp8": 4,
-         "prefill_gqa70b": 5, "prefill_mha13b": 6, "chunked_gqa70b": 7, "chunked_fp8": 8}
+         "prefill_gqa70b": 5, "prefill_mha13b": 6, "chunked_gqa70b": 7, "chunked_fp8": 8,
+         "beam": 9, "prefix": 10}
 
 
 @dataclass
@@ -212,6 +215,12 @@ def make_workload(name: str, small: bool = False, device="cpu", seed: int | None
                        seed, device, rng, partition_tokens=512, fp8_scales=True)
     if name in ("sampling_a", "sampling_b"):
         return _sampling(name, small, device, seed, rng, num_seqs)
+    if name == "beam":
+        return make_beam_workload(small, device, seed)
+    if name == "prefix":
+        return make_prefix_workload(small, device, seed)
+    if name in PREFILL_IDS:
+        return make_prefill_workload(name, small, device, seed)
     raise KeyError(name)
 
 
@@ -262,6 +271,183 @@ def make_prefill_workload(name: str, small: bool = False, device="cpu",
     gen.manual_seed(seed + 1000)
     w.query_start = qs
     w.prefill_q = _randn(gen, (int(qs[-1]), Hq, 128), torch.bfloat16, device)
+    return w
+
+
+def make_beam_workload(small: bool = False, device="cpu", seed: int | None = None,
+                       steps: int | None = None) -> Workload:
+    """Beam search over shared prompts (glossary page, sharing blocks: beam
+    search reuses one copy of the shared prefix; a sequence about to write
+    into a block others still use copies it first).
+
+    R requests x W beams with the 70B-like heads (64 q / 8 KV, head dim 128,
+    bf16).  Each prompt (1000 tokens, so its last block is partial) is written
+    once and shared by its W beams.  Every step then re-selects W parents per
+    request with replacement (seeded): beams chosen by no one are freed, a
+    beam chosen c times keeps its table for one child and is forked for the
+    other c - 1, and every new beam appends one token; writers into a shared
+    partial last block copy it first (copy-on-write), in beam order.  The last
+    step's copies and writes are the benchmarked step; ``beam_tokens`` holds
+    each beam's logical token history (indices into the concatenated writes).
+    Full size: 64 requests x 8 beams, 40 steps; small: 2 x 4, 6 steps.
+    """
+    if seed is None:
+        seed = SEEDS["beam"]
+    rng = np.random.default_rng(seed)
+    R, W = (2, 4) if small else (64, 8)
+    T = steps if steps is not None else (6 if small else 40)
+    prompt = 37 if small else 1000
+    Hq, Hkv, D = 64, 8, 128
+    nb = R * (blocks_for(prompt) + W * (T + 2))
+    mgr = BlockManager(nb, free_list=rng.permutation(nb))
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    ops, hist, ntok = [], {}, 0
+    slots = []
+    for r in range(R):
+        mgr.add_sequence(("prompt", r))
+        sl, _ = mgr.append_tokens(("prompt", r), prompt)
+        slots.extend(sl)
+        hist[("prompt", r)] = list(range(ntok, ntok + prompt))
+        ntok += prompt
+    k = _randn(gen, (R * prompt, Hkv, D), torch.bfloat16, device)
+    v = _randn(gen, (R * prompt, Hkv, D), torch.bfloat16, device)
+    ops.append(("write", k, v, np.asarray(slots, dtype=np.int32)))
+    beams = []
+    for r in range(R):
+        for b in range(W):
+            mgr.fork(("prompt", r), (r, b, 0))
+            hist[(r, b, 0)] = list(hist[("prompt", r)])
+        mgr.free_sequence(("prompt", r))
+        beams.append([(r, b, 0) for b in range(W)])
+    step_pairs = np.zeros((0, 2), np.int32)
+    for t in range(1, T + 1):
+        new_beams = []
+        for r in range(R):
+            parents = np.sort(rng.integers(0, W, size=W))
+            counts = np.bincount(parents, minlength=W)
+            for b in range(W):                      # drop beams nobody continues
+                if counts[b] == 0:
+                    mgr.free_sequence(beams[r][b])
+                    del hist[beams[r][b]]
+            kids = []
+            for b in range(W):
+                for c in range(int(counts[b])):
+                    child = (r, len(kids), t)
+                    if c == 0:                      # the first child takes the parent's table
+                        mgr.seqs[child] = mgr.seqs.pop(beams[r][b])
+                        hist[child] = hist.pop(beams[r][b])
+                    else:
+                        mgr.fork(kids[-c], child)
+                        hist[child] = list(hist[kids[-c]])
+                    kids.append(child)
+            new_beams.append(kids)
+        beams = new_beams
+        slots, pairs = [], []
+        for r in range(R):
+            for sid in beams[r]:
+                sl, pr = mgr.append_tokens(sid, 1)
+                slots.extend(sl)
+                pairs.extend(pr)
+                hist[sid].append(ntok)
+                ntok += 1
+        n = len(slots)
+        kn = _randn(gen, (n, Hkv, D), torch.bfloat16, device)
+        vn = _randn(gen, (n, Hkv, D), torch.bfloat16, device)
+        step_pairs = np.asarray(pairs, dtype=np.int32).reshape(-1, 2)
+        if len(pairs):
+            ops.append(("copy", step_pairs))
+        ops.append(("write", kn, vn, np.asarray(slots, dtype=np.int32)))
+    seqs = [sid for r in range(R) for sid in beams[r]]
+    ctx = np.asarray([mgr.length(sq) for sq in seqs], dtype=np.int32)
+    tables = _tables_from(mgr, seqs)
+    q = _randn(gen, (len(seqs), Hq, D), torch.bfloat16, device)
+    last = ops[-1]
+    w = Workload(name="beam", S=len(seqs), Hq=Hq, Hkv=Hkv, D=D, pool_dtype=BF16, q_dtype=BF16,
+                 kv_in_dtype=BF16, num_blocks=nb, context_lens=ctx, block_tables=tables, q=q,
+                 scale=_f32(1.0 / math.sqrt(D)), ops=ops, step_k=last[1], step_v=last[2],
+                 step_slots=last[3])
+    w.info.update(manager=mgr, requests=R, beams=W, steps=T, prompt_len=prompt,
+                  step_pairs=step_pairs, beam_tokens=[hist[sq] for sq in seqs],
+                  cow_copies=mgr.n_cow, physical_blocks=mgr.physical_blocks_in_use(),
+                  logical_blocks=mgr.logical_blocks())
+    return w
+
+
+def make_prefix_workload(small: bool = False, device="cpu", seed: int | None = None,
+                         caching: bool = True, num_blocks: int | None = None) -> Workload:
+    """Requests that start with shared system prompts, served with prefix
+    caching by full-block hashing (glossary page, sharing blocks: hashing
+    complete blocks extends sharing across requests).
+
+    P system prompts (lengths uniform in [64, 2048]) and R requests, each a
+    seeded choice of system prompt plus a private user part of 16..512
+    tokens; 70B-like heads (64 q / 8 KV, head dim 128, bf16).  A system
+    prompt's K/V depends only on (prompt, position) and user tokens are
+    private, so equal prefixes hold equal K/V, as in a model.  Requests
+    arrive in order; each reuses the cached full blocks of its prefix and
+    writes only the rest (``caching=False`` writes every token into private
+    blocks: the reference).  ``query_start`` counts each request's uncached
+    tokens, the chunk a chunked prefill computes.  Full size: 8 prompts, 128
+    requests; small: 3 prompts, 8 requests.
+    """
+    from .prefix_cache import PrefixCache
+    if seed is None:
+        seed = SEEDS["prefix"]
+    rng = np.random.default_rng(seed)
+    P, R = (3, 8) if small else (8, 128)
+    Hq, Hkv, D = 64, 8, 128
+    sys_len = rng.integers(64, (300 if small else 2049), size=P)
+    sys_ids = [rng.integers(0, 32000, size=int(n)) for n in sys_len]
+    choice = rng.integers(0, P, size=R)
+    user_len = rng.integers(16, (60 if small else 513), size=R)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    sys_k = [_randn(gen, (int(n), Hkv, D), torch.bfloat16, device) for n in sys_len]
+    sys_v = [_randn(gen, (int(n), Hkv, D), torch.bfloat16, device) for n in sys_len]
+    user_k = _randn(gen, (int(user_len.sum()), Hkv, D), torch.bfloat16, device)
+    user_v = _randn(gen, (int(user_len.sum()), Hkv, D), torch.bfloat16, device)
+    user_off = np.concatenate([[0], np.cumsum(user_len)])
+    lens = sys_len[choice] + user_len
+    nb = num_blocks or int(sum(blocks_for(n) for n in lens))
+    mgr = BlockManager(nb, free_list=rng.permutation(nb))
+    cache = PrefixCache(mgr) if caching else None
+    ks, vs, slots, cached, history = [], [], [], [], []
+    for r in range(R):
+        s_ = int(choice[r])
+        ids = np.concatenate([sys_ids[s_], rng.integers(32000, 64000, size=int(user_len[r]))])
+        if cache is not None:
+            c, sl = cache.add_request(r, ids)
+        else:
+            mgr.add_sequence(r)
+            c = 0
+            sl, _ = mgr.append_tokens(r, len(ids))
+        cached.append(c)
+        # K/V of tokens c.. of this request, in order
+        a, b = user_off[r], user_off[r + 1]
+        k_full = torch.cat([sys_k[s_], user_k[a:b]])
+        v_full = torch.cat([sys_v[s_], user_v[a:b]])
+        ks.append(k_full[c:])
+        vs.append(v_full[c:])
+        slots.extend(sl)
+        history.append((s_, int(a), int(b)))
+    cached = np.asarray(cached, dtype=np.int64)
+    ctx = lens.astype(np.int32)
+    tables = _tables_from(mgr, range(R))
+    qs = np.zeros(R + 1, dtype=np.int32)
+    qs[1:] = np.cumsum(ctx - cached)
+    q = _randn(gen, (R, Hq, D), torch.bfloat16, device)
+    w = Workload(name="prefix", S=R, Hq=Hq, Hkv=Hkv, D=D, pool_dtype=BF16, q_dtype=BF16,
+                 kv_in_dtype=BF16, num_blocks=nb, context_lens=ctx, block_tables=tables, q=q,
+                 scale=_f32(1.0 / math.sqrt(D)),
+                 ops=[("write", torch.cat(ks), torch.cat(vs), np.asarray(slots, dtype=np.int32))])
+    w.query_start = qs
+    w.prefill_q = _randn(gen, (int(qs[-1]), Hq, D), torch.bfloat16, device)
+    w.info.update(manager=mgr, cache=cache, cached_tokens=cached, system_len=sys_len,
+                  system_choice=choice, user_len=user_len, history=history,
+                  physical_blocks=mgr.physical_blocks_in_use(),
+                  logical_blocks=mgr.logical_blocks(),
+                  system_kv=(sys_k, sys_v), user_kv=(user_k, user_v))
     return w
 
 

@@ -144,3 +144,13 @@ def test_prefill_argument_rules():
     assert call(scale=float("inf")) == -8
     assert call(mql=0, q=None, qs=None, bt=None, ctx=None, out=None) == 0   # nothing to do
     assert call(S=0, q=None, qs=None, bt=None, ctx=None, out=None) == 0
+
+
+def test_swap_argument_rules():
+    L = ops.lib()
+    d = desc()
+    assert L.pa_swap_blocks(ctypes.byref(d), 16, 16, 4, 16, 2, 5, None) == -3   # bad direction
+    assert L.pa_swap_blocks(ctypes.byref(d), 16, 16, -1, 16, 2, 0, None) == -3  # negative slots
+    assert L.pa_swap_blocks(ctypes.byref(d), None, 16, 4, 16, 2, 0, None) == -1
+    assert L.pa_swap_blocks(ctypes.byref(d), 17, 16, 4, 16, 2, 1, None) == -6   # misaligned
+    assert L.pa_swap_blocks(ctypes.byref(d), None, None, 0, None, 0, 0, None) == 0

@@ -22,7 +22,7 @@ from paged_kv_cache_401_amd.workloads import raw_numpy
 
 pytestmark = pytest.mark.gpu
 
-SMALL = ["tiny", "mha13b", "gqa70b", "sampling_a", "sampling_b", "fp8"]
+SMALL = ["tiny", "mha13b", "gqa70b", "sampling_a", "sampling_b", "fp8", "beam"]
 
 
 def _pool_bytes(pool):
@@ -292,3 +292,42 @@ def test_full_size_sampled_rows(name):
     err = float(np.max(np.abs(got - ref)))
     print("%s full size: %d rows, max abs err %.3e" % (name, len(rows), err))
     assert err <= tolerance(w)
+
+
+def test_beam_search_full_size_pool_and_decode():
+    """64 requests x 8 beams, 40 beam-search steps of forks, frees and
+    copy-on-write copies (~176 pairs per step): every pool byte equals the
+    oracle's after the whole run, and decode of sampled beams agrees."""
+    w = wl.make_workload("beam", small=False)
+    pool = gpu_pool(w, fill=0xFF)
+    out = gpu_decode(w, pool)
+    kp, vp = oracle_pools(w, fill=0xFF)
+    gk, gv = _pool_bytes(pool)
+    assert np.array_equal(gk, kp) and np.array_equal(gv, vp)
+    seqs = [0, 7, 100, 255, 511]
+    rows = _sampled_rows(w, seqs)
+    ref = oracle_decode(w, kp, vp, rows=rows)
+    got = np.stack([out[s, h] for s, h in rows])
+    assert float(np.max(np.abs(got - ref))) <= tolerance(w)
+
+
+@pytest.mark.parametrize("num_pairs", [1, 3, 700, 1500])
+@pytest.mark.parametrize("dtype,heads,dim", [(ops.BF16, 8, 128), (ops.FP8, 1, 64), (ops.F32, 2, 64)])
+def test_copy_blocks_many_pairs_bit_exact(num_pairs, dtype, heads, dim):
+    """Random pools, random disjoint (src, dst) pairs: destinations equal their
+    sources and every other byte is unchanged (block sizes 2 KiB .. 32 KiB)."""
+    rng = np.random.default_rng(num_pairs + dim)
+    nb = 2 * num_pairs + 5
+    pool = ops.KVPool(nb, heads, dim, dtype, device="cuda", k_scale=0.5, v_scale=0.5)
+    nbytes = pool.k.numel()
+    k0 = torch.as_tensor(rng.integers(0, 256, nbytes, dtype=np.uint8))
+    v0 = torch.as_tensor(rng.integers(0, 256, nbytes, dtype=np.uint8))
+    pool.k.copy_(k0)
+    pool.v.copy_(v0)
+    perm = rng.permutation(nb)
+    pairs = np.stack([perm[:num_pairs], perm[num_pairs:2 * num_pairs]], 1).astype(np.int32)
+    ops.copy_blocks(pool, torch.as_tensor(pairs, device="cuda"))
+    kp, vp = k0.numpy().copy(), v0.numpy().copy()
+    oracle.copy_blocks(kp, vp, dtype, heads, dim, pairs)
+    gk, gv = _pool_bytes(pool)
+    assert np.array_equal(gk, kp) and np.array_equal(gv, vp)

@@ -1,0 +1,89 @@
+"""Prefix caching by full-block hashing, on the host: hit accounting, the
+life of cached blocks on the free list, and the oracle's view (caching moves
+bytes, not results).
+
+Glossary page, sharing blocks between sequences: hashing complete blocks
+extends sharing across requests (how vLLM caches prompts).
+"""
+import numpy as np
+
+import oracle
+from oracle_helpers import oracle_decode, oracle_pools
+from paged_kv_cache_401_amd import workloads as wl
+from paged_kv_cache_401_amd.blocks import BlockManager
+from paged_kv_cache_401_amd.prefix_cache import PrefixCache
+from paged_kv_cache_401_amd.workloads import raw_numpy
+
+
+def test_hits_are_exactly_the_full_blocks_of_repeated_system_prompts():
+    w = wl.make_prefix_workload(small=True)
+    seen, want = set(), 0
+    for r in range(w.S):
+        s = int(w.info["system_choice"][r])
+        if s in seen:
+            want += int(w.info["system_len"][s]) // 16
+        seen.add(s)
+    assert w.info["cache"].hit_blocks == want
+    assert int(w.info["cached_tokens"].sum()) == 16 * want
+    assert w.info["physical_blocks"] == w.info["logical_blocks"] - want
+
+
+def test_caching_changes_where_bytes_live_not_outputs():
+    """Decode over cached prefixes equals decode over private copies, bit for
+    bit, and every request reads back its own tokens."""
+    a = wl.make_prefix_workload(small=True, caching=True)
+    b = wl.make_prefix_workload(small=True, caching=False)
+    assert (a.context_lens == b.context_lens).all()
+    kpa, vpa = oracle_pools(a)
+    kpb, vpb = oracle_pools(b)
+    out_a = oracle_decode(a, kpa, vpa)
+    out_b = oracle_decode(b, kpb, vpb)
+    assert out_a.tobytes() == out_b.tobytes()
+    for s in range(a.S):
+        for g in (0, a.Hkv - 1):
+            ga = oracle.gather(kpa, False, a.pool_dtype, a.Hkv, a.D, a.block_tables[s],
+                               int(a.context_lens[s]), g)
+            gb = oracle.gather(kpb, False, b.pool_dtype, b.Hkv, b.D, b.block_tables[s],
+                               int(b.context_lens[s]), g)
+            assert ga.tobytes() == gb.tobytes()
+
+
+def test_prefill_of_uncached_rest_equals_whole_prompt_prefill():
+    """Chunked prefill of each prompt's uncached rest over its cached prefix
+    gives the same rows as prefilling the whole prompt, bit for bit."""
+    a = wl.make_prefix_workload(small=True, caching=True)
+    b = wl.make_prefix_workload(small=True, caching=False)
+    kpa, vpa = oracle_pools(a)
+    kpb, vpb = oracle_pools(b)
+    cached = a.info["cached_tokens"]
+    # the same query rows for the overlapping positions
+    qb = b.prefill_q.clone()
+    qa = np.concatenate([np.arange(b.query_start[s] + cached[s], b.query_start[s + 1])
+                         for s in range(a.S)])
+    qa_t = qb[qa]
+    ra = oracle.prefill_attention(kpa, vpa, a.pool_dtype, a.Hkv, a.D, raw_numpy(qa_t),
+                                  a.q_dtype, a.S, a.Hq, a.query_start, a.block_tables,
+                                  a.context_lens, a.scale)
+    rb = oracle.prefill_attention(kpb, vpb, b.pool_dtype, b.Hkv, b.D, raw_numpy(qb), b.q_dtype,
+                                  b.S, b.Hq, b.query_start, b.block_tables, b.context_lens,
+                                  b.scale)
+    assert ra.tobytes() == rb[qa].tobytes()
+
+
+def test_cached_blocks_wait_on_the_free_list_until_reused():
+    mgr = BlockManager(4, free_list=[0, 1, 2, 3])
+    cache = PrefixCache(mgr)
+    x = np.arange(40)                       # two full blocks + 8 tokens
+    c, _ = cache.add_request("a", x)
+    assert c == 0 and cache.new_blocks == 2
+    mgr.free_sequence("a")                  # blocks free, hashes kept
+    c, slots = cache.add_request("b", x)
+    assert c == 32 and len(slots) == 8 and cache.hit_blocks == 2
+    assert mgr.block_table("b")[:2] == [0, 1]
+    mgr.free_sequence("b")
+    # a different 64-token prompt needs all four blocks: the cached ones are reused
+    c, _ = cache.add_request("c", np.arange(1000, 1064))
+    assert c == 0 and cache.evicted == 2
+    mgr.free_sequence("c")
+    c, _ = cache.add_request("d", x)        # the prefix must be computed again
+    assert c == 0
