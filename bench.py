@@ -177,12 +177,15 @@ def main():
     torch.cuda.synchronize()
     setup_s = time.time() - t0
 
+    # blocks shared across sequences (prompts, beams): cached rather than streaming loads
+    shared = bool(w.info.get("shared_kv", False))
+
     def step():
         ops.copy_blocks(pool, step_pairs)
         if step_slots is not None:
             ops.reshape_and_cache(pool, step_k, step_v, step_slots)
         ops.decode(pool, q, tables, ctx, w.scale, out=out, partition_tokens=ptok,
-                   workspace=ws)
+                   workspace=ws, shared_kv=shared)
 
     for _ in range(args.warmup):
         step()
@@ -204,7 +207,8 @@ def main():
         if step_slots is not None:
             ops.reshape_and_cache(pool, step_k, step_v, step_slots)
         ops.set_profile_events(evs[2 * i], evs[2 * i + 1])
-        ops.decode(pool, q, tables, ctx, w.scale, out=out, partition_tokens=ptok, workspace=ws)
+        ops.decode(pool, q, tables, ctx, w.scale, out=out, partition_tokens=ptok, workspace=ws,
+                   shared_kv=shared)
     step_end.record(stream)
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - wall0
@@ -263,6 +267,7 @@ def main():
                    "num_q_heads": w.Hq, "num_kv_heads": w.Hkv, "head_dim": w.D,
                    "total_context_tokens": int(w.context_lens.sum()),
                    "partition_tokens": ptok_used, "kv_bytes": kv_bytes,
+                   "kv_loads": "cached (shared blocks)" if shared else "non-temporal",
                    "parallelism": "single GPU"},
         "pct_hbm_peak_step": round(100.0 * value / HBM_PEAK_GBPS, 2),
         "decode_seqs_per_s": round(w.S / (ms_per_step * 1e-3), 1),

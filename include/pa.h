@@ -132,6 +132,20 @@ int pa_decode(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t num
               const int32_t *context_lens, float scale, float *out, int32_t partition_tokens,
               void *workspace, size_t workspace_bytes, void *stream);
 
+/* Flags of pa_decode_ex: how the kernels load K/V. */
+#define PA_DECODE_STREAM_KV 0u /* every block is read once per call: non-temporal loads (default) */
+#define PA_DECODE_SHARED_KV 1u /* blocks are shared by several sequences of the batch (shared
+                                  prompts, parallel sampling, beams): ordinary cached loads, so
+                                  sequences read later find them in cache */
+
+/* pa_decode with flags (PA_DECODE_* above); pa_decode is pa_decode_ex with
+ * PA_DECODE_STREAM_KV.  The flags change only the cache policy of the K/V
+ * loads, never the result.  Unknown flags give PA_ERR_SHAPE. */
+int pa_decode_ex(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t num_seqs,
+                 int32_t num_q_heads, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                 const int32_t *context_lens, float scale, float *out, int32_t partition_tokens,
+                 void *workspace, size_t workspace_bytes, uint32_t flags, void *stream);
+
 /*
  * pa_prefill -- causal (chunked) prefill attention over the paged pool.
  * Each sequence's chunk of new tokens is the last

@@ -140,6 +140,17 @@ int pa_decode(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t num
               int32_t num_q_heads, const int32_t *block_tables, int32_t max_blocks_per_seq,
               const int32_t *context_lens, float scale, float *out, int32_t partition_tokens,
               void *workspace, size_t workspace_bytes, void *stream) {
+    return pa_decode_ex(pool, q, q_dtype, num_seqs, num_q_heads, block_tables, max_blocks_per_seq,
+                        context_lens, scale, out, partition_tokens, workspace, workspace_bytes,
+                        PA_DECODE_STREAM_KV, stream);
+}
+
+int pa_decode_ex(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t num_seqs,
+                 int32_t num_q_heads, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                 const int32_t *context_lens, float scale, float *out, int32_t partition_tokens,
+                 void *workspace, size_t workspace_bytes, uint32_t flags, void *stream) {
+    if (flags & ~(uint32_t)PA_DECODE_SHARED_KV)
+        return fail(PA_ERR_SHAPE, "unknown decode flags 0x%x", flags);
     int rc = check_pool(pool);
     if (rc != PA_OK) return rc;
     rc = check_heads(pool, num_seqs, num_q_heads, max_blocks_per_seq);
@@ -181,6 +192,7 @@ int pa_decode(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t num
     const double kscale = pool->kv_dtype == PA_FP8_E4M3 ? (double)pool->k_scale : 1.0;
     p.qk_scale_log2 = (float)((double)scale * kscale * 1.4426950408889634);
     p.out_scale = pool->kv_dtype == PA_FP8_E4M3 ? pool->v_scale : 1.0f;
+    p.shared_kv = (flags & PA_DECODE_SHARED_KV) ? 1 : 0;
     if (need > 0) {
         const int64_t rows = (int64_t)num_seqs * num_q_heads * np;
         char *ws = static_cast<char *>(workspace);

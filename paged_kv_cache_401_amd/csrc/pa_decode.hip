@@ -27,6 +27,7 @@
 // Masked tokens (position >= ctx) get score -inf, i.e. weight exactly 0, by
 // selection: the values they read are never multiplied in.
 #include "pa_internal.h"
+#include "pa_mfma_util.h"
 
 namespace pa {
 namespace {
@@ -73,7 +74,7 @@ __device__ __forceinline__ float wave_max16(float x) {
     return x;
 }
 
-template <int KV, int D>
+template <int KV, int D, bool STREAM>
 __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
     constexpr int EB = KV == kF32 ? 4 : (KV == kBF16 ? 2 : 1);
     constexpr int X = 16 / EB;          // K: elements per 16-byte run
@@ -148,10 +149,10 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
         const char *vt = vbase + tile;
 #pragma unroll
         for (int jk = 0; jk < NKL; ++jk)
-            kc[jk] = *reinterpret_cast<const uint4 *>(kt + ((c + 4 * jk) * kBlock + t) * 16);
+            kc[jk] = __builtin_bit_cast(uint4, load_kv<STREAM>(kt + ((c + 4 * jk) * kBlock + t) * 16));
 #pragma unroll
         for (int jj = 0; jj < NVL; ++jj)
-            vc[jj] = *reinterpret_cast<const uint4 *>(vt + (c * (D / W) + 16 * jj + t) * 16);
+            vc[jj] = __builtin_bit_cast(uint4, load_kv<STREAM>(vt + (c * (D / W) + 16 * jj + t) * 16));
     };
 
     auto compute_block = [&](const uint4 (&kc)[NKL], const uint4 (&vc)[NVL], int j) {
@@ -404,7 +405,10 @@ template <int KV, int D>
 hipError_t launch_valu(const DecodeParams &p, hipStream_t stream) {
     const int64_t grid = (int64_t)p.num_seqs * p.num_q_heads * p.max_partitions;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-    decode_valu_kernel<KV, D><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(p);
+    if (p.shared_kv)
+        decode_valu_kernel<KV, D, false><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(p);
+    else
+        decode_valu_kernel<KV, D, true><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(p);
     return hipGetLastError();
 }
 

@@ -41,7 +41,7 @@ namespace {
 
 constexpr float kNegInf = kNegInfF;
 
-template <int KV, int D>
+template <int KV, int D, bool STREAM>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void decode_mfma_kernel(DecodeParams p) {
     constexpr int EB = KV == kBF16 ? 2 : 1;
     constexpr int TILE_BYTES = kBlock * D * EB;
@@ -108,9 +108,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         const char *kt = kbase + tile + koff;
         const char *vt = vbase + tile + voff;
 #pragma unroll
-        for (int i = 0; i < NKL; ++i) kr[i] = *reinterpret_cast<const u32x4 *>(kt + i * 4 * kBlock * 16);
+        for (int i = 0; i < NKL; ++i) kr[i] = load_kv<STREAM>(kt + i * 4 * kBlock * 16);
 #pragma unroll
-        for (int i = 0; i < NVL; ++i) vr[i] = *reinterpret_cast<const u32x4 *>(vt + i * 16 * 16);
+        for (int i = 0; i < NVL; ++i) vr[i] = load_kv<STREAM>(vt + i * 16 * 16);
     };
 
     auto compute_block = [&](const u32x4 (&kr)[NKL], const u32x4 (&vr)[NVL], int j) {
@@ -276,7 +276,10 @@ template <int KV, int D>
 hipError_t launch(const DecodeParams &p, hipStream_t stream) {
     const int64_t grid = (int64_t)p.num_seqs * p.num_kv_heads * p.max_partitions;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-    decode_mfma_kernel<KV, D><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(p);
+    if (p.shared_kv)
+        decode_mfma_kernel<KV, D, false><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(p);
+    else
+        decode_mfma_kernel<KV, D, true><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(p);
     return hipGetLastError();
 }
 

@@ -14,38 +14,68 @@
 // Rows and work split.  The query heads of one KV head g (G = Hq / Hkv of
 // them) and BQ = 128 / G consecutive chunk tokens form 128 rows
 // (row r = token r / G, head g G + r % G); one workgroup (4 wavefronts) takes
-// one such tile of one sequence.  Each wavefront owns 32 rows as two
-// 16-column matrix-core groups and walks blocks 0 .. (its last row's
-// position) / 16 on its own: no LDS and no barrier.  Its four wavefronts read
-// the same K/V tiles, which the second and later readers find in cache.
-// Workgroups are issued latest tile first, so the longest causal ranges
-// start first.
+// one such tile of one sequence, and each wavefront owns 32 of its rows as
+// two 16-column matrix-core groups.  Workgroups are issued latest tile
+// first, so the longest causal ranges start first.
+//
+// Staging.  The workgroup walks blocks 0 .. (its last row's position) / 16.
+// Every block's K and V tiles are loaded once per workgroup into one of two
+// LDS stages (the next block is already in flight in registers while the
+// current one is computed, and is written to the other stage afterwards; one
+// barrier per block).  Each wavefront reads its matrix-core A operands from
+// LDS at the same offsets the pool's tiled layout gives in memory, and skips
+// the blocks past its own rows' last position.
 //
 // Per block, for each 16-row group (operand layouts as in the grouped decode
-// kernel: K and V go from the pool's tiled layout straight into A operands
-// with one 16-byte load per lane per run/cell):
+// kernel):
 //     S^T[16 tokens][16 rows]  = K[16][D] . Q^T[D][16]
 //     O^T[D][16 rows]         += V^T[D][16 tokens] . P^T[16][16]
 // with P carried as bf16 hi + lo (16 significant bits).  Causal masking sets
 // the score of every token past a row's position to -inf (selection); the V
-// elements of slots past the context are zeroed before the product.
+// elements of slots past the context are zeroed before the product.  The
+// running maximum is raised lazily: only when a block's maximum exceeds it by
+// more than 8 (in log2 units) are the numerators rescaled, so probabilities
+// stay below 2^8 and most blocks skip the rescale.
 #include "pa_internal.h"
 #include "pa_mfma_util.h"
 
 namespace pa {
 namespace {
 
-template <int KV, int D, int kGroups>
+constexpr int kGroups = 2;                                    // 16-row groups per wavefront
+constexpr int kRowsPerWave = 16 * kGroups;                    // 32
+constexpr int kRowsPerTile = kRowsPerWave * (kThreads / 64);  // 128
+constexpr float kLazyMax = 8.0f;  // rescale when a block's max exceeds the running max by 2^8
+
+// [hi(p0..p3) | lo(p0..p3)] as bf16 pairs, packed with byte permutes: hi keeps
+// each p's top 16 bits, lo the top 16 bits of the remainder
+__device__ __forceinline__ bf16x8 p_hi_lo_perm(const float (&pr)[4]) {
+    uint32_t u[4], r[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        u[i] = __float_as_uint(pr[i]);
+        r[i] = __float_as_uint(pr[i] - __uint_as_float(u[i] & 0xffff0000u));
+    }
+    const u32x4 w = {__builtin_amdgcn_perm(u[1], u[0], 0x07060302u),
+                     __builtin_amdgcn_perm(u[3], u[2], 0x07060302u),
+                     __builtin_amdgcn_perm(r[1], r[0], 0x07060302u),
+                     __builtin_amdgcn_perm(r[3], r[2], 0x07060302u)};
+    return as_bf16x8(w);
+}
+
+template <int KV, int D>
 __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p) {
-    constexpr int kRowsPerWave = 16 * kGroups;
-    constexpr int kRowsPerTile = kRowsPerWave * (kThreads / 64);
     constexpr int EB = KV == kBF16 ? 2 : 1;
     constexpr int TILE_BYTES = kBlock * D * EB;
+    constexpr int STAGE_UNITS = 2 * TILE_BYTES / 16;               // 16-byte units: K tile, V tile
+    constexpr int LOADS = (STAGE_UNITS + kThreads - 1) / kThreads;  // per thread per block
     constexpr int NQK = D / 32;                       // 32-deep q.K steps per block
-    constexpr int NKL = KV == kBF16 ? NQK : NQK / 2;  // 16-byte K loads per lane per block
+    constexpr int NKL = KV == kBF16 ? NQK : NQK / 2;  // 16-byte K reads per lane per block
     constexpr int W = 4 / EB;                         // V: head dims per 16-byte cell
-    constexpr int NVL = D / W / 16;                   // 16-byte V loads per lane per block
+    constexpr int NVL = D / W / 16;                   // 16-byte V reads per lane per block
     constexpr int NT = D / 16;                        // 16 x 16 output tiles per group
+
+    __shared__ __attribute__((aligned(16))) u32x4 stage[2][STAGE_UNITS];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -66,6 +96,9 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
     n_new = n_new < 0 ? 0 : (n_new > p.max_query_len ? p.max_query_len : n_new);
     const int first = ctx - n_new;  // position of chunk token 0 (< 0: chunk longer than context)
     if (tile * BQ >= n_new) return;
+    // the workgroup's blocks: up to its last row's position
+    const int pos_last = first + min(tile * BQ + BQ, n_new) - 1;
+    const int nblk_wg = pos_last < 0 ? 0 : pos_last / kBlock + 1;
 
     // this lane's two rows (one per group): chunk token, head, position
     int row_tok[kGroups], row_head[kGroups], pos_mask[kGroups];
@@ -89,7 +122,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
         maxpos = max(maxpos, __shfl_xor(maxpos, o));
         minpos = min(minpos, __shfl_xor(minpos, o));
     }
-    const int nblk = maxpos < 0 ? 0 : maxpos / kBlock + 1;
+    const int nblk_wave = maxpos < 0 ? 0 : maxpos / kBlock + 1;
 
     // Q^T operands (zero for rows outside the chunk), head dims per the K mapping
     bf16x8 qop[kGroups][NQK];
@@ -121,37 +154,49 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
     }
 
     const int32_t *table = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
-    const char *kbase = static_cast<const char *>(p.k_pool);
-    const char *vbase = static_cast<const char *>(p.v_pool);
-    const int koff = (c * kBlock + n) * 16;   // K run c, token n
-    const int voff = (c * (D / W) + n) * 16;  // V cell (tokens 4c.., dims W n..)
+    const u32x4 *kpool = static_cast<const u32x4 *>(p.k_pool);
+    const u32x4 *vpool = static_cast<const u32x4 *>(p.v_pool);
+    auto ok = [&](int32_t b) { return b >= 0 && b < p.num_blocks; };
 
-    auto load_block = [&](int32_t b, u32x4 (&kr)[NKL], u32x4 (&vr)[NVL]) {
-        const int64_t t0 = ((int64_t)b * p.num_kv_heads + g) * TILE_BYTES;
-        const char *kt = kbase + t0 + koff;
-        const char *vt = vbase + t0 + voff;
+    // staging: thread t moves 16-byte units t, t + 256, ... of a block's K
+    // tile (units 0 .. TILE/16 - 1) and V tile (the rest), byte for byte
+    auto gload = [&](int32_t b, u32x4 (&r)[LOADS]) {
+        const int64_t t0 = ((int64_t)b * p.num_kv_heads + g) * (TILE_BYTES / 16);
 #pragma unroll
-        for (int i = 0; i < NKL; ++i) kr[i] = *reinterpret_cast<const u32x4 *>(kt + i * 4 * kBlock * 16);
+        for (int i = 0; i < LOADS; ++i) {
+            const int u = threadIdx.x + i * kThreads;
+            if (u < STAGE_UNITS)
+                r[i] = u < TILE_BYTES / 16 ? kpool[t0 + u] : vpool[t0 + u - TILE_BYTES / 16];
+        }
+    };
+    auto swrite = [&](int st, const u32x4 (&r)[LOADS]) {
 #pragma unroll
-        for (int i = 0; i < NVL; ++i) vr[i] = *reinterpret_cast<const u32x4 *>(vt + i * 16 * 16);
+        for (int i = 0; i < LOADS; ++i) {
+            const int u = threadIdx.x + i * kThreads;
+            if (u < STAGE_UNITS) stage[st][u] = r[i];
+        }
     };
 
-    auto compute_block = [&](const u32x4 (&kr)[NKL], const u32x4 (&vr)[NVL], int j) {
+    auto compute_block = [&](int st, int j) {
+        const u32x4 *ks = stage[st] + c * kBlock + n;                      // K run c, token n
+        const u32x4 *vs = stage[st] + TILE_BYTES / 16 + c * (D / W) + n;  // V cell (tokens 4c.., dims W n..)
         // K operands (fp8 widened to bf16 once, used by both groups)
         bf16x8 kop[NQK];
         if constexpr (KV == kBF16) {
 #pragma unroll
-            for (int u = 0; u < NQK; ++u) kop[u] = as_bf16x8(kr[u]);
+            for (int u = 0; u < NQK; ++u) kop[u] = as_bf16x8(ks[u * 4 * kBlock]);
         } else {
 #pragma unroll
-            for (int i = 0; i < NKL; ++i)
+            for (int i = 0; i < NKL; ++i) {
+                const u32x4 kr = ks[i * 4 * kBlock];
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     uint32_t a0, a1, a2, a3;
-                    e4m3x4_to_bf16(kr[i][2 * h], a0, a1);
-                    e4m3x4_to_bf16(kr[i][2 * h + 1], a2, a3);
+                    e4m3x4_to_bf16(kr[2 * h], a0, a1);
+                    e4m3x4_to_bf16(kr[2 * h + 1], a2, a3);
                     kop[2 * i + h] = as_bf16x8(u32x4{a0, a1, a2, a3});
                 }
+            }
         }
         const bool need_mask = j * kBlock + kBlock - 1 > minpos;
         const int nvalid = ctx - j * kBlock;
@@ -174,35 +219,37 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
             float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
             bm = fmaxf(bm, __shfl_xor(bm, 16));
             bm = fmaxf(bm, __shfl_xor(bm, 32));
-            // block 0 holds token 0 <= every row's position, so m_new is finite
-            // from the first block on; the guard only keeps a row whose first
-            // block id is out of range free of NaN
-            const float m_new = fmaxf(m[k], bm);
+            // raise the running max only past a margin of 2^8; the first block
+            // always raises it (m = -inf).  m stays -inf only while every
+            // token so far was masked, which the guard keeps free of NaN.
+            const bool grow = bm > m[k] + kLazyMax;
+            const float m_new = grow ? bm : m[k];
             const float m_use = m_new == kNegInfF ? 0.f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m[k] - m_use);
+            const float alpha = grow ? __builtin_amdgcn_exp2f(m[k] - m_use) : 1.f;
             float pr[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(sc[i] - m_use);
             m[k] = m_new;
             l[k] = l[k] * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-            if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
+            if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
                 for (int t = 0; t < NT; ++t) acc[k][t] *= alpha;
             }
-            pop[k] = p_operand_hi_lo(pr);
+            pop[k] = p_hi_lo_perm(pr);
         }
 
         // O^T += V^T . P^T, one MFMA per 16 x 16 output tile and group
 #pragma unroll
         for (int jj = 0; jj < NVL; ++jj) {
+            const u32x4 vr = vs[jj * 16];
 #pragma unroll
             for (int w = 0; w < W; ++w) {
                 uint32_t v01, v23;
                 if constexpr (KV == kBF16) {
-                    v01 = vr[jj][2 * w];
-                    v23 = vr[jj][2 * w + 1];
+                    v01 = vr[2 * w];
+                    v23 = vr[2 * w + 1];
                 } else {
-                    e4m3x4_to_bf16(vr[jj][w], v01, v23);
+                    e4m3x4_to_bf16(vr[w], v01, v23);
                 }
                 v01 &= keep01;
                 v23 &= keep23;
@@ -215,40 +262,37 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
         }
     };
 
-    // blocks 0 .. nblk-1: ids fetched 64 at a time into one VGPR; block k+1's
-    // loads are issued before block k is computed (register buffers A and B)
-    for (int k0 = 0; k0 < nblk; k0 += 64) {
-        const int kend = min(nblk, k0 + 64);
-        int32_t ids = -1;
-        if (k0 + lane < kend) ids = table[k0 + lane];
-        auto block_id = [&](int k) { return __builtin_amdgcn_readlane(ids, k - k0); };
-        auto ok = [&](int32_t b) { return b >= 0 && b < p.num_blocks; };
-        u32x4 kA[NKL], vA[NVL], kB[NKL], vB[NVL];
-        int k = k0;
-        int32_t bA = block_id(k);
-        bool okA = ok(bA);
-        if (okA) load_block(bA, kA, vA);
-        while (true) {
-            const int k1 = k + 1;
-            bool okB = false;
-            if (k1 < kend) {
-                const int32_t bB = block_id(k1);
-                okB = ok(bB);
-                if (okB) load_block(bB, kB, vB);
-            }
-            if (okA) compute_block(kA, vA, k);
-            if (k1 >= kend) break;
-            const int k2 = k1 + 1;
-            okA = false;
-            if (k2 < kend) {
-                bA = block_id(k2);
-                okA = ok(bA);
-                if (okA) load_block(bA, kA, vA);
-            }
-            if (okB) compute_block(kB, vB, k1);
-            if (k2 >= kend) break;
-            k = k2;
+    // Block ids come 64 at a time in one VGPR (lane i: block j0 + i).  Block
+    // j is computed from stage j & 1 while block j + 1 is in flight in
+    // registers; block j + 1 then goes to the other stage and block j + 2's
+    // loads are issued, and one barrier ends the step.
+    int32_t ids = lane < nblk_wg ? table[lane] : -1;
+    int32_t id_cur = -1, id_next = -1;
+    u32x4 pre[LOADS];
+    if (nblk_wg > 0) {
+        id_cur = __builtin_amdgcn_readlane(ids, 0);
+        if (ok(id_cur)) {
+            gload(id_cur, pre);
+            swrite(0, pre);
         }
+        if (nblk_wg > 1) {
+            id_next = __builtin_amdgcn_readlane(ids, 1);
+            if (ok(id_next)) gload(id_next, pre);
+        }
+    }
+    __syncthreads();
+    for (int j = 0; j < nblk_wg; ++j) {
+        if (j < nblk_wave && ok(id_cur)) compute_block(j & 1, j);
+        if (j + 1 < nblk_wg && ok(id_next)) swrite((j + 1) & 1, pre);
+        int32_t id_after = -1;
+        if (j + 2 < nblk_wg) {
+            if (((j + 2) & 63) == 0) ids = j + 2 + lane < nblk_wg ? table[j + 2 + lane] : -1;
+            id_after = __builtin_amdgcn_readlane(ids, (j + 2) & 63);
+            if (ok(id_after)) gload(id_after, pre);
+        }
+        id_cur = id_next;
+        id_next = id_after;
+        __syncthreads();
     }
 
     // rows: out = O / l (times v_scale); rows before the context start are zero
@@ -275,28 +319,21 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
     }
 }
 
-// 16-row groups per wavefront: more rows reuse each K/V load more often but
-// hold more accumulators (two groups at head dim 128 exceed 256 registers)
-#ifndef PA_PREFILL_GROUPS_D128
-#define PA_PREFILL_GROUPS_D128 1
-#endif
-constexpr int groups_for(int head_dim) { return head_dim == 64 ? 2 : PA_PREFILL_GROUPS_D128; }
-
 template <int KV, int D>
 hipError_t launch(const PrefillParams &p, hipStream_t stream) {
     const int64_t grid = (int64_t)p.num_tiles * p.num_seqs * p.num_kv_heads;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-    prefill_mfma_kernel<KV, D, groups_for(D)><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(p);
+    prefill_mfma_kernel<KV, D><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(p);
     return hipGetLastError();
 }
 
 }  // namespace
 
-int prefill_tile_tokens(int head_dim, int group) { return 16 * groups_for(head_dim) * (kThreads / 64) / group; }
+int prefill_tile_tokens(int head_dim, int group) { return (void)head_dim, kRowsPerTile / group; }
 
 bool prefill_supported(int kv, int head_dim, int group) {
     return (kv == kBF16 || kv == kFP8) && (head_dim == 64 || head_dim == 128) && group >= 1 &&
-           group <= 16 * groups_for(head_dim) * (kThreads / 64);
+           group <= kRowsPerTile;
 }
 
 hipError_t launch_prefill(int kv, int head_dim, const PrefillParams &p, hipStream_t stream) {

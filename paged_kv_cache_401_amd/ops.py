@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 
 # every symbol include/pa.h declares
 EXPORTS = ("pa_pool_bytes", "pa_decode_partition_tokens", "pa_decode_workspace_size", "pa_decode",
+           "pa_decode_ex",
            "pa_prefill", "pa_reshape_and_cache", "pa_swap_blocks", "pa_copy_blocks", "pa_decode_variant", "pa_set_profile_events",
            "pa_probe_read", "pa_strerror", "pa_last_error", "pa_build_info")
 
@@ -62,6 +63,8 @@ def lib() -> ctypes.CDLL:
     L.pa_decode_workspace_size.restype = SZ
     L.pa_decode.argtypes = [PD, P, I32, I32, I32, P, I32, P, F, P, I32, P, SZ, P]
     L.pa_decode.restype = ctypes.c_int
+    L.pa_decode_ex.argtypes = [PD, P, I32, I32, I32, P, I32, P, F, P, I32, P, SZ, ctypes.c_uint32, P]
+    L.pa_decode_ex.restype = ctypes.c_int
     L.pa_prefill.argtypes = [PD, P, I32, I32, I32, P, I32, P, I32, P, F, P, P]
     L.pa_prefill.restype = ctypes.c_int
     L.pa_reshape_and_cache.argtypes = [PD, P, P, I32, P, I32, P]
@@ -199,9 +202,15 @@ def decode_workspace_size(pool: KVPool, num_seqs, num_q_heads, max_blocks_per_se
                                               max_blocks_per_seq, partition_tokens))
 
 
+DECODE_STREAM_KV, DECODE_SHARED_KV = 0, 1
+
+
 def decode(pool: KVPool, q: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
            scale: float, out: torch.Tensor | None = None, partition_tokens: int = 0,
-           workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+           workspace: torch.Tensor | None = None, stream=None,
+           shared_kv: bool = False) -> torch.Tensor:
+    """Paged decode attention; ``shared_kv`` marks batches whose sequences
+    share blocks (cached rather than streaming K/V loads; same result)."""
     S, Hq, D = q.shape
     if D != pool.head_dim:
         raise ValueError("q head dim %d differs from the pool's %d" % (D, pool.head_dim))
@@ -218,11 +227,12 @@ def decode(pool: KVPool, q: torch.Tensor, block_tables: torch.Tensor, context_le
     wptr = workspace.data_ptr() if workspace is not None else None
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     d = pool.desc()
-    _check(lib().pa_decode(ctypes.byref(d), _dev(q, "q"), TORCH_TO_PA[q.dtype], S, Hq,
-                           _dev(block_tables, "block_tables", torch.int32), mbs,
-                           _dev(context_lens, "context_lens", torch.int32), float(scale),
-                           _dev(out, "out", torch.float32), int(partition_tokens), wptr, wbytes,
-                           _stream(stream)))
+    _check(lib().pa_decode_ex(ctypes.byref(d), _dev(q, "q"), TORCH_TO_PA[q.dtype], S, Hq,
+                              _dev(block_tables, "block_tables", torch.int32), mbs,
+                              _dev(context_lens, "context_lens", torch.int32), float(scale),
+                              _dev(out, "out", torch.float32), int(partition_tokens), wptr,
+                              wbytes, DECODE_SHARED_KV if shared_kv else DECODE_STREAM_KV,
+                              _stream(stream)))
     return out
 
 

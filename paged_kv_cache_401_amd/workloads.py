@@ -367,7 +367,7 @@ def make_beam_workload(small: bool = False, device="cpu", seed: int | None = Non
                  kv_in_dtype=BF16, num_blocks=nb, context_lens=ctx, block_tables=tables, q=q,
                  scale=_f32(1.0 / math.sqrt(D)), ops=ops, step_k=last[1], step_v=last[2],
                  step_slots=last[3])
-    w.info.update(manager=mgr, requests=R, beams=W, steps=T, prompt_len=prompt,
+    w.info.update(shared_kv=True, manager=mgr, requests=R, beams=W, steps=T, prompt_len=prompt,
                   step_pairs=step_pairs, beam_tokens=[hist[sq] for sq in seqs],
                   cow_copies=mgr.n_cow, physical_blocks=mgr.physical_blocks_in_use(),
                   logical_blocks=mgr.logical_blocks())
@@ -443,7 +443,8 @@ def make_prefix_workload(small: bool = False, device="cpu", seed: int | None = N
                  ops=[("write", torch.cat(ks), torch.cat(vs), np.asarray(slots, dtype=np.int32))])
     w.query_start = qs
     w.prefill_q = _randn(gen, (int(qs[-1]), Hq, D), torch.bfloat16, device)
-    w.info.update(manager=mgr, cache=cache, cached_tokens=cached, system_len=sys_len,
+    w.info.update(shared_kv=caching, manager=mgr, cache=cache, cached_tokens=cached,
+                  system_len=sys_len,
                   system_choice=choice, user_len=user_len, history=history,
                   physical_blocks=mgr.physical_blocks_in_use(),
                   logical_blocks=mgr.logical_blocks(),
@@ -500,7 +501,7 @@ def _sampling(name, small, device, seed, rng, num_prompts=None) -> Workload:
     w = Workload(name=name, S=P * n, Hq=Hq, Hkv=Hkv, D=D, pool_dtype=BF16, q_dtype=BF16,
                  kv_in_dtype=BF16, num_blocks=nb, context_lens=ctx, block_tables=tables, q=q,
                  scale=_f32(1.0 / math.sqrt(D)), ops=ops)
-    w.info.update(manager=mgr, prompt_len=prompt, continuation=cont,
+    w.info.update(shared_kv=True, manager=mgr, prompt_len=prompt, continuation=cont,
                   shared_prompt_blocks=shared_blocks,
                   physical_blocks=mgr.physical_blocks_in_use(),
                   logical_blocks=mgr.logical_blocks(), cow_pairs=len(cow))

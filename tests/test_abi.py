@@ -154,3 +154,12 @@ def test_swap_argument_rules():
     assert L.pa_swap_blocks(ctypes.byref(d), None, 16, 4, 16, 2, 0, None) == -1
     assert L.pa_swap_blocks(ctypes.byref(d), 17, 16, 4, 16, 2, 1, None) == -6   # misaligned
     assert L.pa_swap_blocks(ctypes.byref(d), None, None, 0, None, 0, 0, None) == 0
+
+
+def test_decode_ex_flags():
+    L = ops.lib()
+    d = desc()
+    assert L.pa_decode_ex(ctypes.byref(d), None, ops.BF16, 0, 8, None, 4, None, 0.1, None, 0, None,
+                          0, 4, None) == -3
+    assert L.pa_decode_ex(ctypes.byref(d), None, ops.BF16, 0, 8, None, 4, None, 0.1, None, 0, None,
+                          0, 1, None) == 0

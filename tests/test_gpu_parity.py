@@ -331,3 +331,18 @@ def test_copy_blocks_many_pairs_bit_exact(num_pairs, dtype, heads, dim):
     oracle.copy_blocks(kp, vp, dtype, heads, dim, pairs)
     gk, gv = _pool_bytes(pool)
     assert np.array_equal(gk, kp) and np.array_equal(gv, vp)
+
+
+@pytest.mark.parametrize("name", ["sampling_b", "gqa70b", "mha13b", "fp8"])
+def test_shared_kv_flag_changes_nothing_but_cache_policy(name):
+    """pa_decode_ex with PA_DECODE_SHARED_KV (cached loads) and the default
+    streaming loads give bit-identical outputs."""
+    w = wl.make_workload(name, small=True)
+    pool = gpu_pool(w)
+    dev = "cuda"
+    args = (pool, w.q.to(dev), torch.as_tensor(w.block_tables, dtype=torch.int32, device=dev),
+            torch.as_tensor(w.context_lens, dtype=torch.int32, device=dev), w.scale)
+    a = ops.decode(*args, partition_tokens=w.partition_tokens, shared_kv=False)
+    b = ops.decode(*args, partition_tokens=w.partition_tokens, shared_kv=True)
+    torch.cuda.synchronize()
+    assert a.cpu().numpy().tobytes() == b.cpu().numpy().tobytes()
