@@ -99,8 +99,9 @@ def copy_probe(nbytes: int, steps: int) -> None:
 
 
 def source_digest() -> str:
+    """Digest of the sources the matrix-core decode kernel is built from."""
     h = hashlib.sha256()
-    for f in ("pa_decode.hip", "pa_decode_mfma.hip", "pa_internal.h"):
+    for f in ("pa_decode_mfma.hip", "pa_mfma_util.h", "pa_internal.h"):
         h.update(open(os.path.join(ROOT, "paged_kv_cache_401_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
