@@ -99,10 +99,13 @@ def copy_probe(nbytes: int, steps: int) -> None:
 
 
 def source_digest() -> str:
-    """Digest of the sources the matrix-core decode kernel is built from."""
+    """Digest of the sources and compile flags the matrix-core decode kernel
+    is built from."""
+    from paged_kv_cache_401_amd import build as pa_build
     h = hashlib.sha256()
     for f in ("pa_decode_mfma.hip", "pa_mfma_util.h", "pa_internal.h"):
         h.update(open(os.path.join(ROOT, "paged_kv_cache_401_amd", "csrc", f), "rb").read())
+    h.update(" ".join(pa_build.common_flags()).replace(ROOT, "").encode())
     return h.hexdigest()[:16]
 
 

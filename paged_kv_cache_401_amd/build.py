@@ -2,7 +2,8 @@
 
 Every HIP translation unit is compiled with packed-fp32 instructions disabled
 (``-Xclang -target-feature -Xclang -packed-fp32-ops``); the host pass warns
-that it does not know the feature, which is harmless.
+that it does not know the feature, which is harmless.  Matrix-core
+accumulators are kept in ordinary VGPRs (``-mllvm -amdgpu-mfma-vgpr-form``).
 """
 from __future__ import annotations
 
@@ -28,8 +29,12 @@ def hipcc() -> str:
 
 
 def common_flags():
+    # -amdgpu-mfma-vgpr-form: matrix-core accumulators live in ordinary VGPRs
+    # (gfx950 MFMAs take either register file); without it the prefill loop
+    # copied its accumulators between the two files every iteration
     return ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-I", INCLUDE, "-I", CSRC]
 
 

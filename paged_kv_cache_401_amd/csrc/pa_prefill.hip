@@ -23,8 +23,7 @@
 // LDS stages (the next block is already in flight in registers while the
 // current one is computed, and is written to the other stage afterwards; one
 // barrier per block).  Each wavefront reads its matrix-core A operands from
-// LDS at the same offsets the pool's tiled layout gives in memory, and skips
-// the blocks past its own rows' last position.
+// LDS at the same offsets the pool's tiled layout gives in memory.
 //
 // Per block, for each 16-row group (operand layouts as in the grouped decode
 // kernel):
@@ -103,7 +102,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
     // this lane's two rows (one per group): chunk token, head, position
     int row_tok[kGroups], row_head[kGroups], pos_mask[kGroups];
     bool valid[kGroups], live[kGroups];
-    int maxpos = -1, minpos = 0x7fffffff;
+    int minpos = 0x7fffffff;
 #pragma unroll
     for (int k = 0; k < kGroups; ++k) {
         const int r = kRowsPerWave * wave + 16 * k + n;
@@ -114,15 +113,10 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
         live[k] = valid[k] && pos >= 0;
         // rows that produce no output are masked like the context's last token
         pos_mask[k] = live[k] ? pos : ctx - 1;
-        if (live[k]) maxpos = max(maxpos, pos);
         minpos = min(minpos, pos_mask[k]);
     }
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        maxpos = max(maxpos, __shfl_xor(maxpos, o));
-        minpos = min(minpos, __shfl_xor(minpos, o));
-    }
-    const int nblk_wave = maxpos < 0 ? 0 : maxpos / kBlock + 1;
+    for (int o = 1; o < 64; o <<= 1) minpos = min(minpos, __shfl_xor(minpos, o));
 
     // Q^T operands (zero for rows outside the chunk), head dims per the K mapping
     bf16x8 qop[kGroups][NQK];
@@ -177,7 +171,8 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
         }
     };
 
-    auto compute_block = [&](int st, int j) {
+    // `skip`: the block's id is out of range, so all of its tokens are masked
+    auto compute_block = [&](int st, int j, bool skip) {
         const u32x4 *ks = stage[st] + c * kBlock + n;                      // K run c, token n
         const u32x4 *vs = stage[st] + TILE_BYTES / 16 + c * (D / W) + n;  // V cell (tokens 4c.., dims W n..)
         // K operands (fp8 widened to bf16 once, used by both groups)
@@ -198,7 +193,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
                 }
             }
         }
-        const bool need_mask = j * kBlock + kBlock - 1 > minpos;
+        const bool need_mask = skip || j * kBlock + kBlock - 1 > minpos;
         const int nvalid = ctx - j * kBlock;
         uint32_t keep01 = 0xffffffffu, keep23 = 0xffffffffu;
         if (nvalid < kBlock) v_keep_masks(c, nvalid, keep01, keep23);
@@ -214,7 +209,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 sc[i] = sacc[i] * p.qk_scale_log2;
-                if (need_mask && j * kBlock + 4 * c + i > pos_mask[k]) sc[i] = kNegInfF;
+                if (need_mask && (skip || j * kBlock + 4 * c + i > pos_mask[k])) sc[i] = kNegInfF;
             }
             float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
             bm = fmaxf(bm, __shfl_xor(bm, 16));
@@ -282,7 +277,10 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
     }
     __syncthreads();
     for (int j = 0; j < nblk_wg; ++j) {
-        if (j < nblk_wave && ok(id_cur)) compute_block(j & 1, j);
+        // Every wavefront computes every block of the workgroup: blocks past its
+        // own rows are masked out by the causal test (at most one block for
+        // G = 8), and a straight-line loop body keeps the accumulators in place.
+        compute_block(j & 1, j, !ok(id_cur));
         if (j + 1 < nblk_wg && ok(id_next)) swrite((j + 1) & 1, pre);
         int32_t id_after = -1;
         if (j + 2 < nblk_wg) {
