@@ -19,22 +19,23 @@
 // first, so the longest causal ranges start first.
 //
 // Staging.  The workgroup walks blocks 0 .. (its last row's position) / 16.
-// Every block's K and V tiles are loaded once per workgroup into one of two
-// LDS stages (the next block is already in flight in registers while the
-// current one is computed, and is written to the other stage afterwards; one
-// barrier per block).  Each wavefront reads its matrix-core A operands from
-// LDS at the same offsets the pool's tiled layout gives in memory.
+// Every block's K and V tiles are loaded once per workgroup and written to
+// one of two LDS stages (the next block is already in flight in registers
+// while the current one is computed, and is written to the other stage
+// afterwards; one barrier per block).  The stage holds K as bf16 runs and V as
+// duplicated bf16 cells that are directly the A operands of both products
+// (fp8 widened and tokens past the context zeroed once, at staging).
 //
 // Per block, for each 16-row group (operand layouts as in the grouped decode
 // kernel):
 //     S^T[16 tokens][16 rows]  = K[16][D] . Q^T[D][16]
 //     O^T[D][16 rows]         += V^T[D][16 tokens] . P^T[16][16]
 // with P carried as bf16 hi + lo (16 significant bits).  Causal masking sets
-// the score of every token past a row's position to -inf (selection); the V
-// elements of slots past the context are zeroed before the product.  The
-// running maximum is raised lazily: only when a block's maximum exceeds it by
-// more than 8 (in log2 units) are the numerators rescaled, so probabilities
-// stay below 2^8 and most blocks skip the rescale.
+// the score of every token past a row's position to -inf (selection).  The
+// running maximum is raised lazily: only when some lane's block maximum
+// exceeds it by more than 8 (in log2 units) is the row maximum exchanged
+// across lanes and are the numerators rescaled, so probabilities stay below
+// 2^8 and most blocks skip both.
 #include "pa_internal.h"
 #include "pa_mfma_util.h"
 
@@ -65,14 +66,19 @@ __device__ __forceinline__ bf16x8 p_hi_lo_perm(const float (&pr)[4]) {
 template <int KV, int D>
 __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p) {
     constexpr int EB = KV == kBF16 ? 2 : 1;
-    constexpr int TILE_BYTES = kBlock * D * EB;
-    constexpr int STAGE_UNITS = 2 * TILE_BYTES / 16;               // 16-byte units: K tile, V tile
-    constexpr int LOADS = (STAGE_UNITS + kThreads - 1) / kThreads;  // per thread per block
-    constexpr int NQK = D / 32;                       // 32-deep q.K steps per block
-    constexpr int NKL = KV == kBF16 ? NQK : NQK / 2;  // 16-byte K reads per lane per block
-    constexpr int W = 4 / EB;                         // V: head dims per 16-byte cell
-    constexpr int NVL = D / W / 16;                   // 16-byte V reads per lane per block
-    constexpr int NT = D / 16;                        // 16 x 16 output tiles per group
+    constexpr int TILE_BYTES = kBlock * D * EB;                  // one pool tile (K or V)
+    constexpr int SRC_UNITS = 2 * TILE_BYTES / 16;               // 16-byte units loaded per block
+    constexpr int LOADS = (SRC_UNITS + kThreads - 1) / kThreads;  // per thread per block
+    // LDS stage: K as a bf16 tile in the bf16 pool order (D/8 runs x 16 tokens
+    // x 16 bytes), then V as D x 4 duplicated bf16 cells: cell (token group
+    // tg, dim d) = [t0 t1 | t2 t3 | t0 t1 | t2 t3] of dim d, tokens 4 tg..4 tg+3,
+    // zeroed past the context -- exactly the A operand [V | V] of the
+    // hi + lo P.V product
+    constexpr int KS_UNITS = kBlock * D * 2 / 16;
+    constexpr int VS_UNITS = 4 * D;
+    constexpr int STAGE_UNITS = KS_UNITS + VS_UNITS;
+    constexpr int NQK = D / 32;  // 32-deep q.K steps per block
+    constexpr int NT = D / 16;   // 16 x 16 output tiles per group: tile T = head dims 16 T .. 16 T + 15
 
     __shared__ __attribute__((aligned(16))) u32x4 stage[2][STAGE_UNITS];
 
@@ -118,7 +124,8 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) minpos = min(minpos, __shfl_xor(minpos, o));
 
-    // Q^T operands (zero for rows outside the chunk), head dims per the K mapping
+    // Q^T operands (zero for rows outside the chunk): head dims 8 (4 u + c) .. +7
+    // for step u, matching the staged bf16 K runs
     bf16x8 qop[kGroups][NQK];
 #pragma unroll
     for (int k = 0; k < kGroups; ++k) {
@@ -126,22 +133,18 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
                                ((int64_t)(q0 + row_tok[k]) * p.num_q_heads + row_head[k]) * D;
 #pragma unroll
         for (int u = 0; u < NQK; ++u) {
-            int d0;
-            if constexpr (KV == kBF16)
-                d0 = 8 * (4 * u + c);
-            else
-                d0 = 16 * (c + 4 * (u >> 1)) + 8 * (u & 1);
             u32x4 v = {0u, 0u, 0u, 0u};
-            if (valid[k]) v = *reinterpret_cast<const u32x4 *>(qrow + d0);
+            if (valid[k]) v = *reinterpret_cast<const u32x4 *>(qrow + 8 * (4 * u + c));
             qop[k][u] = as_bf16x8(v);
         }
     }
 
-    float m[kGroups], l[kGroups];
+    float m[kGroups], m_use[kGroups], l[kGroups];
     floatx4 acc[kGroups][NT];
 #pragma unroll
     for (int k = 0; k < kGroups; ++k) {
         m[k] = kNegInfF;
+        m_use[k] = 0.f;
         l[k] = 0.f;
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[k][t] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -152,108 +155,131 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
     const u32x4 *vpool = static_cast<const u32x4 *>(p.v_pool);
     auto ok = [&](int32_t b) { return b >= 0 && b < p.num_blocks; };
 
-    // staging: thread t moves 16-byte units t, t + 256, ... of a block's K
-    // tile (units 0 .. TILE/16 - 1) and V tile (the rest), byte for byte
+    // staging: thread t loads 16-byte units t, t + 256, ... of a block's K tile
+    // (units 0 .. TILE/16 - 1) and V tile (the rest) ...
     auto gload = [&](int32_t b, u32x4 (&r)[LOADS]) {
         const int64_t t0 = ((int64_t)b * p.num_kv_heads + g) * (TILE_BYTES / 16);
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
             const int u = threadIdx.x + i * kThreads;
-            if (u < STAGE_UNITS)
+            if (u < SRC_UNITS)
                 r[i] = u < TILE_BYTES / 16 ? kpool[t0 + u] : vpool[t0 + u - TILE_BYTES / 16];
         }
     };
-    auto swrite = [&](int st, const u32x4 (&r)[LOADS]) {
+    // ... and writes them to a stage in the LDS order above (fp8 widened to
+    // bf16, exact); V of tokens at or past `nvalid` is zeroed
+    auto swrite = [&](int st, const u32x4 (&r)[LOADS], int nvalid) {
+        u32x4 *ks = stage[st];
+        u32x4 *vs = stage[st] + KS_UNITS;
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
             const int u = threadIdx.x + i * kThreads;
-            if (u < STAGE_UNITS) stage[st][u] = r[i];
+            if (u >= SRC_UNITS) continue;
+            const u32x4 x = r[i];
+            if (u < TILE_BYTES / 16) {
+                if constexpr (KV == kBF16) {
+                    ks[u] = x;
+                } else {  // fp8 run u / 16 (16 dims) of token u % 16 -> two bf16 runs
+                    const int rr = u >> 4, t = u & 15;
+                    uint32_t a0, a1, a2, a3, b0, b1, b2, b3;
+                    e4m3x4_to_bf16(x[0], a0, a1);
+                    e4m3x4_to_bf16(x[1], a2, a3);
+                    e4m3x4_to_bf16(x[2], b0, b1);
+                    e4m3x4_to_bf16(x[3], b2, b3);
+                    ks[(2 * rr) * kBlock + t] = u32x4{a0, a1, a2, a3};
+                    ks[(2 * rr + 1) * kBlock + t] = u32x4{b0, b1, b2, b3};
+                }
+            } else {
+                const int cu = u - TILE_BYTES / 16;
+                constexpr int W = 4 / EB;  // head dims per pool V cell
+                const int tg = cu / (D / W);
+                const int d0 = W * (cu % (D / W));
+                uint32_t k01 = 0xffffffffu, k23 = 0xffffffffu;
+                if (nvalid < kBlock) v_keep_masks(tg, nvalid, k01, k23);
+                if constexpr (KV == kBF16) {  // words: (t0 t1)(t2 t3) of dim d0, then of d0 + 1
+                    const uint32_t w0 = x[0] & k01, w1 = x[1] & k23, w2 = x[2] & k01, w3 = x[3] & k23;
+                    vs[tg * D + d0] = u32x4{w0, w1, w0, w1};
+                    vs[tg * D + d0 + 1] = u32x4{w2, w3, w2, w3};
+                } else {  // word w: tokens 0..3 of dim d0 + w
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        uint32_t lo, hi;
+                        e4m3x4_to_bf16(x[w], lo, hi);
+                        lo &= k01;
+                        hi &= k23;
+                        vs[tg * D + d0 + w] = u32x4{lo, hi, lo, hi};
+                    }
+                }
+            }
         }
     };
 
     // `skip`: the block's id is out of range, so all of its tokens are masked
     auto compute_block = [&](int st, int j, bool skip) {
-        const u32x4 *ks = stage[st] + c * kBlock + n;                      // K run c, token n
-        const u32x4 *vs = stage[st] + TILE_BYTES / 16 + c * (D / W) + n;  // V cell (tokens 4c.., dims W n..)
-        // K operands (fp8 widened to bf16 once, used by both groups)
+        const u32x4 *ks = stage[st] + c * kBlock + n;  // K run c (+ 4 per step), token n
+        const u32x4 *vs = stage[st] + KS_UNITS + c * D + n;  // V cell (token group c, dim n (+ 16 T))
         bf16x8 kop[NQK];
-        if constexpr (KV == kBF16) {
 #pragma unroll
-            for (int u = 0; u < NQK; ++u) kop[u] = as_bf16x8(ks[u * 4 * kBlock]);
-        } else {
-#pragma unroll
-            for (int i = 0; i < NKL; ++i) {
-                const u32x4 kr = ks[i * 4 * kBlock];
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    uint32_t a0, a1, a2, a3;
-                    e4m3x4_to_bf16(kr[2 * h], a0, a1);
-                    e4m3x4_to_bf16(kr[2 * h + 1], a2, a3);
-                    kop[2 * i + h] = as_bf16x8(u32x4{a0, a1, a2, a3});
-                }
-            }
-        }
+        for (int u = 0; u < NQK; ++u) kop[u] = as_bf16x8(ks[u * 4 * kBlock]);
         const bool need_mask = skip || j * kBlock + kBlock - 1 > minpos;
-        const int nvalid = ctx - j * kBlock;
-        uint32_t keep01 = 0xffffffffu, keep23 = 0xffffffffu;
-        if (nvalid < kBlock) v_keep_masks(c, nvalid, keep01, keep23);
 
-        bf16x8 pop[kGroups];
+        // scores of both groups first, so their matrix-core products issue back to back
+        floatx4 sacc[kGroups];
 #pragma unroll
         for (int k = 0; k < kGroups; ++k) {
-            floatx4 sacc = {0.f, 0.f, 0.f, 0.f};
+            sacc[k] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int u = 0; u < NQK; ++u)
-                sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[u], qop[k][u], sacc, 0, 0, 0);
-            float sc[4];
+                sacc[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[u], qop[k][u], sacc[k], 0, 0, 0);
+        }
+        float sc[kGroups][4], bl[kGroups];
+        bool want = false;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                sc[i] = sacc[i] * p.qk_scale_log2;
-                if (need_mask && (skip || j * kBlock + 4 * c + i > pos_mask[k])) sc[i] = kNegInfF;
-            }
-            float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-            bm = fmaxf(bm, __shfl_xor(bm, 16));
-            bm = fmaxf(bm, __shfl_xor(bm, 32));
-            // raise the running max only past a margin of 2^8; the first block
-            // always raises it (m = -inf).  m stays -inf only while every
-            // token so far was masked, which the guard keeps free of NaN.
-            const bool grow = bm > m[k] + kLazyMax;
-            const float m_new = grow ? bm : m[k];
-            const float m_use = m_new == kNegInfF ? 0.f : m_new;
-            const float alpha = grow ? __builtin_amdgcn_exp2f(m[k] - m_use) : 1.f;
-            float pr[4];
+        for (int k = 0; k < kGroups; ++k) {
+            // tokens 4c + i past `lim` are masked (selection)
+            const int lim = need_mask ? (skip ? -1 : pos_mask[k] - j * kBlock - 4 * c) : 3;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(sc[i] - m_use);
-            m[k] = m_new;
-            l[k] = l[k] * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-            if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+            for (int i = 0; i < 4; ++i) sc[k][i] = i > lim ? kNegInfF : sacc[k][i] * p.qk_scale_log2;
+            bl[k] = fmaxf(fmaxf(sc[k][0], sc[k][1]), fmaxf(sc[k][2], sc[k][3]));
+            want = want || bl[k] > m[k] + kLazyMax;
+        }
+        // the row max is exchanged across lanes, and the running max raised
+        // (rescaling the numerators), only when some lane's block max exceeds
+        // the running max by more than the margin; otherwise every probability
+        // stays below 2^8 and the max stays put
+        if (__builtin_amdgcn_ballot_w64(want) != 0) {
+#pragma unroll
+            for (int k = 0; k < kGroups; ++k) {
+                float bm = fmaxf(bl[k], __shfl_xor(bl[k], 16));
+                bm = fmaxf(bm, __shfl_xor(bm, 32));
+                const bool grow = bm > m[k] + kLazyMax;
+                const float m_new = grow ? bm : m[k];
+                const float mu = m_new == kNegInfF ? 0.f : m_new;
+                const float alpha = grow ? __builtin_amdgcn_exp2f(m[k] - mu) : 1.f;
+                m[k] = m_new;
+                m_use[k] = mu;
+                l[k] *= alpha;
 #pragma unroll
                 for (int t = 0; t < NT; ++t) acc[k][t] *= alpha;
             }
+        }
+        bf16x8 pop[kGroups];
+#pragma unroll
+        for (int k = 0; k < kGroups; ++k) {
+            float pr[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(sc[k][i] - m_use[k]);
+            l[k] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
             pop[k] = p_hi_lo_perm(pr);
         }
 
-        // O^T += V^T . P^T, one MFMA per 16 x 16 output tile and group
+        // O^T += V^T . P^T: the staged cell is the ready [V | V] operand
 #pragma unroll
-        for (int jj = 0; jj < NVL; ++jj) {
-            const u32x4 vr = vs[jj * 16];
+        for (int t = 0; t < NT; ++t) {
+            const bf16x8 a = as_bf16x8(vs[16 * t]);
 #pragma unroll
-            for (int w = 0; w < W; ++w) {
-                uint32_t v01, v23;
-                if constexpr (KV == kBF16) {
-                    v01 = vr[2 * w];
-                    v23 = vr[2 * w + 1];
-                } else {
-                    e4m3x4_to_bf16(vr[w], v01, v23);
-                }
-                v01 &= keep01;
-                v23 &= keep23;
-                const bf16x8 a = as_bf16x8(u32x4{v01, v23, v01, v23});
-#pragma unroll
-                for (int k = 0; k < kGroups; ++k)
-                    acc[k][jj * W + w] =
-                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pop[k], acc[k][jj * W + w], 0, 0, 0);
-            }
+            for (int k = 0; k < kGroups; ++k)
+                acc[k][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pop[k], acc[k][t], 0, 0, 0);
         }
     };
 
@@ -268,7 +294,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
         id_cur = __builtin_amdgcn_readlane(ids, 0);
         if (ok(id_cur)) {
             gload(id_cur, pre);
-            swrite(0, pre);
+            swrite(0, pre, ctx);
         }
         if (nblk_wg > 1) {
             id_next = __builtin_amdgcn_readlane(ids, 1);
@@ -281,7 +307,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
         // own rows are masked out by the causal test (at most one block for
         // G = 8), and a straight-line loop body keeps the accumulators in place.
         compute_block(j & 1, j, !ok(id_cur));
-        if (j + 1 < nblk_wg && ok(id_next)) swrite((j + 1) & 1, pre);
+        if (j + 1 < nblk_wg && ok(id_next)) swrite((j + 1) & 1, pre, ctx - (j + 1) * kBlock);
         int32_t id_after = -1;
         if (j + 2 < nblk_wg) {
             if (((j + 2) & 63) == 0) ids = j + 2 + lane < nblk_wg ? table[j + 2 + lane] : -1;
@@ -293,7 +319,8 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
         __syncthreads();
     }
 
-    // rows: out = O / l (times v_scale); rows before the context start are zero
+    // rows: out = O / l (times v_scale); rows before the context start are zero.
+    // Tile T element i is head dim 16 T + 4 c + i: one float4 per tile.
 #pragma unroll
     for (int k = 0; k < kGroups; ++k) {
         float lt = l[k];
@@ -302,17 +329,12 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
         if (!valid[k]) continue;
         const float f = live[k] && lt > 0.f ? p.out_scale / lt : 0.f;
         float *orow = p.out + ((int64_t)(q0 + row_tok[k]) * p.num_q_heads + row_head[k]) * D;
-        // tile (jj, w) element i is head dim W (16 jj + 4 c + i) + w: 4W contiguous floats per jj
 #pragma unroll
-        for (int jj = 0; jj < NVL; ++jj) {
-            float v[4 * W];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int w = 0; w < W; ++w) v[i * W + w] = live[k] ? acc[k][jj * W + w][i] * f : 0.f;
-            float4 *dst = reinterpret_cast<float4 *>(orow + W * (16 * jj + 4 * c));
-#pragma unroll
-            for (int e = 0; e < W; ++e) dst[e] = make_float4(v[4 * e], v[4 * e + 1], v[4 * e + 2], v[4 * e + 3]);
+        for (int t = 0; t < NT; ++t) {
+            const float4 v = live[k] ? make_float4(acc[k][t][0] * f, acc[k][t][1] * f, acc[k][t][2] * f,
+                                                   acc[k][t][3] * f)
+                                     : make_float4(0.f, 0.f, 0.f, 0.f);
+            *reinterpret_cast<float4 *>(orow + 16 * t + 4 * c) = v;
         }
     }
 }
