@@ -92,7 +92,8 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
     const int part = bid % p.max_partitions;
     bid /= p.max_partitions;
     const int h = bid % p.num_q_heads;
-    const int s = bid / p.num_q_heads;
+    const int s = sequence_of_rank(p.context_lens, p.num_seqs, p.max_blocks_per_seq * kBlock,
+                                   bid / p.num_q_heads);
     const int g = h / p.group;
 
     int ctx = p.context_lens[s];

@@ -51,6 +51,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     constexpr int NVL = D / W / 16;               // 16-byte V loads per lane per block
     constexpr int NT = D / 16;                    // 16 x 16 output tiles (= NVL * W)
     constexpr int LDS_STRIDE = 17;                // [wave][d][head] with padding
+    // K/V register buffers: block k + 1 is in flight while block k is
+    // computed.  Deeper pipelines cost occupancy and measured slower on
+    // MI355X (fp8: 3 buffers at 3 waves/SIMD, 0.228 ms against 0.206 ms).
+    constexpr int DEPTH = 2;
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -61,7 +65,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     const int part = bid % p.max_partitions;
     bid /= p.max_partitions;
     const int g = bid % p.num_kv_heads;
-    const int s = bid / p.num_kv_heads;
+    const int s = sequence_of_rank(p.context_lens, p.num_seqs, p.max_blocks_per_seq * kBlock,
+                                   bid / p.num_kv_heads);
     const int G = p.group;
 
     int ctx = p.context_lens[s];
@@ -189,8 +194,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 
     // This wavefront's blocks are j = blk0 + wave + 4k, k = 0..nk-1.  Their ids
     // are fetched 64 at a time into one VGPR (lane i holds block k0 + i), and
-    // the K/V loads of block k+1 are issued before block k is computed (two
-    // register buffers, A and B, used alternately).
+    // the K/V loads run DEPTH - 1 blocks ahead of the block being computed
+    // (DEPTH register buffers used in turn).
     const int nk = blk1 - blk0 > wave ? (blk1 - blk0 - wave + 3) / 4 : 0;
     for (int k0 = 0; k0 < nk; k0 += 64) {
         const int kend = min(nk, k0 + 64);
@@ -198,31 +203,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         if (k0 + lane < kend) ids = table[blk0 + wave + 4 * (k0 + lane)];
         auto block_id = [&](int k) { return __builtin_amdgcn_readlane(ids, k - k0); };
         auto valid = [&](int32_t b) { return b >= 0 && b < p.num_blocks; };
-        u32x4 kA[NKL], vA[NVL], kB[NKL], vB[NVL];
-        int k = k0;
-        int32_t bA = block_id(k);
-        bool okA = valid(bA);
-        if (okA) load_block(bA, kA, vA);
-        while (true) {
-            const int k1 = k + 1;
-            bool okB = false;
-            if (k1 < kend) {
-                const int32_t bB = block_id(k1);
-                okB = valid(bB);
-                if (okB) load_block(bB, kB, vB);
+        u32x4 kb[DEPTH][NKL], vb[DEPTH][NVL];
+        bool okb[DEPTH];
+#pragma unroll
+        for (int d = 0; d < DEPTH - 1; ++d) {
+            okb[d] = false;
+            if (k0 + d < kend) {
+                const int32_t b = block_id(k0 + d);
+                okb[d] = valid(b);
+                if (okb[d]) load_block(b, kb[d], vb[d]);
             }
-            if (okA) compute_block(kA, vA, blk0 + wave + 4 * k);
-            if (k1 >= kend) break;
-            const int k2 = k1 + 1;
-            okA = false;
-            if (k2 < kend) {
-                bA = block_id(k2);
-                okA = valid(bA);
-                if (okA) load_block(bA, kA, vA);
+        }
+        for (int k = k0; k < kend; k += DEPTH) {
+#pragma unroll
+            for (int d = 0; d < DEPTH; ++d) {
+                const int kk = k + d;
+                if (kk < kend) {
+                    const int dn = (d + DEPTH - 1) % DEPTH;  // the buffer block kk - 1 used
+                    okb[dn] = false;
+                    if (kk + DEPTH - 1 < kend) {
+                        const int32_t b = block_id(kk + DEPTH - 1);
+                        okb[dn] = valid(b);
+                        if (okb[dn]) load_block(b, kb[dn], vb[dn]);
+                    }
+                    if (okb[d]) compute_block(kb[d], vb[d], blk0 + wave + 4 * kk);
+                }
             }
-            if (okB) compute_block(kB, vB, blk0 + wave + 4 * k1);
-            if (k2 >= kend) break;
-            k = k2;
         }
     }
 
