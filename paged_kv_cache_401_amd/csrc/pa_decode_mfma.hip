@@ -10,9 +10,10 @@
 // fp8 (E4M3FN) pool is widened to bf16 in registers, which is exact.
 //
 // Work split: one workgroup per (sequence, KV head, partition of
-// partition_tokens tokens); its four wavefronts take every fourth block and
-// keep their own online-softmax state (running max m and sum l per head,
-// base-2 exponent domain), merged through LDS at the end.  Longer contexts
+// partition_tokens tokens); its four wavefronts (two for short split-K
+// partitions) take every fourth (second) block and keep their own
+// online-softmax state (running max m and sum l per head, base-2 exponent
+// domain), merged through LDS at the end.  Longer contexts
 // leave per-partition (m, l, O) in the workspace for the reduce kernel.
 //
 // Operand layouts (lane = 16 c + n, n = lane % 16):
@@ -41,8 +42,9 @@ namespace {
 
 constexpr float kNegInf = kNegInfF;
 
-template <int KV, int D, bool STREAM>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void decode_mfma_kernel(DecodeParams p) {
+// NW wavefronts per workgroup (4, or 2 for short split-K partitions).
+template <int KV, int D, bool STREAM, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) void decode_mfma_kernel(DecodeParams p) {
     constexpr int EB = KV == kBF16 ? 2 : 1;
     constexpr int TILE_BYTES = kBlock * D * EB;
     constexpr int NQK = D / 32;                   // QK steps (32-deep) per block
@@ -192,15 +194,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         }
     };
 
-    // This wavefront's blocks are j = blk0 + wave + 4k, k = 0..nk-1.  Their ids
+    // This wavefront's blocks are j = blk0 + wave + NW k, k = 0..nk-1.  Their ids
     // are fetched 64 at a time into one VGPR (lane i holds block k0 + i), and
     // the K/V loads run DEPTH - 1 blocks ahead of the block being computed
     // (DEPTH register buffers used in turn).
-    const int nk = blk1 - blk0 > wave ? (blk1 - blk0 - wave + 3) / 4 : 0;
+    const int nk = blk1 - blk0 > wave ? (blk1 - blk0 - wave + NW - 1) / NW : 0;
     for (int k0 = 0; k0 < nk; k0 += 64) {
         const int kend = min(nk, k0 + 64);
         int32_t ids = -1;
-        if (k0 + lane < kend) ids = table[blk0 + wave + 4 * (k0 + lane)];
+        if (k0 + lane < kend) ids = table[blk0 + wave + NW * (k0 + lane)];
         auto block_id = [&](int k) { return __builtin_amdgcn_readlane(ids, k - k0); };
         auto valid = [&](int32_t b) { return b >= 0 && b < p.num_blocks; };
         u32x4 kb[DEPTH][NKL], vb[DEPTH][NVL];
@@ -226,7 +228,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
                         okb[dn] = valid(b);
                         if (okb[dn]) load_block(b, kb[dn], vb[dn]);
                     }
-                    if (okb[d]) compute_block(kb[d], vb[d], blk0 + wave + 4 * kk);
+                    if (okb[d]) compute_block(kb[d], vb[d], blk0 + wave + NW * kk);
                 }
             }
         }
@@ -236,8 +238,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
 
-    __shared__ float sm_m[4][16], sm_l[4][16];
-    __shared__ float sm_acc[4][D * LDS_STRIDE];
+    __shared__ float sm_m[NW][16], sm_l[NW][16];
+    __shared__ float sm_acc[NW][D * LDS_STRIDE];
     if (c == 0) {
         sm_m[wave][n] = m;
         sm_l[wave][n] = l;
@@ -253,13 +255,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
             }
     __syncthreads();
 
-    for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+    for (int idx = threadIdx.x; idx < G * D; idx += 64 * NW) {
         const int hh = idx / D;
         const int d = idx % D;
-        const float M = fmaxf(fmaxf(sm_m[0][hh], sm_m[1][hh]), fmaxf(sm_m[2][hh], sm_m[3][hh]));
+        float M = sm_m[0][hh];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) M = fmaxf(M, sm_m[w][hh]);
         float L = 0.f, O = 0.f;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
+        for (int w = 0; w < NW; ++w) {
             const float f = sm_m[w][hh] == kNegInf ? 0.f : exp2f(sm_m[w][hh] - M);
             L += sm_l[w][hh] * f;
             O += sm_acc[w][d * LDS_STRIDE + hh] * f;
@@ -282,10 +286,21 @@ template <int KV, int D>
 hipError_t launch(const DecodeParams &p, hipStream_t stream) {
     const int64_t grid = (int64_t)p.num_seqs * p.num_kv_heads * p.max_partitions;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-    if (p.shared_kv)
-        decode_mfma_kernel<KV, D, false><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(p);
-    else
-        decode_mfma_kernel<KV, D, true><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(p);
+    // Short split-K partitions (<= 512 tokens: <= 8 blocks per wavefront with
+    // four) go to two-wavefront workgroups, so each wavefront walks twice as
+    // many blocks per start-up and merge.
+    const bool two = p.max_partitions > 1 && p.partition_tokens <= 512;
+    if (p.shared_kv) {
+        if (two)
+            decode_mfma_kernel<KV, D, false, 2><<<dim3((unsigned)grid), dim3(128), 0, stream>>>(p);
+        else
+            decode_mfma_kernel<KV, D, false, 4><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(p);
+    } else {
+        if (two)
+            decode_mfma_kernel<KV, D, true, 2><<<dim3((unsigned)grid), dim3(128), 0, stream>>>(p);
+        else
+            decode_mfma_kernel<KV, D, true, 4><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(p);
+    }
     return hipGetLastError();
 }
 
