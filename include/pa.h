@@ -163,7 +163,9 @@ int pa_decode_ex(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t 
  *                  (16-byte aligned).
  *   query_start    int32 [num_seqs + 1], non-decreasing, query_start[0] = 0.
  *   max_query_len  host-side upper bound of every n_s (sizes the grid);
- *                  chunk tokens beyond it are not computed.  0 is a no-op.
+ *                  chunk tokens beyond it are not computed (their rows of out
+ *                  are left as they were), and those below it keep their
+ *                  positions context_len - n_s + i.  0 is a no-op.
  *   block_tables, max_blocks_per_seq, context_lens, scale: as for pa_decode.
  *   out            fp32 [query_start[num_seqs]][num_q_heads][head_dim]
  *                  (16-byte aligned).  A row whose position is negative (a

@@ -97,9 +97,11 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
     int ctx = p.context_lens[s];
     ctx = ctx < 0 ? 0 : (ctx > p.max_blocks_per_seq * kBlock ? p.max_blocks_per_seq * kBlock : ctx);
     const int q0 = p.query_start[s];
-    int n_new = p.query_start[s + 1] - q0;
-    n_new = n_new < 0 ? 0 : (n_new > p.max_query_len ? p.max_query_len : n_new);
-    const int first = ctx - n_new;  // position of chunk token 0 (< 0: chunk longer than context)
+    int n_chunk = p.query_start[s + 1] - q0;
+    n_chunk = n_chunk < 0 ? 0 : n_chunk;
+    const int first = ctx - n_chunk;  // position of chunk token 0 (< 0: chunk longer than context)
+    // only the chunk's first max_query_len tokens are computed, each at its own position
+    const int n_new = n_chunk > p.max_query_len ? p.max_query_len : n_chunk;
     if (tile * BQ >= n_new) return;
     // the workgroup's blocks: up to its last row's position
     const int pos_last = first + min(tile * BQ + BQ, n_new) - 1;

@@ -15,6 +15,7 @@ from oracle_helpers import oracle_decode, oracle_pools
 from paged_kv_cache_401_amd import workloads as wl
 from paged_kv_cache_401_amd.blocks import BlockManager, blocks_for
 from paged_kv_cache_401_amd.workloads import raw_numpy
+from bitwise import assert_same_bytes
 
 
 def _all_writes(w):
@@ -67,7 +68,7 @@ def test_beam_shared_equals_private_histories():
         for g in range(w.Hkv):
             got = oracle.gather(kp, False, w.pool_dtype, w.Hkv, w.D, w.block_tables[s],
                                 int(w.context_lens[s]), g)
-            assert got.tobytes() == raw_numpy(K[hist[s], g, :]).tobytes()
+            assert_same_bytes(got, raw_numpy(K[hist[s], g, :]))
     mgr = BlockManager(sum(blocks_for(n) for n in w.context_lens))
     kp2 = oracle.new_pool(mgr.num_blocks, w.Hkv, w.D, w.pool_dtype)
     vp2 = oracle.new_pool(mgr.num_blocks, w.Hkv, w.D, w.pool_dtype)
@@ -83,4 +84,4 @@ def test_beam_shared_equals_private_histories():
         t = mgr.block_table(s)
         tables[s, :len(t)] = t
     private = oracle_decode(w, kp2, vp2, tables=tables)
-    assert private.tobytes() == shared.tobytes()
+    assert_same_bytes(private, shared)

@@ -19,6 +19,7 @@ from paged_kv_cache_401_amd import ops
 from paged_kv_cache_401_amd import workloads as wl
 from paged_kv_cache_401_amd.blocks import BlockManager, blocks_for
 from paged_kv_cache_401_amd.workloads import raw_numpy
+from bitwise import assert_same_bytes
 
 pytestmark = pytest.mark.gpu
 
@@ -185,7 +186,7 @@ def test_block_relabelling_is_bit_exact():
     w2.ops = [("write", k, v, (perm[slots // 16] * 16 + slots % 16).astype(np.int32))]
     tables = np.where(w.block_tables >= 0, perm[np.maximum(w.block_tables, 0)], -1)
     out = gpu_decode(w2, gpu_pool(w2), tables=tables.astype(np.int32))
-    assert out.tobytes() == ref.tobytes()
+    assert_same_bytes(out, ref)
 
 
 @pytest.mark.parametrize("name", ["sampling_a", "sampling_b"])
@@ -214,7 +215,7 @@ def test_shared_prefix_equals_private_copies_on_gpu(name):
         t = mgr.block_table(s)
         tables[s, :len(t)] = t
     private = gpu_decode(wp, gpu_pool(wp), tables=tables)
-    assert private.tobytes() == shared.tobytes()
+    assert_same_bytes(private, shared)
 
 
 @pytest.mark.parametrize("name", SMALL)
@@ -224,7 +225,7 @@ def test_poisoned_pool_gives_identical_output(name):
     w = wl.make_workload(name, small=True)
     clean = gpu_decode(w, gpu_pool(w, fill=0))
     poisoned = gpu_decode(w, gpu_pool(w, fill=0xFF))
-    assert poisoned.tobytes() == clean.tobytes()
+    assert_same_bytes(poisoned, clean)
     assert not np.isnan(clean).any()
 
 
@@ -234,7 +235,7 @@ def test_run_to_run_deterministic(name):
     pool = gpu_pool(w)
     a = gpu_decode(w, pool)
     b = gpu_decode(w, pool)
-    assert a.tobytes() == b.tobytes()
+    assert_same_bytes(a, b)
 
 
 def test_empty_and_overlong_contexts():
@@ -248,7 +249,7 @@ def test_empty_and_overlong_contexts():
     ctx2[1] = ctx2[1] + 100  # beyond the table: clamped to max_blocks_per_seq * 16
     out2 = gpu_decode(w, pool, ctx=ctx2)
     ref = gpu_decode(w, pool)
-    assert out2[1].tobytes() == ref[1].tobytes()
+    assert_same_bytes(out2[1], ref[1])
 
 
 # --------------------------------------------------------- full-size configs
@@ -345,4 +346,4 @@ def test_shared_kv_flag_changes_nothing_but_cache_policy(name):
     a = ops.decode(*args, partition_tokens=w.partition_tokens, shared_kv=False)
     b = ops.decode(*args, partition_tokens=w.partition_tokens, shared_kv=True)
     torch.cuda.synchronize()
-    assert a.cpu().numpy().tobytes() == b.cpu().numpy().tobytes()
+    assert_same_bytes(a.cpu().numpy(), b.cpu().numpy())

@@ -11,6 +11,7 @@ from gpu_helpers import gpu_decode, gpu_pool, tolerance
 from oracle_helpers import oracle_decode, oracle_pools
 from paged_kv_cache_401_amd import ops
 from paged_kv_cache_401_amd import workloads as wl
+from bitwise import assert_same_bytes
 
 pytestmark = pytest.mark.gpu
 
@@ -33,7 +34,7 @@ def test_prefix_cache_pool_and_decode_bit_exact():
     torch.cuda.synchronize()
     assert np.array_equal(pa.k.cpu().numpy(), kp) and np.array_equal(pa.v.cpu().numpy(), vp)
     out_a, out_b = gpu_decode(a, pa), gpu_decode(b, pb)
-    assert out_a.tobytes() == out_b.tobytes()
+    assert_same_bytes(out_a, out_b)
     assert float(np.max(np.abs(out_a - oracle_decode(a, kp, vp)))) <= tolerance(a)
 
 
@@ -46,7 +47,7 @@ def test_prefill_of_uncached_rest_equals_whole_prompt_rows():
                            for s in range(a.S)])
     ra = _prefill(a, pa, b.prefill_q[rows].contiguous())
     rb = _prefill(b, pb, b.prefill_q)
-    assert ra.tobytes() == rb[rows].tobytes()
+    assert_same_bytes(ra, rb[rows])
 
 
 def test_prefix_cache_full_size():

@@ -13,6 +13,7 @@ from paged_kv_cache_401_amd import workloads as wl
 from paged_kv_cache_401_amd.blocks import BlockManager
 from paged_kv_cache_401_amd.prefix_cache import PrefixCache
 from paged_kv_cache_401_amd.workloads import raw_numpy
+from bitwise import assert_same_bytes
 
 
 def test_hits_are_exactly_the_full_blocks_of_repeated_system_prompts():
@@ -38,14 +39,14 @@ def test_caching_changes_where_bytes_live_not_outputs():
     kpb, vpb = oracle_pools(b)
     out_a = oracle_decode(a, kpa, vpa)
     out_b = oracle_decode(b, kpb, vpb)
-    assert out_a.tobytes() == out_b.tobytes()
+    assert_same_bytes(out_a, out_b)
     for s in range(a.S):
         for g in (0, a.Hkv - 1):
             ga = oracle.gather(kpa, False, a.pool_dtype, a.Hkv, a.D, a.block_tables[s],
                                int(a.context_lens[s]), g)
             gb = oracle.gather(kpb, False, b.pool_dtype, b.Hkv, b.D, b.block_tables[s],
                                int(b.context_lens[s]), g)
-            assert ga.tobytes() == gb.tobytes()
+            assert_same_bytes(ga, gb)
 
 
 def test_prefill_of_uncached_rest_equals_whole_prompt_prefill():
@@ -67,7 +68,7 @@ def test_prefill_of_uncached_rest_equals_whole_prompt_prefill():
     rb = oracle.prefill_attention(kpb, vpb, b.pool_dtype, b.Hkv, b.D, raw_numpy(qb), b.q_dtype,
                                   b.S, b.Hq, b.query_start, b.block_tables, b.context_lens,
                                   b.scale)
-    assert ra.tobytes() == rb[qa].tobytes()
+    assert_same_bytes(ra, rb[qa])
 
 
 def test_cached_blocks_wait_on_the_free_list_until_reused():
