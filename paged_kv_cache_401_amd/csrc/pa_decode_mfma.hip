@@ -37,6 +37,8 @@
 #include "pa_internal.h"
 #include "pa_mfma_util.h"
 
+#include <type_traits>
+
 namespace pa {
 namespace {
 
@@ -53,10 +55,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
     constexpr int NVL = D / W / 16;               // 16-byte V loads per lane per block
     constexpr int NT = D / 16;                    // 16 x 16 output tiles (= NVL * W)
     constexpr int LDS_STRIDE = 17;                // [wave][d][head] with padding
-    // K/V register buffers: block k + 1 is in flight while block k is
-    // computed.  Deeper pipelines cost occupancy and measured slower on
-    // MI355X (fp8: 3 buffers at 3 waves/SIMD, 0.228 ms against 0.206 ms).
-    constexpr int DEPTH = 2;
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -109,19 +107,37 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
     const char *vbase = static_cast<const char *>(p.v_pool);
     const int koff = (c * kBlock + n) * 16;        // run c, token n
     const int voff = (c * (D / W) + n) * 16;       // cell (tokens 4c.., dims W*n..)
+    auto valid = [&](int32_t b) { return b >= 0 && b < p.num_blocks; };
 
-    auto load_block = [&](int32_t b, u32x4 (&kr)[NKL], u32x4 (&vr)[NVL]) {
-        const int64_t tile = ((int64_t)b * p.num_kv_heads + g) * TILE_BYTES;
-        const char *kt = kbase + tile + koff;
-        const char *vt = vbase + tile + voff;
-#pragma unroll
-        for (int i = 0; i < NKL; ++i) kr[i] = load_kv<STREAM>(kt + i * 4 * kBlock * 16);
-#pragma unroll
-        for (int i = 0; i < NVL; ++i) vr[i] = load_kv<STREAM>(vt + i * 16 * 16);
+    // one tile of a pool as a buffer resource: empty (loads give zeros and
+    // touch no memory) for an id outside the pool or past the end (-1)
+    auto tile = [&](const char *base, int32_t b) {
+        const bool ok = valid(b);
+        return tile_rsrc(base + ((int64_t)(ok ? b : 0) * p.num_kv_heads + g) * TILE_BYTES, ok ? TILE_BYTES : 0);
     };
+    // FENCED: keep the loads in program order (the prologue issues them in
+    // the loop's order, so the loop's waits hold from its first iteration)
+    auto load_k = [&](int32_t b, u32x4 (&kr)[NKL], auto fenced) {
+        const auto r = tile(kbase, b);
+#pragma unroll
+        for (int i = 0; i < NKL; ++i) {
+            kr[i] = load_tile<STREAM>(r, koff + i * 4 * kBlock * 16);
+            if constexpr (decltype(fenced)::value) __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    auto load_v = [&](int32_t b, u32x4 (&vr)[NVL], auto fenced) {
+        const auto r = tile(vbase, b);
+#pragma unroll
+        for (int i = 0; i < NVL; ++i) {
+            vr[i] = load_tile<STREAM>(r, voff + i * 16 * 16);
+            if constexpr (decltype(fenced)::value) __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    constexpr std::true_type kFenced{};
+    constexpr std::false_type kFree{};
 
-    auto compute_block = [&](const u32x4 (&kr)[NKL], const u32x4 (&vr)[NVL], int j) {
-        // S^T = K . Q^T
+    // S^T = K . Q^T for one block
+    auto qk = [&](const u32x4 (&kr)[NKL]) {
         floatx4 sacc = {0.f, 0.f, 0.f, 0.f};
         if constexpr (KV == kBF16) {
 #pragma unroll
@@ -141,7 +157,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
                 }
             }
         }
+        return sacc;
+    };
 
+    // online softmax and O^T += V^T . P^T for block j
+    auto softmax_pv = [&](floatx4 sacc, const u32x4 (&vr)[NVL], int j) {
         // online softmax over this block (tokens 4c..4c+3 of head n in this lane)
         const int nvalid = tok1 - j * kBlock;       // >= 1
         float sc[4];
@@ -151,8 +171,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
             if (4 * c + i >= nvalid) sc[i] = kNegInf;
         }
         float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-        bm = fmaxf(bm, __shfl_xor(bm, 16));
-        bm = fmaxf(bm, __shfl_xor(bm, 32));
+        bm = max_xor32(max_xor16(bm));
         const float m_new = fmaxf(m, bm);
         const float alpha = __builtin_amdgcn_exp2f(m - m_new);
         float pr[4];
@@ -194,49 +213,50 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
         }
     };
 
-    // This wavefront's blocks are j = blk0 + wave + NW k, k = 0..nk-1.  Their ids
-    // are fetched 64 at a time into one VGPR (lane i holds block k0 + i), and
-    // the K/V loads run DEPTH - 1 blocks ahead of the block being computed
-    // (DEPTH register buffers used in turn).
-    const int nk = blk1 - blk0 > wave ? (blk1 - blk0 - wave + NW - 1) / NW : 0;
-    for (int k0 = 0; k0 < nk; k0 += 64) {
-        const int kend = min(nk, k0 + 64);
-        int32_t ids = -1;
-        if (k0 + lane < kend) ids = table[blk0 + wave + NW * (k0 + lane)];
-        auto block_id = [&](int k) { return __builtin_amdgcn_readlane(ids, k - k0); };
-        auto valid = [&](int32_t b) { return b >= 0 && b < p.num_blocks; };
-        u32x4 kb[DEPTH][NKL], vb[DEPTH][NVL];
-        bool okb[DEPTH];
+    // This wavefront's blocks are j = blk0 + wave + NW k, k = 0..nk-1; their ids
+    // come from the table by scalar loads, one block ahead of their use.  Two
+    // register buffers hold blocks k and k + 1; block k + 2 reuses block k's
+    // buffer half by half: its K loads are issued as soon as block k's scores
+    // are computed, its V loads once block k's V is consumed, so a wavefront
+    // keeps close to two blocks in flight in the registers of one.  Every step
+    // issues the same loads (empty resources past the end), which lets each
+    // wait cover exactly the loads it needs.
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const int nk = blk1 - blk0 > wv ? (blk1 - blk0 - wv + NW - 1) / NW : 0;
+    if (nk > 0) {
+        const int32_t *wtable = table + blk0 + wv;
+        auto id_at = [&](int k) -> int32_t {
+            const int32_t b = wtable[NW * min(k, nk - 1)];
+            return k < nk ? b : -1;
+        };
+        u32x4 kb[2][NKL], vb[2][NVL];
+        int32_t idb[2];
 #pragma unroll
-        for (int d = 0; d < DEPTH - 1; ++d) {
-            okb[d] = false;
-            if (k0 + d < kend) {
-                const int32_t b = block_id(k0 + d);
-                okb[d] = valid(b);
-                if (okb[d]) load_block(b, kb[d], vb[d]);
-            }
+        for (int d = 0; d < 2; ++d) {
+            idb[d] = id_at(d);
+            load_k(idb[d], kb[d], kFenced);
+            load_v(idb[d], vb[d], kFenced);
         }
-        for (int k = k0; k < kend; k += DEPTH) {
-#pragma unroll
-            for (int d = 0; d < DEPTH; ++d) {
-                const int kk = k + d;
-                if (kk < kend) {
-                    const int dn = (d + DEPTH - 1) % DEPTH;  // the buffer block kk - 1 used
-                    okb[dn] = false;
-                    if (kk + DEPTH - 1 < kend) {
-                        const int32_t b = block_id(kk + DEPTH - 1);
-                        okb[dn] = valid(b);
-                        if (okb[dn]) load_block(b, kb[dn], vb[dn]);
-                    }
-                    if (okb[d]) compute_block(kb[d], vb[d], blk0 + wave + NW * kk);
-                }
-            }
+        int32_t id_pre = id_at(2);
+        auto step = [&](int d, int kk) {
+            const int32_t id_after = id_pre;  // block kk + 2
+            id_pre = id_at(kk + 3);
+            const floatx4 sacc = qk(kb[d]);
+            load_k(id_after, kb[d], kFree);
+            if (valid(idb[d])) softmax_pv(sacc, vb[d], blk0 + wv + NW * kk);
+            load_v(id_after, vb[d], kFree);
+            idb[d] = id_after;
+        };
+        int k = 0;
+        for (; k + 1 < nk; k += 2) {
+            step(0, k);
+            step(1, k + 1);
         }
+        if (k < nk) step(0, k);
     }
 
     // per-head totals of the lane-partial sums
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    l = add_xor32(add_xor16(l));
 
     __shared__ float sm_m[NW][16], sm_l[NW][16];
     __shared__ float sm_acc[NW][D * LDS_STRIDE];

@@ -40,6 +40,48 @@ __device__ __forceinline__ u32x4 load_kv(const void *p) {
         return *reinterpret_cast<const u32x4 *>(p);
 }
 
+// Buffer resource covering one pool tile: loads through it are bounds-checked
+// by the hardware, and a resource of size 0 turns every load into a zero
+// that touches no memory.  The decode loop issues the same loads every
+// iteration through such resources -- past the end of a wavefront's blocks,
+// or for a block id outside the pool, the size is 0 -- so the compiler can
+// count the loads still in flight exactly, where loads behind branches make
+// it wait for all of them.  Word 3 selects a 32-bit data format (required for
+// untyped buffer loads on this architecture).
+constexpr int kBufWord3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void *tile, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(tile), 0, bytes, kBufWord3);
+}
+
+// 16-byte load at byte offset `off` of a tile resource, non-temporal when
+// STREAM (the cache policy of load_kv)
+template <bool STREAM>
+__device__ __forceinline__ u32x4 load_tile(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, STREAM ? 2 : 0));
+}
+
+// Reductions over lanes i and i ^ 16, and i and i ^ 32, with gfx950's
+// cross-row lane swaps: no LDS traffic, unlike a shuffle through
+// ds_bpermute.  Applied to two copies of x, a swap leaves x_i in one and
+// x_(i^16) (or x_(i^32)) in the other, in an order that differs between
+// rows; max and + do not depend on it.
+__device__ __forceinline__ float max_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float add_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float add_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Longest-first work order for small batches.  Workgroups are dispatched in
 // index order, so the sequence a workgroup takes is the one whose rank, by
 // context length descending (ties by index), is its sequence slot `r`: long
