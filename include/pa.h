@@ -76,7 +76,9 @@ typedef enum pa_status {
     PA_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required */
     PA_ERR_ALIGN = -6,       /* a pointer is not 16-byte aligned */
     PA_ERR_HIP = -7,         /* the HIP runtime reported an error */
-    PA_ERR_RANGE = -8        /* a scale is not finite and positive */
+    PA_ERR_RANGE = -8,       /* a scale is not finite and positive */
+    PA_ERR_INDEX = -9        /* debug mode only: the index data in device memory breaks
+                                the entry point's preconditions (see pa_set_debug) */
 } pa_status;
 
 /* The shared KV block pool.  k_scale / v_scale: per-pool dequantisation
@@ -228,6 +230,71 @@ int pa_copy_blocks(const pa_pool_t *pool, const int32_t *src_dst_pairs, int32_t 
 int pa_swap_blocks(const pa_pool_t *pool, void *host_k, void *host_v, int32_t num_host_slots,
                    const int32_t *block_slot_pairs, int32_t num_pairs, int32_t direction,
                    void *stream);
+
+/*
+ * Index checks.  The entry points above read their index data (context
+ * lengths, block tables, chunk offsets, slots, block pairs) from device
+ * memory and trust it: they skip out-of-range ids and clamp lengths instead
+ * of faulting, and leave repeated slots or destinations as a race.  These
+ * calls check that data on the device against each entry point's stated
+ * preconditions.  Each enqueues its kernels on `stream` and fills `report`,
+ * device int32[3]:
+ *   report[0]  number of faults: one per (element, kind) at fault, where an
+ *              element is a sequence, a chunk offset, a token or a pair;
+ *   report[1]  OR of the PA_FAULT_* kinds found;
+ *   report[2]  smallest index of an element at fault, -1 if none.
+ * A repeated slot or block is a fault of every element that names it.  The
+ * report does not depend on thread timing.  `workspace` (device memory of
+ * pa_check_workspace_size bytes, 4-byte aligned) holds the bitmaps that
+ * find repeats; its contents on entry do not matter.
+ */
+#define PA_FAULT_CONTEXT_LEN 1         /* context_lens[s] < 0 or > max_blocks_per_seq * 16 */
+#define PA_FAULT_BLOCK_ID 2            /* a table entry read for sequence s is outside [0, num_blocks) */
+#define PA_FAULT_SLOT_RANGE 4          /* slot >= num_blocks * 16 (negative slots are skips) */
+#define PA_FAULT_SLOT_REPEATED 8       /* a slot written by two tokens of one call */
+#define PA_FAULT_PAIR_RANGE 16         /* a pair's block (or host slot) outside its range */
+#define PA_FAULT_DST_REPEATED 32       /* copy: destination named twice; swap: block named twice */
+#define PA_FAULT_DST_IS_SRC 64         /* copy: a destination that is also a source */
+#define PA_FAULT_HOST_SLOT_REPEATED 128 /* swap: host slot named twice */
+#define PA_FAULT_QUERY_START 256       /* query_start[0] != 0, or query_start decreases at s */
+
+/* Workspace bytes the checks need for this pool and host pool size. */
+size_t pa_check_workspace_size(const pa_pool_t *pool, int32_t num_host_slots);
+
+/* pa_decode / pa_prefill preconditions on context_lens and block_tables
+ * (elements: sequences). */
+int pa_check_tables(const pa_pool_t *pool, int32_t num_seqs, const int32_t *block_tables,
+                    int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t *report,
+                    void *stream);
+
+/* pa_prefill precondition on query_start[0..num_seqs] (elements: offsets). */
+int pa_check_query_start(int32_t num_seqs, const int32_t *query_start, int32_t *report,
+                         void *stream);
+
+/* pa_reshape_and_cache preconditions on slot_mapping (elements: tokens). */
+int pa_check_slots(const pa_pool_t *pool, const int32_t *slot_mapping, int32_t num_tokens,
+                   void *workspace, size_t workspace_bytes, int32_t *report, void *stream);
+
+/* pa_copy_blocks preconditions on src_dst_pairs (elements: pairs). */
+int pa_check_copy_pairs(const pa_pool_t *pool, const int32_t *src_dst_pairs, int32_t num_pairs,
+                        void *workspace, size_t workspace_bytes, int32_t *report, void *stream);
+
+/* pa_swap_blocks preconditions on block_slot_pairs (elements: pairs). */
+int pa_check_swap_pairs(const pa_pool_t *pool, int32_t num_host_slots,
+                        const int32_t *block_slot_pairs, int32_t num_pairs, void *workspace,
+                        size_t workspace_bytes, int32_t *report, void *stream);
+
+/*
+ * Debug mode (off by default; on at load when the environment variable
+ * PA_DEBUG is 1, or after pa_set_debug(1)).  In it every operation first
+ * runs the matching checks on its stream, waits for them, and returns
+ * PA_ERR_INDEX without enqueueing the operation when any fault is found
+ * (pa_last_error names the kinds and the first index).  Debug mode gives up
+ * two conventions of this header for that: it allocates a device buffer
+ * (kept per device until the process ends) and it synchronises the stream.
+ * Returns the previous setting.
+ */
+int pa_set_debug(int on);
 
 /* Which partition kernel pa_decode launches for this pool and head count:
  * 0 = vector-ALU kernel (one workgroup per query head), 1 = matrix-core

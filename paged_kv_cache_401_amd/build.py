@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libpa.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["pa_api.hip", "pa_cache.hip", "pa_decode.hip", "pa_decode_mfma.hip", "pa_prefill.hip",
+SOURCES = ["pa_api.hip", "pa_cache.hip", "pa_check.hip", "pa_decode.hip", "pa_decode_mfma.hip", "pa_prefill.hip",
            "pa_probe.hip"]
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
 

@@ -3,7 +3,12 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
+
+#include <atomic>
+#include <mutex>
+#include <vector>
 
 #include "pa.h"
 #include "pa_internal.h"
@@ -109,6 +114,96 @@ size_t workspace_for(const pa_pool_t *pool, int32_t num_seqs, int32_t num_q_head
     return (size_t)(acc + 2 * ml);
 }
 
+// ---- debug mode: index checks before every operation -------------------
+
+std::atomic<int> g_debug{-1};  // -1 until PA_DEBUG has been read
+
+bool debug_on() {
+    int d = g_debug.load();
+    if (d < 0) {
+        const char *env = getenv("PA_DEBUG");
+        int want = env && strcmp(env, "1") == 0 ? 1 : 0;
+        g_debug.compare_exchange_strong(d, want);
+        d = g_debug.load();
+    }
+    return d == 1;
+}
+
+// One buffer per device (report words, then the check workspace), grown on
+// demand; held under the lock for the whole check, which ends with a
+// stream synchronisation, so no call can still be using it when another
+// takes it.
+std::mutex g_debug_mu;
+std::vector<std::pair<void *, size_t>> g_debug_buf;
+
+const char *fault_names(int kinds, char *buf, size_t n) {
+    static const char *names[] = {"context length out of range", "block id out of range",
+                                  "slot out of range",           "slot repeated",
+                                  "pair id out of range",        "destination repeated",
+                                  "destination is a source",     "host slot repeated",
+                                  "query_start not non-decreasing from 0"};
+    buf[0] = '\0';
+    for (int k = 0; k < 9; ++k) {
+        if (!(kinds & (1 << k))) continue;
+        if (buf[0]) strncat(buf, ", ", n - strlen(buf) - 1);
+        strncat(buf, names[k], n - strlen(buf) - 1);
+    }
+    return buf;
+}
+
+// Runs `launch(report, workspace)` on `st`, waits, and turns faults into
+// PA_ERR_INDEX.  Called with the operation's arguments already validated.
+template <class Launch>
+int debug_check(const char *what, int64_t ws_bytes, hipStream_t st, Launch launch) {
+    std::lock_guard<std::mutex> lock(g_debug_mu);
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if ((int)g_debug_buf.size() <= dev) g_debug_buf.resize(dev + 1, {nullptr, 0});
+    auto &buf = g_debug_buf[dev];
+    const size_t need = 256 + (size_t)ws_bytes;
+    if (buf.second < need) {
+        if (buf.first) {
+            e = hipFree(buf.first);
+            if (e != hipSuccess) return fail(PA_ERR_HIP, "hipFree: %s", hipGetErrorString(e));
+        }
+        buf = {nullptr, 0};
+        e = hipMalloc(&buf.first, need);
+        if (e != hipSuccess) return fail(PA_ERR_HIP, "debug buffer: %s", hipGetErrorString(e));
+        buf.second = need;
+    }
+    int32_t *report = static_cast<int32_t *>(buf.first);
+    e = launch(report, static_cast<char *>(buf.first) + 256);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    int32_t h[3] = {0, 0, -1};
+    if (e == hipSuccess) e = hipMemcpy(h, report, sizeof(h), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "%s index check: %s", what, hipGetErrorString(e));
+    if (h[0] > 0) {
+        char names[256];
+        return fail(PA_ERR_INDEX, "%s: %d index faults (%s), first at element %d", what, h[0],
+                    fault_names(h[1], names, sizeof(names)), h[2]);
+    }
+    return PA_OK;
+}
+
+int check_report_args(const int32_t *report) {
+    if (!report) return fail(PA_ERR_NULL, "report is NULL");
+    if ((reinterpret_cast<uintptr_t>(report) & 3u) != 0)
+        return fail(PA_ERR_ALIGN, "report must be 4-byte aligned");
+    return PA_OK;
+}
+
+int check_workspace_args(const pa_pool_t *pool, int32_t num_host_slots, const void *workspace,
+                         size_t workspace_bytes) {
+    const size_t need = (size_t)pa::check_workspace_bytes(pool->num_blocks, num_host_slots);
+    if (!workspace || workspace_bytes < need)
+        return fail(PA_ERR_WORKSPACE, "check workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 3u) != 0)
+        return fail(PA_ERR_ALIGN, "workspace must be 4-byte aligned");
+    return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -203,6 +298,13 @@ int pa_decode_ex(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t 
         p.ws_l = reinterpret_cast<float *>(ws + acc + ml);
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (debug_on()) {
+        rc = debug_check("pa_decode", 0, st, [&](int32_t *report, void *) {
+            return pa::launch_check_tables(block_tables, context_lens, num_seqs, max_blocks_per_seq,
+                                           pool->num_blocks, report, st);
+        });
+        if (rc != PA_OK) return rc;
+    }
     const bool mfma = pa::mfma_path_supported(pool->kv_dtype, pool->head_dim, p.group);
     if (g_ev_before) {
         hipError_t e = hipEventRecord(g_ev_before, st);
@@ -265,6 +367,17 @@ int pa_prefill(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t nu
     p.qk_scale_log2 = (float)((double)scale * kscale * 1.4426950408889634);
     p.out_scale = pool->kv_dtype == PA_FP8_E4M3 ? pool->v_scale : 1.0f;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (debug_on()) {
+        rc = debug_check("pa_prefill", 0, st, [&](int32_t *report, void *) {
+            return pa::launch_check_tables(block_tables, context_lens, num_seqs, max_blocks_per_seq,
+                                           pool->num_blocks, report, st);
+        });
+        if (rc == PA_OK)
+            rc = debug_check("pa_prefill", 0, st, [&](int32_t *report, void *) {
+                return pa::launch_check_query_start(query_start, num_seqs, report, st);
+            });
+        if (rc != PA_OK) return rc;
+    }
     if (g_ev_before) {
         hipError_t e = hipEventRecord(g_ev_before, st);
         if (e != hipSuccess) return fail(PA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
@@ -303,8 +416,16 @@ int pa_reshape_and_cache(const pa_pool_t *pool, const void *k, const void *v, in
     p.num_kv_heads = pool->num_kv_heads;
     p.inv_k_scale = pool->kv_dtype == PA_FP8_E4M3 ? 1.0f / pool->k_scale : 1.0f;
     p.inv_v_scale = pool->kv_dtype == PA_FP8_E4M3 ? 1.0f / pool->v_scale : 1.0f;
-    hipError_t e = pa::launch_reshape_and_cache(pool->kv_dtype, kv_dtype, pool->head_dim, p,
-                                                static_cast<hipStream_t>(stream));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (debug_on()) {
+        rc = debug_check("pa_reshape_and_cache", pa::check_workspace_bytes(pool->num_blocks, 0), st,
+                         [&](int32_t *report, void *ws) {
+                             return pa::launch_check_slots(slot_mapping, num_tokens, pool->num_blocks,
+                                                           ws, report, st);
+                         });
+        if (rc != PA_OK) return rc;
+    }
+    hipError_t e = pa::launch_reshape_and_cache(pool->kv_dtype, kv_dtype, pool->head_dim, p, st);
     if (e != hipSuccess) return fail(PA_ERR_HIP, "reshape_and_cache kernel: %s", hipGetErrorString(e));
     return ok();
 }
@@ -316,9 +437,17 @@ int pa_copy_blocks(const pa_pool_t *pool, const int32_t *src_dst_pairs, int32_t 
     if (num_pairs < 0) return fail(PA_ERR_SHAPE, "num_pairs %d is negative", num_pairs);
     if (num_pairs == 0) return ok();
     if (!src_dst_pairs) return fail(PA_ERR_NULL, "src_dst_pairs is NULL");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (debug_on()) {
+        rc = debug_check("pa_copy_blocks", pa::check_workspace_bytes(pool->num_blocks, 0), st,
+                         [&](int32_t *report, void *ws) {
+                             return pa::launch_check_pairs(src_dst_pairs, num_pairs, pool->num_blocks, 0,
+                                                           false, ws, report, st);
+                         });
+        if (rc != PA_OK) return rc;
+    }
     hipError_t e = pa::launch_copy_blocks(pool->k_pool, pool->v_pool, src_dst_pairs, num_pairs,
-                                          pool->num_blocks, pool->num_kv_heads * tile_bytes(pool),
-                                          static_cast<hipStream_t>(stream));
+                                          pool->num_blocks, pool->num_kv_heads * tile_bytes(pool), st);
     if (e != hipSuccess) return fail(PA_ERR_HIP, "copy_blocks kernel: %s", hipGetErrorString(e));
     return ok();
 }
@@ -345,12 +474,105 @@ int pa_swap_blocks(const pa_pool_t *pool, void *host_k, void *host_v, int32_t nu
     if (e != hipSuccess)
         return fail(PA_ERR_HIP, "host pools must be pinned, device-mapped host memory: %s",
                     hipGetErrorString(e));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (debug_on()) {
+        rc = debug_check("pa_swap_blocks", pa::check_workspace_bytes(pool->num_blocks, num_host_slots),
+                         st, [&](int32_t *report, void *ws) {
+                             return pa::launch_check_pairs(block_slot_pairs, num_pairs, pool->num_blocks,
+                                                           num_host_slots, true, ws, report, st);
+                         });
+        if (rc != PA_OK) return rc;
+    }
     e = pa::launch_swap_blocks(pool->k_pool, pool->v_pool, dk, dv, block_slot_pairs, num_pairs,
                                pool->num_blocks, num_host_slots,
-                               pool->num_kv_heads * tile_bytes(pool), direction == PA_SWAP_OUT,
-                               static_cast<hipStream_t>(stream));
+                               pool->num_kv_heads * tile_bytes(pool), direction == PA_SWAP_OUT, st);
     if (e != hipSuccess) return fail(PA_ERR_HIP, "swap_blocks kernel: %s", hipGetErrorString(e));
     return ok();
+}
+
+size_t pa_check_workspace_size(const pa_pool_t *pool, int32_t num_host_slots) {
+    if (check_pool(pool) != PA_OK || num_host_slots < 0) return 0;
+    return (size_t)pa::check_workspace_bytes(pool->num_blocks, num_host_slots);
+}
+
+int pa_check_tables(const pa_pool_t *pool, int32_t num_seqs, const int32_t *block_tables,
+                    int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t *report,
+                    void *stream) {
+    int rc = check_pool(pool);
+    if (rc == PA_OK) rc = check_report_args(report);
+    if (rc != PA_OK) return rc;
+    if (num_seqs < 0) return fail(PA_ERR_SHAPE, "num_seqs %d is negative", num_seqs);
+    if (max_blocks_per_seq <= 0 || max_blocks_per_seq > (1 << 26))
+        return fail(PA_ERR_SHAPE, "max_blocks_per_seq %d out of range", max_blocks_per_seq);
+    if (num_seqs > 0 && (!block_tables || !context_lens))
+        return fail(PA_ERR_NULL, "block_tables and context_lens must be non-NULL");
+    hipError_t e = pa::launch_check_tables(block_tables, context_lens, num_seqs, max_blocks_per_seq,
+                                           pool->num_blocks, report, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "table check: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int pa_check_query_start(int32_t num_seqs, const int32_t *query_start, int32_t *report, void *stream) {
+    int rc = check_report_args(report);
+    if (rc != PA_OK) return rc;
+    if (num_seqs < 0) return fail(PA_ERR_SHAPE, "num_seqs %d is negative", num_seqs);
+    if (!query_start) return fail(PA_ERR_NULL, "query_start is NULL");
+    hipError_t e = pa::launch_check_query_start(query_start, num_seqs, report,
+                                                static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "query_start check: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int pa_check_slots(const pa_pool_t *pool, const int32_t *slot_mapping, int32_t num_tokens,
+                   void *workspace, size_t workspace_bytes, int32_t *report, void *stream) {
+    int rc = check_pool(pool);
+    if (rc == PA_OK) rc = check_report_args(report);
+    if (rc == PA_OK) rc = check_workspace_args(pool, 0, workspace, workspace_bytes);
+    if (rc != PA_OK) return rc;
+    if (num_tokens < 0) return fail(PA_ERR_SHAPE, "num_tokens %d is negative", num_tokens);
+    if (num_tokens > 0 && !slot_mapping) return fail(PA_ERR_NULL, "slot_mapping is NULL");
+    hipError_t e = pa::launch_check_slots(slot_mapping, num_tokens, pool->num_blocks, workspace, report,
+                                          static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "slot check: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int pa_check_copy_pairs(const pa_pool_t *pool, const int32_t *src_dst_pairs, int32_t num_pairs,
+                        void *workspace, size_t workspace_bytes, int32_t *report, void *stream) {
+    int rc = check_pool(pool);
+    if (rc == PA_OK) rc = check_report_args(report);
+    if (rc == PA_OK) rc = check_workspace_args(pool, 0, workspace, workspace_bytes);
+    if (rc != PA_OK) return rc;
+    if (num_pairs < 0) return fail(PA_ERR_SHAPE, "num_pairs %d is negative", num_pairs);
+    if (num_pairs > 0 && !src_dst_pairs) return fail(PA_ERR_NULL, "src_dst_pairs is NULL");
+    hipError_t e = pa::launch_check_pairs(src_dst_pairs, num_pairs, pool->num_blocks, 0, false,
+                                          workspace, report, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "copy pair check: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int pa_check_swap_pairs(const pa_pool_t *pool, int32_t num_host_slots,
+                        const int32_t *block_slot_pairs, int32_t num_pairs, void *workspace,
+                        size_t workspace_bytes, int32_t *report, void *stream) {
+    int rc = check_pool(pool);
+    if (rc == PA_OK) rc = check_report_args(report);
+    if (rc != PA_OK) return rc;
+    if (num_pairs < 0 || num_host_slots < 0)
+        return fail(PA_ERR_SHAPE, "num_pairs %d and num_host_slots %d must be >= 0", num_pairs,
+                    num_host_slots);
+    rc = check_workspace_args(pool, num_host_slots, workspace, workspace_bytes);
+    if (rc != PA_OK) return rc;
+    if (num_pairs > 0 && !block_slot_pairs) return fail(PA_ERR_NULL, "block_slot_pairs is NULL");
+    hipError_t e = pa::launch_check_pairs(block_slot_pairs, num_pairs, pool->num_blocks, num_host_slots,
+                                          true, workspace, report, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "swap pair check: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int pa_set_debug(int on) {
+    const int was = debug_on() ? 1 : 0;
+    g_debug.store(on ? 1 : 0);
+    return was;
 }
 
 int pa_decode_variant(const pa_pool_t *pool, int32_t num_q_heads) {
@@ -380,6 +602,7 @@ const char *pa_strerror(int status) {
     case PA_ERR_ALIGN: return "pointer not 16-byte aligned";
     case PA_ERR_HIP: return "HIP runtime error";
     case PA_ERR_RANGE: return "scale out of range";
+    case PA_ERR_INDEX: return "index data breaks the operation's preconditions (debug mode)";
     default: return "unknown status";
     }
 }
@@ -389,7 +612,7 @@ const char *pa_last_error(void) { return g_last_error; }
 const char *pa_build_info(void) {
     return "libpa gfx950: decode (vector-ALU partition kernel, matrix-core GQA kernel, split-K "
            "reduce), causal chunked prefill (matrix-core), reshape_and_cache (fp32/bf16/fp8-e4m3), "
-           "copy_blocks";
+           "copy_blocks, swap_blocks, device-side index checks";
 }
 
 }  // extern "C"

@@ -87,4 +87,17 @@ hipError_t launch_swap_blocks(void *k_pool, void *v_pool, void *host_k, void *ho
                               int32_t num_host_slots, int64_t block_bytes, bool to_host,
                               hipStream_t stream);
 
+// Index checks (pa_check.hip); each fills a report int32[3] on `stream`.
+int64_t check_workspace_bytes(int32_t num_blocks, int32_t num_host_slots);
+hipError_t launch_check_tables(const int32_t *tables, const int32_t *context_lens, int32_t num_seqs,
+                               int32_t max_blocks_per_seq, int32_t num_blocks, int32_t *report,
+                               hipStream_t stream);
+hipError_t launch_check_query_start(const int32_t *qs, int32_t num_seqs, int32_t *report,
+                                    hipStream_t stream);
+hipError_t launch_check_slots(const int32_t *slots, int32_t n, int32_t num_blocks, void *workspace,
+                              int32_t *report, hipStream_t stream);
+hipError_t launch_check_pairs(const int32_t *pairs, int32_t n, int32_t num_blocks,
+                              int32_t num_host_slots, bool swap, void *workspace, int32_t *report,
+                              hipStream_t stream);
+
 }  // namespace pa

@@ -24,8 +24,17 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 # every symbol include/pa.h declares
 EXPORTS = ("pa_pool_bytes", "pa_decode_partition_tokens", "pa_decode_workspace_size", "pa_decode",
            "pa_decode_ex",
-           "pa_prefill", "pa_reshape_and_cache", "pa_swap_blocks", "pa_copy_blocks", "pa_decode_variant", "pa_set_profile_events",
+           "pa_prefill", "pa_reshape_and_cache", "pa_swap_blocks", "pa_copy_blocks",
+           "pa_check_workspace_size", "pa_check_tables", "pa_check_query_start", "pa_check_slots",
+           "pa_check_copy_pairs", "pa_check_swap_pairs", "pa_set_debug",
+           "pa_decode_variant", "pa_set_profile_events",
            "pa_probe_read", "pa_strerror", "pa_last_error", "pa_build_info")
+
+# index fault kinds of the pa_check_* reports (PA_FAULT_* in pa.h)
+FAULT_CONTEXT_LEN, FAULT_BLOCK_ID, FAULT_SLOT_RANGE, FAULT_SLOT_REPEATED = 1, 2, 4, 8
+FAULT_PAIR_RANGE, FAULT_DST_REPEATED, FAULT_DST_IS_SRC = 16, 32, 64
+FAULT_HOST_SLOT_REPEATED, FAULT_QUERY_START = 128, 256
+ERR_INDEX = -9
 
 
 class PAError(RuntimeError):
@@ -73,6 +82,20 @@ def lib() -> ctypes.CDLL:
     L.pa_swap_blocks.restype = ctypes.c_int
     L.pa_copy_blocks.argtypes = [PD, P, I32, P]
     L.pa_copy_blocks.restype = ctypes.c_int
+    L.pa_check_workspace_size.argtypes = [PD, I32]
+    L.pa_check_workspace_size.restype = SZ
+    L.pa_check_tables.argtypes = [PD, I32, P, I32, P, P, P]
+    L.pa_check_tables.restype = ctypes.c_int
+    L.pa_check_query_start.argtypes = [I32, P, P, P]
+    L.pa_check_query_start.restype = ctypes.c_int
+    L.pa_check_slots.argtypes = [PD, P, I32, P, SZ, P, P]
+    L.pa_check_slots.restype = ctypes.c_int
+    L.pa_check_copy_pairs.argtypes = [PD, P, I32, P, SZ, P, P]
+    L.pa_check_copy_pairs.restype = ctypes.c_int
+    L.pa_check_swap_pairs.argtypes = [PD, I32, P, I32, P, SZ, P, P]
+    L.pa_check_swap_pairs.restype = ctypes.c_int
+    L.pa_set_debug.argtypes = [ctypes.c_int]
+    L.pa_set_debug.restype = ctypes.c_int
     L.pa_decode_variant.argtypes = [PD, I32]
     L.pa_decode_variant.restype = ctypes.c_int
     L.pa_set_profile_events.argtypes = [P, P]
@@ -260,6 +283,75 @@ def prefill(pool: KVPool, q: torch.Tensor, query_start: torch.Tensor, max_query_
                             _dev(context_lens, "context_lens", torch.int32), float(scale),
                             _dev(out, "out", torch.float32), _stream(stream)))
     return out
+
+
+class IndexChecker:
+    """Runs the library's device-side index checks for one pool.  Each check
+    returns (faults, kinds, first): the number of faults, the OR of their
+    FAULT_* kinds and the smallest element index at fault (-1 if none).  It
+    waits for the check's stream to read the report."""
+
+    def __init__(self, pool: KVPool, num_host_slots: int = 0):
+        self.pool = pool
+        self.num_host_slots = int(num_host_slots)
+        d = pool.desc()
+        n = int(lib().pa_check_workspace_size(ctypes.byref(d), self.num_host_slots))
+        if n == 0:
+            raise PAError(-3, "pa_check_workspace_size rejected the pool")
+        self.workspace = torch.empty(n, dtype=torch.uint8, device=pool.k.device)
+        self.report = torch.empty(3, dtype=torch.int32, device=pool.k.device)
+
+    def _result(self, rc, stream):
+        _check(rc)
+        if stream is not None and hasattr(stream, "synchronize"):
+            stream.synchronize()
+        elif stream is not None:
+            torch.cuda.synchronize()
+        return tuple(int(x) for x in self.report.cpu().tolist())
+
+    def tables(self, block_tables: torch.Tensor, context_lens: torch.Tensor, stream=None):
+        d = self.pool.desc()
+        S = context_lens.numel()
+        return self._result(lib().pa_check_tables(
+            ctypes.byref(d), S, _dev(block_tables, "block_tables", torch.int32),
+            block_tables.shape[1], _dev(context_lens, "context_lens", torch.int32),
+            self.report.data_ptr(), _stream(stream)), stream)
+
+    def query_start(self, query_start: torch.Tensor, stream=None):
+        return self._result(lib().pa_check_query_start(
+            query_start.numel() - 1, _dev(query_start, "query_start", torch.int32),
+            self.report.data_ptr(), _stream(stream)), stream)
+
+    def slots(self, slot_mapping: torch.Tensor, stream=None):
+        d = self.pool.desc()
+        n = slot_mapping.numel()
+        ptr = _dev(slot_mapping, "slot_mapping", torch.int32) if n else None
+        return self._result(lib().pa_check_slots(
+            ctypes.byref(d), ptr, n, self.workspace.data_ptr(), self.workspace.numel(),
+            self.report.data_ptr(), _stream(stream)), stream)
+
+    def copy_pairs(self, pairs: torch.Tensor, stream=None):
+        d = self.pool.desc()
+        n = pairs.numel() // 2
+        ptr = _dev(pairs, "pairs", torch.int32) if n else None
+        return self._result(lib().pa_check_copy_pairs(
+            ctypes.byref(d), ptr, n, self.workspace.data_ptr(), self.workspace.numel(),
+            self.report.data_ptr(), _stream(stream)), stream)
+
+    def swap_pairs(self, pairs: torch.Tensor, stream=None):
+        d = self.pool.desc()
+        n = pairs.numel() // 2
+        ptr = _dev(pairs, "pairs", torch.int32) if n else None
+        return self._result(lib().pa_check_swap_pairs(
+            ctypes.byref(d), self.num_host_slots, ptr, n, self.workspace.data_ptr(),
+            self.workspace.numel(), self.report.data_ptr(), _stream(stream)), stream)
+
+
+def set_debug(on: bool) -> bool:
+    """Debug mode: every operation first checks its index data and raises
+    PAError(ERR_INDEX) instead of running when a check finds a fault.
+    Returns the previous setting."""
+    return bool(lib().pa_set_debug(1 if on else 0))
 
 
 def decode_variant(pool: KVPool, num_q_heads: int) -> str:

@@ -163,3 +163,61 @@ def test_decode_ex_flags():
                           0, 4, None) == -3
     assert L.pa_decode_ex(ctypes.byref(d), None, ops.BF16, 0, 8, None, 4, None, 0.1, None, 0, None,
                           0, 1, None) == 0
+
+
+def _words(n):
+    return (n + 31) // 32
+
+
+@pytest.mark.parametrize("nb,hs", [(10, 0), (65536, 0), (1000, 4096), (3, 100000)])
+def test_check_workspace_size(nb, hs):
+    L = ops.lib()
+    w = max(2 * _words(nb * 16), 3 * _words(nb), 2 * _words(nb) + 2 * _words(hs))
+    want = ((w * 4 + 255) // 256) * 256
+    assert L.pa_check_workspace_size(ctypes.byref(desc(num_blocks=nb)), hs) == want
+    assert L.pa_check_workspace_size(ctypes.byref(desc(num_blocks=nb)), -1) == 0
+    assert L.pa_check_workspace_size(None, hs) == 0
+
+
+def test_index_check_argument_rules():
+    """Every check validates its host-side arguments before enqueueing."""
+    L = ops.lib()
+    d = desc()
+    ws = L.pa_check_workspace_size(ctypes.byref(d), 8)
+    # report NULL or misaligned
+    assert L.pa_check_tables(ctypes.byref(d), 1, 16, 4, 16, None, None) == -1
+    assert L.pa_check_tables(ctypes.byref(d), 1, 16, 4, 16, 18, None) == -6
+    assert L.pa_check_tables(ctypes.byref(d), -1, 16, 4, 16, 16, None) == -3
+    assert L.pa_check_tables(ctypes.byref(d), 1, 16, 0, 16, 16, None) == -3
+    assert L.pa_check_tables(ctypes.byref(d), 1, None, 4, 16, 16, None) == -1
+    assert L.pa_check_query_start(1, None, 16, None) == -1
+    assert L.pa_check_query_start(-2, 16, 16, None) == -3
+    assert L.pa_check_query_start(1, 16, None, None) == -1
+    # workspace missing, too small or misaligned
+    assert L.pa_check_slots(ctypes.byref(d), 16, 4, None, 0, 16, None) == -5
+    assert L.pa_check_slots(ctypes.byref(d), 16, 4, 16, ws - 1, 16, None) == -5
+    assert L.pa_check_slots(ctypes.byref(d), 16, 4, 18, ws, 16, None) == -6
+    assert L.pa_check_slots(ctypes.byref(d), 16, -4, 16, ws, 16, None) == -3
+    assert L.pa_check_slots(ctypes.byref(d), None, 4, 16, ws, 16, None) == -1
+    assert L.pa_check_copy_pairs(ctypes.byref(d), 16, -1, 16, ws, 16, None) == -3
+    assert L.pa_check_copy_pairs(ctypes.byref(d), None, 3, 16, ws, 16, None) == -1
+    assert L.pa_check_copy_pairs(ctypes.byref(desc(block_size=8)), 16, 3, 16, ws, 16, None) == -4
+    assert L.pa_check_swap_pairs(ctypes.byref(d), -1, 16, 3, 16, ws, 16, None) == -3
+    assert L.pa_check_swap_pairs(ctypes.byref(d), 8, None, 3, 16, ws, 16, None) == -1
+    # the host pool size enters the workspace size
+    big = L.pa_check_workspace_size(ctypes.byref(d), 1 << 20)
+    assert big > ws
+    assert L.pa_check_swap_pairs(ctypes.byref(d), 1 << 20, 16, 3, 16, ws, 16, None) == -5
+    assert L.pa_last_error().decode()
+
+
+def test_debug_switch_and_status_text():
+    L = ops.lib()
+    was = L.pa_set_debug(1)
+    try:
+        assert L.pa_set_debug(1) == 1
+        assert L.pa_set_debug(0) == 1
+        assert L.pa_set_debug(0) == 0
+    finally:
+        L.pa_set_debug(was)
+    assert "index" in L.pa_strerror(ops.ERR_INDEX).decode()
