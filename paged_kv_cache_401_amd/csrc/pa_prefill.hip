@@ -67,8 +67,6 @@ template <int KV, int D>
 __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p) {
     constexpr int EB = KV == kBF16 ? 2 : 1;
     constexpr int TILE_BYTES = kBlock * D * EB;                  // one pool tile (K or V)
-    constexpr int SRC_UNITS = 2 * TILE_BYTES / 16;               // 16-byte units loaded per block
-    constexpr int LOADS = (SRC_UNITS + kThreads - 1) / kThreads;  // per thread per block
     // LDS stage: K as a bf16 tile in the bf16 pool order (D/8 runs x 16 tokens
     // x 16 bytes), then V as D x 4 duplicated bf16 cells: cell (token group
     // tg, dim d) = [t0 t1 | t2 t3 | t0 t1 | t2 t3] of dim d, tokens 4 tg..4 tg+3,
@@ -153,66 +151,74 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
     }
 
     const int32_t *table = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
-    const u32x4 *kpool = static_cast<const u32x4 *>(p.k_pool);
-    const u32x4 *vpool = static_cast<const u32x4 *>(p.v_pool);
+    const char *kpool = static_cast<const char *>(p.k_pool);
+    const char *vpool = static_cast<const char *>(p.v_pool);
     auto ok = [&](int32_t b) { return b >= 0 && b < p.num_blocks; };
 
-    // staging: thread t loads 16-byte units t, t + 256, ... of a block's K tile
-    // (units 0 .. TILE/16 - 1) and V tile (the rest) ...
-    auto gload = [&](int32_t b, u32x4 (&r)[LOADS]) {
-        const int64_t t0 = ((int64_t)b * p.num_kv_heads + g) * (TILE_BYTES / 16);
+    // Staging.  K: thread t < KU loads pool unit t of the block's K tile and
+    // writes it to the stage (fp8: widened to two bf16 runs).  V: thread t
+    // writes stage cells t, t + 256, ... (cell (tg, d) = unit tg * D + d) and
+    // loads the pool cell holding dim d of token group tg; lanes sharing a
+    // pool cell load the same 16 bytes.  Every lane writes one whole 16-byte
+    // unit after its neighbour's, which keeps the LDS stores free of bank
+    // conflicts.  The loads go through tile resources, so a lane past the K
+    // tile, or a block id out of range, loads zeros without touching memory.
+    constexpr int KU = TILE_BYTES / 16;   // K pool units per block (<= 256)
+    constexpr int VLOADS = VS_UNITS / kThreads;
+    constexpr int W = 4 / EB;             // head dims per pool V cell
+    static_assert(KU <= kThreads && VS_UNITS % kThreads == 0, "staging split");
+    auto gload = [&](int32_t b, u32x4 &kr, u32x4 (&vr)[VLOADS]) {
+        const bool good = ok(b);
+        const int64_t off = ((int64_t)(good ? b : 0) * p.num_kv_heads + g) * TILE_BYTES;
+        const auto kt = tile_rsrc(kpool + off, good ? TILE_BYTES : 0);
+        const auto vt = tile_rsrc(vpool + off, good ? TILE_BYTES : 0);
+        kr = load_tile<false>(kt, threadIdx.x * 16);
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            const int u = threadIdx.x + i * kThreads;
-            if (u < SRC_UNITS)
-                r[i] = u < TILE_BYTES / 16 ? kpool[t0 + u] : vpool[t0 + u - TILE_BYTES / 16];
+        for (int i = 0; i < VLOADS; ++i) {
+            const int su = threadIdx.x + i * kThreads;
+            const int tg = su / D, d = su % D;
+            vr[i] = load_tile<false>(vt, (tg * (D / W) + d / W) * 16);
         }
     };
     // ... and writes them to a stage in the LDS order above (fp8 widened to
     // bf16, exact); V of tokens at or past `nvalid` is zeroed
-    auto swrite = [&](int st, const u32x4 (&r)[LOADS], int nvalid) {
+    auto swrite = [&](int st, const u32x4 &kr, const u32x4 (&vr)[VLOADS], int nvalid) {
         u32x4 *ks = stage[st];
         u32x4 *vs = stage[st] + KS_UNITS;
-#pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            const int u = threadIdx.x + i * kThreads;
-            if (u >= SRC_UNITS) continue;
-            const u32x4 x = r[i];
-            if (u < TILE_BYTES / 16) {
-                if constexpr (KV == kBF16) {
-                    ks[u] = x;
-                } else {  // fp8 run u / 16 (16 dims) of token u % 16 -> two bf16 runs
-                    const int rr = u >> 4, t = u & 15;
-                    uint32_t a0, a1, a2, a3, b0, b1, b2, b3;
-                    e4m3x4_to_bf16(x[0], a0, a1);
-                    e4m3x4_to_bf16(x[1], a2, a3);
-                    e4m3x4_to_bf16(x[2], b0, b1);
-                    e4m3x4_to_bf16(x[3], b2, b3);
-                    ks[(2 * rr) * kBlock + t] = u32x4{a0, a1, a2, a3};
-                    ks[(2 * rr + 1) * kBlock + t] = u32x4{b0, b1, b2, b3};
-                }
-            } else {
-                const int cu = u - TILE_BYTES / 16;
-                constexpr int W = 4 / EB;  // head dims per pool V cell
-                const int tg = cu / (D / W);
-                const int d0 = W * (cu % (D / W));
-                uint32_t k01 = 0xffffffffu, k23 = 0xffffffffu;
-                if (nvalid < kBlock) v_keep_masks(tg, nvalid, k01, k23);
-                if constexpr (KV == kBF16) {  // words: (t0 t1)(t2 t3) of dim d0, then of d0 + 1
-                    const uint32_t w0 = x[0] & k01, w1 = x[1] & k23, w2 = x[2] & k01, w3 = x[3] & k23;
-                    vs[tg * D + d0] = u32x4{w0, w1, w0, w1};
-                    vs[tg * D + d0 + 1] = u32x4{w2, w3, w2, w3};
-                } else {  // word w: tokens 0..3 of dim d0 + w
-#pragma unroll
-                    for (int w = 0; w < 4; ++w) {
-                        uint32_t lo, hi;
-                        e4m3x4_to_bf16(x[w], lo, hi);
-                        lo &= k01;
-                        hi &= k23;
-                        vs[tg * D + d0 + w] = u32x4{lo, hi, lo, hi};
-                    }
-                }
+        const int t = threadIdx.x;
+        if (t < KU) {
+            if constexpr (KV == kBF16) {
+                ks[t] = kr;
+            } else {  // fp8 run t / 16 (16 dims) of token t % 16 -> two bf16 runs
+                const int rr = t >> 4, tt = t & 15;
+                uint32_t a0, a1, a2, a3, b0, b1, b2, b3;
+                e4m3x4_to_bf16(kr[0], a0, a1);
+                e4m3x4_to_bf16(kr[1], a2, a3);
+                e4m3x4_to_bf16(kr[2], b0, b1);
+                e4m3x4_to_bf16(kr[3], b2, b3);
+                ks[(2 * rr) * kBlock + tt] = u32x4{a0, a1, a2, a3};
+                ks[(2 * rr + 1) * kBlock + tt] = u32x4{b0, b1, b2, b3};
             }
+        }
+#pragma unroll
+        for (int i = 0; i < VLOADS; ++i) {
+            const int su = t + i * kThreads;
+            const int tg = su / D, d = su % D;
+            uint32_t k01 = 0xffffffffu, k23 = 0xffffffffu;
+            if (nvalid < kBlock) v_keep_masks(tg, nvalid, k01, k23);
+            uint32_t w0, w1;
+            if constexpr (KV == kBF16) {  // cell words: (t0 t1)(t2 t3) of dim 2m, then of dim 2m + 1
+                const bool odd = d & 1;
+                w0 = odd ? vr[i][2] : vr[i][0];
+                w1 = odd ? vr[i][3] : vr[i][1];
+            } else {  // cell word w: tokens 0..3 of dim 4m + w
+                const int w = d & 3;
+                const uint32_t x = w == 0 ? vr[i][0] : (w == 1 ? vr[i][1] : (w == 2 ? vr[i][2] : vr[i][3]));
+                e4m3x4_to_bf16(x, w0, w1);
+            }
+            w0 &= k01;
+            w1 &= k23;
+            vs[su] = u32x4{w0, w1, w0, w1};
         }
     };
 
@@ -252,8 +258,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
         if (__builtin_amdgcn_ballot_w64(want) != 0) {
 #pragma unroll
             for (int k = 0; k < kGroups; ++k) {
-                float bm = fmaxf(bl[k], __shfl_xor(bl[k], 16));
-                bm = fmaxf(bm, __shfl_xor(bm, 32));
+                const float bm = max_xor32(max_xor16(bl[k]));
                 const bool grow = bm > m[k] + kLazyMax;
                 const float m_new = grow ? bm : m[k];
                 const float mu = m_new == kNegInfF ? 0.f : m_new;
@@ -285,40 +290,35 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
         }
     };
 
-    // Block ids come 64 at a time in one VGPR (lane i: block j0 + i).  Block
+    // Block ids come by scalar loads from the table, two blocks ahead.  Block
     // j is computed from stage j & 1 while block j + 1 is in flight in
     // registers; block j + 1 then goes to the other stage and block j + 2's
-    // loads are issued, and one barrier ends the step.
-    int32_t ids = lane < nblk_wg ? table[lane] : -1;
-    int32_t id_cur = -1, id_next = -1;
-    u32x4 pre[LOADS];
+    // loads are issued (every step issues the same loads), and one barrier
+    // ends the step.
+    auto id_at = [&](int j) -> int32_t {
+        const int32_t b = table[min(j, nblk_wg - 1)];
+        return j < nblk_wg ? b : -1;
+    };
     if (nblk_wg > 0) {
-        id_cur = __builtin_amdgcn_readlane(ids, 0);
-        if (ok(id_cur)) {
-            gload(id_cur, pre);
-            swrite(0, pre, ctx);
-        }
-        if (nblk_wg > 1) {
-            id_next = __builtin_amdgcn_readlane(ids, 1);
-            if (ok(id_next)) gload(id_next, pre);
-        }
-    }
-    __syncthreads();
-    for (int j = 0; j < nblk_wg; ++j) {
-        // Every wavefront computes every block of the workgroup: blocks past its
-        // own rows are masked out by the causal test (at most one block for
-        // G = 8), and a straight-line loop body keeps the accumulators in place.
-        compute_block(j & 1, j, !ok(id_cur));
-        if (j + 1 < nblk_wg && ok(id_next)) swrite((j + 1) & 1, pre, ctx - (j + 1) * kBlock);
-        int32_t id_after = -1;
-        if (j + 2 < nblk_wg) {
-            if (((j + 2) & 63) == 0) ids = j + 2 + lane < nblk_wg ? table[j + 2 + lane] : -1;
-            id_after = __builtin_amdgcn_readlane(ids, (j + 2) & 63);
-            if (ok(id_after)) gload(id_after, pre);
-        }
-        id_cur = id_next;
-        id_next = id_after;
+        int32_t id_cur = id_at(0), id_next = id_at(1);
+        u32x4 kpre, vpre[VLOADS];
+        gload(id_cur, kpre, vpre);
+        swrite(0, kpre, vpre, ctx);
+        gload(id_next, kpre, vpre);
         __syncthreads();
+        for (int j = 0; j < nblk_wg; ++j) {
+            const int32_t id_after = id_at(j + 2);
+            // Every wavefront computes every block of the workgroup: blocks past
+            // its own rows are masked out by the causal test (at most one block
+            // for G = 8), and a straight-line loop body keeps the accumulators
+            // in place.
+            compute_block(j & 1, j, !ok(id_cur));
+            if (j + 1 < nblk_wg) swrite((j + 1) & 1, kpre, vpre, ctx - (j + 1) * kBlock);
+            gload(id_after, kpre, vpre);
+            id_cur = id_next;
+            id_next = id_after;
+            __syncthreads();
+        }
     }
 
     // rows: out = O / l (times v_scale); rows before the context start are zero.
@@ -326,8 +326,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
 #pragma unroll
     for (int k = 0; k < kGroups; ++k) {
         float lt = l[k];
-        lt += __shfl_xor(lt, 16);
-        lt += __shfl_xor(lt, 32);
+        lt = add_xor32(add_xor16(lt));
         if (!valid[k]) continue;
         const float f = live[k] && lt > 0.f ? p.out_scale / lt : 0.f;
         float *orow = p.out + ((int64_t)(q0 + row_tok[k]) * p.num_q_heads + row_head[k]) * D;
