@@ -60,6 +60,14 @@ __device__ __forceinline__ u32x4 load_tile(__amdgpu_buffer_rsrc_t r, int off) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, STREAM ? 2 : 0));
 }
 
+// 8- and 4-byte loads at byte offset `off` of a tile resource (cached)
+__device__ __forceinline__ uint2 load_tile_b64(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+__device__ __forceinline__ uint32_t load_tile_b32(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
 // Reductions over lanes i and i ^ 16, and i and i ^ 32, with gfx950's
 // cross-row lane swaps: no LDS traffic, unlike a shuffle through
 // ds_bpermute.  Applied to two copies of x, a swap leaves x_i in one and

@@ -39,6 +39,8 @@
 #include "pa_internal.h"
 #include "pa_mfma_util.h"
 
+#include <type_traits>
+
 namespace pa {
 namespace {
 
@@ -158,8 +160,8 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
     // Staging.  K: thread t < KU loads pool unit t of the block's K tile and
     // writes it to the stage (fp8: widened to two bf16 runs).  V: thread t
     // writes stage cells t, t + 256, ... (cell (tg, d) = unit tg * D + d) and
-    // loads the pool cell holding dim d of token group tg; lanes sharing a
-    // pool cell load the same 16 bytes.  Every lane writes one whole 16-byte
+    // loads the words of dim d from the pool cell holding it (bf16: 8 bytes,
+    // fp8: 4); the lanes of one pool cell together load its 16 bytes.  Every lane writes one whole 16-byte
     // unit after its neighbour's, which keeps the LDS stores free of bank
     // conflicts.  The loads go through tile resources, so a lane past the K
     // tile, or a block id out of range, loads zeros without touching memory.
@@ -167,7 +169,8 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
     constexpr int VLOADS = VS_UNITS / kThreads;
     constexpr int W = 4 / EB;             // head dims per pool V cell
     static_assert(KU <= kThreads && VS_UNITS % kThreads == 0, "staging split");
-    auto gload = [&](int32_t b, u32x4 &kr, u32x4 (&vr)[VLOADS]) {
+    using VWords = typename std::conditional<KV == kBF16, uint2, uint32_t>::type;
+    auto gload = [&](int32_t b, u32x4 &kr, VWords (&vr)[VLOADS]) {
         const bool good = ok(b);
         const int64_t off = ((int64_t)(good ? b : 0) * p.num_kv_heads + g) * TILE_BYTES;
         const auto kt = tile_rsrc(kpool + off, good ? TILE_BYTES : 0);
@@ -177,12 +180,16 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
         for (int i = 0; i < VLOADS; ++i) {
             const int su = threadIdx.x + i * kThreads;
             const int tg = su / D, d = su % D;
-            vr[i] = load_tile<false>(vt, (tg * (D / W) + d / W) * 16);
+            const int off = (tg * (D / W) + d / W) * 16 + (d % W) * (4 * EB);
+            if constexpr (KV == kBF16)
+                vr[i] = load_tile_b64(vt, off);
+            else
+                vr[i] = load_tile_b32(vt, off);
         }
     };
     // ... and writes them to a stage in the LDS order above (fp8 widened to
     // bf16, exact); V of tokens at or past `nvalid` is zeroed
-    auto swrite = [&](int st, const u32x4 &kr, const u32x4 (&vr)[VLOADS], int nvalid) {
+    auto swrite = [&](int st, const u32x4 &kr, const VWords (&vr)[VLOADS], int nvalid) {
         u32x4 *ks = stage[st];
         u32x4 *vs = stage[st] + KS_UNITS;
         const int t = threadIdx.x;
@@ -203,21 +210,19 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
 #pragma unroll
         for (int i = 0; i < VLOADS; ++i) {
             const int su = t + i * kThreads;
-            const int tg = su / D, d = su % D;
-            uint32_t k01 = 0xffffffffu, k23 = 0xffffffffu;
-            if (nvalid < kBlock) v_keep_masks(tg, nvalid, k01, k23);
-            uint32_t w0, w1;
-            if constexpr (KV == kBF16) {  // cell words: (t0 t1)(t2 t3) of dim 2m, then of dim 2m + 1
-                const bool odd = d & 1;
-                w0 = odd ? vr[i][2] : vr[i][0];
-                w1 = odd ? vr[i][3] : vr[i][1];
-            } else {  // cell word w: tokens 0..3 of dim 4m + w
-                const int w = d & 3;
-                const uint32_t x = w == 0 ? vr[i][0] : (w == 1 ? vr[i][1] : (w == 2 ? vr[i][2] : vr[i][3]));
-                e4m3x4_to_bf16(x, w0, w1);
+            uint32_t w0, w1;  // tokens (t0 t1) and (t2 t3) of dim d as bf16 pairs
+            if constexpr (KV == kBF16) {
+                w0 = vr[i].x;
+                w1 = vr[i].y;
+            } else {
+                e4m3x4_to_bf16(vr[i], w0, w1);
             }
-            w0 &= k01;
-            w1 &= k23;
+            if (nvalid < kBlock) {  // the context's last block: zero the tokens past it
+                uint32_t k01, k23;
+                v_keep_masks(su / D, nvalid, k01, k23);
+                w0 &= k01;
+                w1 &= k23;
+            }
             vs[su] = u32x4{w0, w1, w0, w1};
         }
     };
@@ -240,14 +245,21 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
             for (int u = 0; u < NQK; ++u)
                 sacc[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[u], qop[k][u], sacc[k], 0, 0, 0);
         }
+        // Scaled scores; tokens 4c + i past a row's position are masked by
+        // selection, on the blocks that cross some row's position only.  The
+        // scaled score itself (not a fused multiply-add) enters the exponent,
+        // so the token holding the max gets probability exactly 1.
         float sc[kGroups][4], bl[kGroups];
         bool want = false;
 #pragma unroll
         for (int k = 0; k < kGroups; ++k) {
-            // tokens 4c + i past `lim` are masked (selection)
-            const int lim = need_mask ? (skip ? -1 : pos_mask[k] - j * kBlock - 4 * c) : 3;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sc[k][i] = i > lim ? kNegInfF : sacc[k][i] * p.qk_scale_log2;
+            for (int i = 0; i < 4; ++i) sc[k][i] = sacc[k][i] * p.qk_scale_log2;
+            if (need_mask) {
+                const int lim = skip ? -1 : pos_mask[k] - j * kBlock - 4 * c;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sc[k][i] = i > lim ? kNegInfF : sc[k][i];
+            }
             bl[k] = fmaxf(fmaxf(sc[k][0], sc[k][1]), fmaxf(sc[k][2], sc[k][3]));
             want = want || bl[k] > m[k] + kLazyMax;
         }
@@ -301,7 +313,8 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
     };
     if (nblk_wg > 0) {
         int32_t id_cur = id_at(0), id_next = id_at(1);
-        u32x4 kpre, vpre[VLOADS];
+        u32x4 kpre;
+        VWords vpre[VLOADS];
         gload(id_cur, kpre, vpre);
         swrite(0, kpre, vpre, ctx);
         gload(id_next, kpre, vpre);

@@ -146,6 +146,19 @@ def test_prefill_block_relabelling_bit_exact():
     assert_same_bytes(got, ref)
 
 
+@pytest.mark.parametrize("factor", [-1.0, 0.0, 3.0])
+def test_prefill_any_scale(factor):
+    """A negative scale, a zero scale (uniform weights) and a large one,
+    against the oracle."""
+    w = wl.make_prefill_workload("chunked_gqa70b", small=True)
+    w.scale = float(np.float32(factor * w.scale))
+    kp, vp = oracle_pools(w)
+    ref = oracle_prefill(w, kp, vp)
+    got = gpu_prefill(w, gpu_pool(w))
+    err = float(np.max(np.abs(got - ref)))
+    assert err <= tolerance(w), "max abs error %.3e" % err
+
+
 def test_prefill_poisoned_tail_and_determinism():
     """Unused slots hold NaN (0xFF) in one run and zeros in the other: the
     outputs are identical bit for bit, and repeat runs agree."""
