@@ -11,8 +11,11 @@ module only marshals numpy arrays.  ``dense_attention`` is a numpy/scipy
 restatement used to pin the C code against a library softmax.
 
 Every function cites the page section it follows in ``pa_oracle.c``.
+``index_checks.py`` states, as plain loops, the index preconditions the
+library's device-side checks enforce.
 Parity status: every entry point here is pinned by CPU tests
-(``tests/test_oracle_pins.py``); none is "parity unpinned".
+(``tests/test_oracle_pins.py``, ``tests/test_oracle_prefill_pins.py``,
+``tests/test_index_checks_host.py``); none is "parity unpinned".
 """
 from __future__ import annotations
 

@@ -29,6 +29,8 @@
 #include "pa_internal.h"
 #include "pa_mfma_util.h"
 
+#include <type_traits>
+
 namespace pa {
 namespace {
 
@@ -65,17 +67,26 @@ __device__ __forceinline__ void split_pair(float p0, float p1, uint32_t &hi, uin
     lo = (r0 >> 16) | (r1 & 0xffff0000u);
 }
 
+// max of x and the value lane-permuted by the DPP control CTRL (within rows)
+template <int CTRL>
+__device__ __forceinline__ float max_dpp(float x) {
+    const int y = __builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, 0xf, 0xf, false);
+    return fmaxf(x, __int_as_float(y));
+}
+
 __device__ __forceinline__ float wave_max16(float x) {
-    // maximum over the 16 lanes of a row (xor butterfly inside the row)
-    x = fmaxf(x, __shfl_xor(x, 1));
-    x = fmaxf(x, __shfl_xor(x, 2));
-    x = fmaxf(x, __shfl_xor(x, 4));
-    x = fmaxf(x, __shfl_xor(x, 8));
+    // maximum over the 16 lanes of a row with data-parallel lane moves (no LDS):
+    // swap neighbours, then pairs (quad permutations [1 0 3 2] and [2 3 0 1]),
+    // then mirror each half row and the whole row
+    x = max_dpp<0xB1>(x);
+    x = max_dpp<0x4E>(x);
+    x = max_dpp<0x141>(x);
+    x = max_dpp<0x140>(x);
     return x;
 }
 
 template <int KV, int D, bool STREAM>
-__global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KV == kF32 ? 1 : 4))) void decode_valu_kernel(DecodeParams p) {
     constexpr int EB = KV == kF32 ? 4 : (KV == kBF16 ? 2 : 1);
     constexpr int X = 16 / EB;          // K: elements per 16-byte run
     constexpr int W = 4 / EB;           // V: head-dim elements per 16-byte cell
@@ -144,19 +155,36 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
     const char *kbase = static_cast<const char *>(p.k_pool);
     const char *vbase = static_cast<const char *>(p.v_pool);
 
-    auto load_block = [&](int32_t b, uint4 (&kc)[NKL], uint4 (&vc)[NVL]) {
-        const int64_t tile = ((int64_t)b * p.num_kv_heads + g) * TILE_BYTES;
-        const char *kt = kbase + tile;
-        const char *vt = vbase + tile;
-#pragma unroll
-        for (int jk = 0; jk < NKL; ++jk)
-            kc[jk] = __builtin_bit_cast(uint4, load_kv<STREAM>(kt + ((c + 4 * jk) * kBlock + t) * 16));
-#pragma unroll
-        for (int jj = 0; jj < NVL; ++jj)
-            vc[jj] = __builtin_bit_cast(uint4, load_kv<STREAM>(vt + (c * (D / W) + 16 * jj + t) * 16));
+    auto valid = [&](int32_t b) { return b >= 0 && b < p.num_blocks; };
+    // one tile of a pool as a buffer resource: empty (loads give zeros and
+    // touch no memory) for an id outside the pool or past the end (-1)
+    auto tile = [&](const char *base, int32_t b) {
+        const bool ok = valid(b);
+        return tile_rsrc(base + ((int64_t)(ok ? b : 0) * p.num_kv_heads + g) * TILE_BYTES, ok ? TILE_BYTES : 0);
     };
+    // FENCED keeps the loads in program order (the prologue issues them in the
+    // loop's order, so the loop's waits hold from its first iteration)
+    auto load_k = [&](int32_t b, uint4 (&kc)[NKL], auto fenced) {
+        const auto r = tile(kbase, b);
+#pragma unroll
+        for (int jk = 0; jk < NKL; ++jk) {
+            kc[jk] = __builtin_bit_cast(uint4, load_tile<STREAM>(r, ((c + 4 * jk) * kBlock + t) * 16));
+            if constexpr (decltype(fenced)::value) __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    auto load_v = [&](int32_t b, uint4 (&vc)[NVL], auto fenced) {
+        const auto r = tile(vbase, b);
+#pragma unroll
+        for (int jj = 0; jj < NVL; ++jj) {
+            vc[jj] = __builtin_bit_cast(uint4, load_tile<STREAM>(r, (c * (D / W) + 16 * jj + t) * 16));
+            if constexpr (decltype(fenced)::value) __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    constexpr std::true_type kFenced{};
+    constexpr std::false_type kFree{};
 
-    auto compute_block = [&](const uint4 (&kc)[NKL], const uint4 (&vc)[NVL], int j) {
+    // this lane's partial q . K (its four K runs of token t)
+    auto qk = [&](const uint4 (&kc)[NKL]) {
         float part_dot = 0.f;
 #pragma unroll
         for (int jk = 0; jk < NKL; ++jk) {
@@ -179,8 +207,12 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
                 }
             }
         }
-        part_dot += __shfl_xor(part_dot, 16);
-        part_dot += __shfl_xor(part_dot, 32);
+        return part_dot;
+    };
+
+    // online softmax over block j and acc += p . V
+    auto softmax_pv = [&](float part_dot, const uint4 (&vc)[NVL], int j) {
+        part_dot = add_xor32(add_xor16(part_dot));
 
         float sc = part_dot * p.qk_scale_log2;
         if (j * kBlock + t >= tok1) sc = kNegInf;
@@ -253,54 +285,52 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
         }
     };
 
-    // This wavefront's blocks are j = blk0 + wave + 4k, k = 0..nk-1; ids are
-    // fetched 64 at a time into one VGPR, and block k+1's loads are issued
-    // before block k is computed (register buffers A and B in turn).
-    const int nk = blk1 - blk0 > wave ? (blk1 - blk0 - wave + 3) / 4 : 0;
-    for (int k0 = 0; k0 < nk; k0 += 64) {
-        const int kend = min(nk, k0 + 64);
-        int32_t ids = -1;
-        if (k0 + lane < kend) ids = table[blk0 + wave + 4 * (k0 + lane)];
-        auto block_id = [&](int k) { return __builtin_amdgcn_readlane(ids, k - k0); };
-        auto valid = [&](int32_t b) { return b >= 0 && b < p.num_blocks; };
-        uint4 kA[NKL], vA[NVL], kB[NKL], vB[NVL];
-        int k = k0;
-        int32_t bA = block_id(k);
-        bool okA = valid(bA);
-        if (okA) load_block(bA, kA, vA);
-        while (true) {
-            const int k1 = k + 1;
-            bool okB = false;
-            if (k1 < kend) {
-                const int32_t bB = block_id(k1);
-                okB = valid(bB);
-                if (okB) load_block(bB, kB, vB);
-            }
-            if (okA) compute_block(kA, vA, blk0 + wave + 4 * k);
-            if (k1 >= kend) break;
-            const int k2 = k1 + 1;
-            okA = false;
-            if (k2 < kend) {
-                bA = block_id(k2);
-                okA = valid(bA);
-                if (okA) load_block(bA, kA, vA);
-            }
-            if (okB) compute_block(kB, vB, blk0 + wave + 4 * k1);
-            if (k2 >= kend) break;
-            k = k2;
+    // This wavefront's blocks are j = blk0 + wave + 4k, k = 0..nk-1; their ids
+    // come from the table by scalar loads, one block ahead of their use.  Two
+    // register buffers hold blocks k and k + 1; block k + 2 reuses block k's
+    // buffer half by half (K once its dot products are formed, V once it is
+    // consumed), and every step issues the same loads (empty resources past
+    // the end), so each wait covers exactly the loads it needs.
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const int nk = blk1 - blk0 > wv ? (blk1 - blk0 - wv + 3) / 4 : 0;
+    if (nk > 0) {
+        const int32_t *wtable = table + blk0 + wv;
+        auto id_at = [&](int k) -> int32_t {
+            const int32_t b = wtable[4 * min(k, nk - 1)];
+            return k < nk ? b : -1;
+        };
+        uint4 kb[2][NKL], vb[2][NVL];
+        int32_t idb[2];
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+            idb[d] = id_at(d);
+            load_k(idb[d], kb[d], kFenced);
+            load_v(idb[d], vb[d], kFenced);
         }
+        int32_t id_pre = id_at(2);
+        auto step = [&](int d, int kk) {
+            const int32_t id_after = id_pre;  // block kk + 2
+            id_pre = id_at(kk + 3);
+            const float part = qk(kb[d]);
+            load_k(id_after, kb[d], kFree);
+            if (valid(idb[d])) softmax_pv(part, vb[d], blk0 + wv + 4 * kk);
+            load_v(id_after, vb[d], kFree);
+            idb[d] = id_after;
+        };
+        int k = 0;
+        for (; k + 1 < nk; k += 2) {
+            step(0, k);
+            step(1, k + 1);
+        }
+        if (k < nk) step(0, k);
     }
 
     // add the four token quarters (rows c = 0..3)
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    l = add_xor32(add_xor16(l));
 #pragma unroll
     for (int jj = 0; jj < NVL; ++jj)
 #pragma unroll
-        for (int w = 0; w < W; ++w) {
-            acc[jj][w] += __shfl_xor(acc[jj][w], 16);
-            acc[jj][w] += __shfl_xor(acc[jj][w], 32);
-        }
+        for (int w = 0; w < W; ++w) acc[jj][w] = add_xor32(add_xor16(acc[jj][w]));
 
     __shared__ float sm_m[4], sm_l[4];
     __shared__ float sm_acc[4][D];
