@@ -184,6 +184,7 @@ int pa_prefill(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t nu
  * pa_reshape_and_cache -- write num_tokens new tokens into the pool.
  *   k, v           [num_tokens][num_kv_heads][head_dim] of kv_dtype: the pool's
  *                  dtype for 16/32-bit pools; PA_BF16 or PA_F32 for an FP8 pool.
+ *                  16-byte aligned.
  *   slot_mapping   int32 [num_tokens]: slot = block * 16 + position in block;
  *                  a negative slot skips the token.
  * FP8 pools store the E4M3FN code nearest to fp32(x) * fp32(1 / scale)

@@ -405,6 +405,7 @@ int pa_reshape_and_cache(const pa_pool_t *pool, const void *k, const void *v, in
     if (num_tokens < 0) return fail(PA_ERR_SHAPE, "num_tokens %d is negative", num_tokens);
     if (num_tokens == 0) return ok();
     if (!k || !v || !slot_mapping) return fail(PA_ERR_NULL, "k, v and slot_mapping must be non-NULL");
+    if (!aligned16(k) || !aligned16(v)) return fail(PA_ERR_ALIGN, "k and v must be 16-byte aligned");
     pa::CacheParams p{};
     p.k_pool = pool->k_pool;
     p.v_pool = pool->v_pool;

@@ -55,38 +55,142 @@ __device__ __forceinline__ float load_in(const void *base, int64_t idx) {
     }
 }
 
-// One thread per (token, KV head, head-dim element).
+// One element (token t, head g, dim d) of K and of V to its place in the tiles.
 template <int POOL, int IN, int D>
-__global__ __launch_bounds__(kThreads) void reshape_and_cache_kernel(CacheParams p) {
+__device__ __forceinline__ void write_element(const CacheParams &p, int64_t tok, int g, int d, int32_t slot) {
     constexpr int EB = POOL == kF32 ? 4 : (POOL == kBF16 ? 2 : 1);
     constexpr int X = 16 / EB;   // K: elements per 16-byte run
     constexpr int W = 4 / EB;    // V: head-dim elements per 16-byte cell
-    const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    const int64_t total = p.num_tokens * p.num_kv_heads * D;
-    if (idx >= total) return;
-    const int d = (int)(idx % D);
-    const int64_t row = idx / D;
-    const int g = (int)(row % p.num_kv_heads);
-    const int64_t tok = row / p.num_kv_heads;
-    const int32_t slot = p.slot_mapping[tok];
     if (slot < 0) return;
     const int64_t b = slot >> 4;
     const int t = slot & 15;
     if (b >= p.num_blocks) return;
+    const int64_t idx = (tok * p.num_kv_heads + g) * D + d;
     const int64_t tile = (b * p.num_kv_heads + g) * (int64_t)(kBlock * D);
     const int64_t ko = tile + ((d / X) * kBlock + t) * X + (d % X);
     const int64_t vo = tile + ((t >> 2) * (D / W) + d / W) * (4 * W) + (d % W) * 4 + (t & 3);
     if constexpr (POOL == kFP8) {
-        const float xk = load_in<IN>(p.k, idx) * p.inv_k_scale;
-        const float xv = load_in<IN>(p.v, idx) * p.inv_v_scale;
-        reinterpret_cast<uint8_t *>(p.k_pool)[ko] = (uint8_t)f32_to_e4m3(xk);
-        reinterpret_cast<uint8_t *>(p.v_pool)[vo] = (uint8_t)f32_to_e4m3(xv);
+        reinterpret_cast<uint8_t *>(p.k_pool)[ko] = (uint8_t)f32_to_e4m3(load_in<IN>(p.k, idx) * p.inv_k_scale);
+        reinterpret_cast<uint8_t *>(p.v_pool)[vo] = (uint8_t)f32_to_e4m3(load_in<IN>(p.v, idx) * p.inv_v_scale);
     } else if constexpr (POOL == kBF16) {
         reinterpret_cast<uint16_t *>(p.k_pool)[ko] = reinterpret_cast<const uint16_t *>(p.k)[idx];
         reinterpret_cast<uint16_t *>(p.v_pool)[vo] = reinterpret_cast<const uint16_t *>(p.v)[idx];
     } else {
         reinterpret_cast<uint32_t *>(p.k_pool)[ko] = reinterpret_cast<const uint32_t *>(p.k)[idx];
         reinterpret_cast<uint32_t *>(p.v_pool)[vo] = reinterpret_cast<const uint32_t *>(p.v)[idx];
+    }
+}
+
+// Four consecutive input elements starting at element `idx` as fp8 codes
+// (byte i = element i), each scaled by `inv` and rounded as f32_to_e4m3 does.
+template <int IN>
+__device__ __forceinline__ uint32_t encode4(const void *base, int64_t idx, float inv) {
+    float x[4];
+    if constexpr (IN == kF32) {
+        const float4 v = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(base) + idx);
+        x[0] = v.x, x[1] = v.y, x[2] = v.z, x[3] = v.w;
+    } else {
+        const uint2 v = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(base) + idx);
+        x[0] = __uint_as_float(v.x << 16), x[1] = __uint_as_float(v.x & 0xffff0000u);
+        x[2] = __uint_as_float(v.y << 16), x[3] = __uint_as_float(v.y & 0xffff0000u);
+    }
+    return f32_to_e4m3(x[0] * inv) | (f32_to_e4m3(x[1] * inv) << 8) | (f32_to_e4m3(x[2] * inv) << 16) |
+           (f32_to_e4m3(x[3] * inv) << 24);
+}
+
+// Workgroup (window of 16 input tokens, KV head).  A run is 16 consecutive
+// input tokens whose slots are one whole block in order (16 b .. 16 b + 15:
+// a prompt written block by block).  The workgroup of the window holding a
+// run's first token writes that block's K and V tiles with 16-byte stores:
+// K unit (run r, token t) is the 16-byte run r of token t's input row
+// (converted for an fp8 pool), V cell (token group tg, dims W dw ..) is
+// gathered from four tokens' inputs.  Tokens of the window that no run
+// covers go to their slots element by element (a decode step's tokens, each
+// in a different sequence, or the partial last block of a prompt).  Runs are
+// found by every wavefront alike: lane l looks at token w0 - 16 + l, and
+// ballots mark the tokens whose slot follows the previous one's.
+template <int POOL, int IN, int D>
+__global__ __launch_bounds__(kThreads) void reshape_and_cache_kernel(CacheParams p) {
+    constexpr int EB = POOL == kF32 ? 4 : (POOL == kBF16 ? 2 : 1);
+    constexpr int IB = IN == kF32 ? 4 : 2;          // input bytes per element
+    constexpr int X = 16 / EB;                      // K: elements per 16-byte run
+    constexpr int W = 4 / EB;                       // V: dims per 16-byte cell
+    constexpr int K_UNITS = kBlock * D * EB / 16;   // 16-byte units of one tile
+    const int64_t w0 = (int64_t)blockIdx.x * kBlock;
+    const int g = blockIdx.y;
+    const int lane = threadIdx.x & 63;
+
+    const int64_t tok = w0 - kBlock + lane;
+    const int32_t v = tok >= 0 && tok < p.num_tokens ? p.slot_mapping[tok] : -2;
+    const int32_t nxt = __shfl_down(v, 1);
+    const uint64_t follows = __builtin_amdgcn_ballot_w64(lane < 63 && v >= 0 && (uint32_t)nxt == (uint32_t)v + 1u);
+    const bool start = v >= 0 && (v & 15) == 0 && (v >> 4) < p.num_blocks && lane <= 48 &&
+                       ((follows >> lane) & 0x7fffull) == 0x7fffull;
+    const uint64_t starts = __builtin_amdgcn_ballot_w64(start);
+    // window tokens (lanes 16..31) covered by a run starting at lane 1..31
+    uint64_t covered = 0;
+    for (uint64_t m = starts & 0xfffffffeull; m != 0; m &= m - 1) covered |= 0xffffull << __builtin_ctzll(m);
+    const uint32_t cov = (uint32_t)(covered >> 16) & 0xffffu;
+    const uint32_t mine = (uint32_t)(starts >> 16) & 0xffffu;
+
+    const int64_t nt = p.num_tokens - w0 < kBlock ? p.num_tokens - w0 : kBlock;
+    for (int e = threadIdx.x; e < nt * D; e += kThreads) {
+        const int t = e / D, d = e % D;
+        if (!((cov >> t) & 1u)) write_element<POOL, IN, D>(p, w0 + t, g, d, p.slot_mapping[w0 + t]);
+    }
+    if (!mine) return;
+    const int64_t i0 = w0 + __builtin_ctz(mine);    // the run's first token
+    const int32_t s0 = p.slot_mapping[i0];
+    const int64_t tile = ((int64_t)(s0 >> 4) * p.num_kv_heads + g) * K_UNITS;
+    uint4 *kt = reinterpret_cast<uint4 *>(p.k_pool) + tile;
+    uint4 *vt = reinterpret_cast<uint4 *>(p.v_pool) + tile;
+    auto row = [&](int t) { return ((i0 + t) * p.num_kv_heads + g) * D; };  // first input element
+    for (int u = threadIdx.x; u < K_UNITS; u += kThreads) {
+        const int r = u / kBlock, t = u % kBlock;
+        const int64_t e = row(t) + r * X;
+        uint4 w;
+        if constexpr (POOL == kFP8) {
+            w.x = encode4<IN>(p.k, e, p.inv_k_scale);
+            w.y = encode4<IN>(p.k, e + 4, p.inv_k_scale);
+            w.z = encode4<IN>(p.k, e + 8, p.inv_k_scale);
+            w.w = encode4<IN>(p.k, e + 12, p.inv_k_scale);
+        } else {
+            w = *reinterpret_cast<const uint4 *>(static_cast<const char *>(p.k) + e * IB);
+        }
+        kt[u] = w;
+    }
+    for (int u = threadIdx.x; u < K_UNITS; u += kThreads) {
+        const int tg = u / (D / W), dw = u % (D / W);
+        const int64_t e = row(4 * tg) + W * dw;      // token 4 tg, first dim of the cell
+        const int64_t step = (int64_t)p.num_kv_heads * D;  // next token, same dim
+        uint4 w;
+        if constexpr (POOL == kFP8) {  // word j: tokens 0..3 of dim 4 dw + j
+            uint32_t c[4];
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) c[tt] = encode4<IN>(p.v, e + tt * step, p.inv_v_scale);
+            // c[tt] byte j = (token tt, dim j): transpose the 4 x 4 bytes
+            const uint32_t a0 = __builtin_amdgcn_perm(c[1], c[0], 0x05010400u);  // t0d0 t1d0 t0d1 t1d1
+            const uint32_t a1 = __builtin_amdgcn_perm(c[3], c[2], 0x05010400u);  // t2d0 t3d0 t2d1 t3d1
+            const uint32_t b0 = __builtin_amdgcn_perm(c[1], c[0], 0x07030602u);  // t0d2 t1d2 t0d3 t1d3
+            const uint32_t b1 = __builtin_amdgcn_perm(c[3], c[2], 0x07030602u);  // t2d2 t3d2 t2d3 t3d3
+            w.x = __builtin_amdgcn_perm(a1, a0, 0x05040100u);  // d0: t0 t1 t2 t3
+            w.y = __builtin_amdgcn_perm(a1, a0, 0x07060302u);  // d1
+            w.z = __builtin_amdgcn_perm(b1, b0, 0x05040100u);  // d2
+            w.w = __builtin_amdgcn_perm(b1, b0, 0x07060302u);  // d3
+        } else if constexpr (POOL == kBF16) {  // words: (t0 t1)(t2 t3) of dim 2 dw, then of 2 dw + 1
+            const char *src = static_cast<const char *>(p.v);
+            uint32_t x[4];
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) x[tt] = *reinterpret_cast<const uint32_t *>(src + (e + tt * step) * 2);
+            w.x = __builtin_amdgcn_perm(x[1], x[0], 0x05040100u);
+            w.y = __builtin_amdgcn_perm(x[3], x[2], 0x05040100u);
+            w.z = __builtin_amdgcn_perm(x[1], x[0], 0x07060302u);
+            w.w = __builtin_amdgcn_perm(x[3], x[2], 0x07060302u);
+        } else {  // fp32: tokens 0..3 of dim dw
+            const uint32_t *src = static_cast<const uint32_t *>(p.v);
+            w.x = src[e], w.y = src[e + step], w.z = src[e + 2 * step], w.w = src[e + 3 * step];
+        }
+        vt[u] = w;
     }
 }
 
@@ -171,10 +275,10 @@ __global__ __launch_bounds__(kThreads) void swap_blocks_kernel(char *k_pool, cha
 
 template <int POOL, int IN, int D>
 hipError_t launch_rc(const CacheParams &p, hipStream_t stream) {
-    const int64_t total = p.num_tokens * p.num_kv_heads * D;
-    const int64_t blocks = (total + kThreads - 1) / kThreads;
-    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    reshape_and_cache_kernel<POOL, IN, D><<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(p);
+    const int64_t groups = (p.num_tokens + kBlock - 1) / kBlock;
+    if (groups > 0x7fffffffLL || p.num_kv_heads > 65535) return hipErrorInvalidValue;
+    reshape_and_cache_kernel<POOL, IN, D>
+        <<<dim3((unsigned)groups, (unsigned)p.num_kv_heads), dim3(kThreads), 0, stream>>>(p);
     return hipGetLastError();
 }
 

@@ -41,6 +41,59 @@ def test_cache_write_and_copy_bit_exact(name):
     assert np.array_equal(gv, vp), "V pool bytes differ"
 
 
+def _mixed_slots(rng, nb):
+    """A slot mapping mixing what a cache write meets: whole blocks in order
+    at arbitrary input offsets, a block written out of order, partial blocks,
+    runs that straddle two blocks, skipped tokens and an out-of-range slot."""
+    blocks = rng.permutation(nb)
+    parts, k = [], 0
+    for kind in rng.permutation(np.repeat(np.arange(6), 6)):
+        b = int(blocks[k]); k += 1
+        base = np.arange(16 * b, 16 * b + 16)
+        if kind == 0:                      # whole block in order (a run)
+            parts.append(base)
+        elif kind == 1:                    # whole block, shuffled
+            parts.append(rng.permutation(base))
+        elif kind == 2:                    # partial block
+            parts.append(base[:int(rng.integers(1, 16))])
+        elif kind == 3:                    # in order, but straddling into the next block
+            b2 = int(blocks[k]); k += 1
+            parts.append(np.concatenate([base[5:], np.arange(16 * b2, 16 * b2 + 5)]))
+        elif kind == 4:                    # a run with a skipped token in it
+            x = base.copy()
+            x[int(rng.integers(0, 16))] = -1
+            parts.append(x)
+        else:                              # a run, then one token past the pool
+            parts.append(np.concatenate([base, [16 * nb + 3]]))
+    return np.concatenate(parts).astype(np.int32)
+
+
+@pytest.mark.parametrize("pool_dt,in_dt", [(ops.F32, ops.F32), (ops.BF16, ops.BF16),
+                                           (ops.FP8, ops.BF16), (ops.FP8, ops.F32)])
+@pytest.mark.parametrize("D", [64, 128])
+def test_cache_write_mixed_slot_runs_bit_exact(pool_dt, in_dt, D):
+    """Whole-block runs are written tile by tile and everything else element
+    by element; the pool bytes equal the oracle's either way."""
+    rng = np.random.default_rng(11 + D + 3 * pool_dt + in_dt)
+    nb, Hkv = 64, 3
+    slots = _mixed_slots(rng, nb)
+    n = slots.size
+    tdt = torch.float32 if in_dt == ops.F32 else torch.bfloat16
+    gen = torch.Generator().manual_seed(int(rng.integers(1 << 30)))
+    k = (torch.randn((n, Hkv, D), generator=gen) * 3).to(tdt)
+    v = (torch.randn((n, Hkv, D), generator=gen) * 3).to(tdt)
+    scale = 0.05 if pool_dt == ops.FP8 else 1.0
+    kp = oracle.new_pool(nb, Hkv, D, pool_dt, fill=0xFF)
+    vp = oracle.new_pool(nb, Hkv, D, pool_dt, fill=0xFF)
+    oracle.reshape_and_cache(kp, vp, pool_dt, nb, Hkv, D, raw_numpy(k), raw_numpy(v), in_dt, slots,
+                             scale, scale)
+    pool = ops.KVPool(nb, Hkv, D, pool_dt, k_scale=scale, v_scale=scale, fill=0xFF)
+    ops.reshape_and_cache(pool, k.cuda(), v.cuda(), torch.from_numpy(slots).cuda())
+    gk, gv = _pool_bytes(pool)
+    assert np.array_equal(gk, kp), "K pool bytes differ"
+    assert np.array_equal(gv, vp), "V pool bytes differ"
+
+
 @pytest.mark.parametrize("scale", [1.0, 0.37])
 def test_fp8_encoder_bit_exact_over_dense_fp32_sweep(scale):
     """Every fp32 pattern of the form (hi 24 bits, random low 8 bits) plus the
