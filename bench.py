@@ -58,7 +58,14 @@ WORKLOAD_TEXT["prefix"] = ("prefix caching by full-block hashing: 128 requests o
                            "(64..2048 tokens) + 16..512 private tokens, 64 q / 8 KV heads, head_dim "
                            "128, bf16; prompt processing = cache write + causal prefill of each "
                            "request's uncached tokens over its (partly cached) context")
+WORKLOAD_TEXT["fill_gqa70b"] = ("bulk cache write: the 70B-like layer's 1,048,576 prompt tokens (256 "
+                                "seqs x 4096, 8 KV heads, head_dim 128, bf16) into scattered 16-token "
+                                "blocks of a 65536-block pool")
+WORKLOAD_TEXT["fill_fp8"] = ("bulk cache write with fp8 encoding: the long-tail workload's prompt tokens "
+                             "(128 seqs, lognormal contexts, 8 KV heads, head_dim 128) from bf16 into "
+                             "an e4m3 pool")
 PREFILL = ("prefill_gqa70b", "prefill_mha13b", "chunked_gqa70b", "chunked_fp8")
+FILL = {"fill_gqa70b": "gqa70b", "fill_fp8": "fp8"}
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 DTYPE_NAME = {0: "f32", 1: "bf16", 2: "fp8e4m3"}
 
@@ -137,6 +144,9 @@ def main():
         return
     if args.workload == "swap":
         run_swap(args)
+        return
+    if args.workload in FILL:
+        run_fill(args)
         return
     if args.workload == "prefix":
         run_prefix(args)
@@ -472,6 +482,73 @@ def run_prefix(args):
                      "traffic": None, "kernel": "prefill_mfma_kernel",
                      "algorithmic_flops_per_launch": flops},
     }
+    print(json.dumps(rec), flush=True)
+
+
+def run_fill(args):
+    """The cache write of a whole workload's tokens per step (the bulk fill of
+    the pool when prompts are stored); ``value`` is algorithmic bytes (K and V
+    inputs read + pool tiles written) per second, against the HBM peak."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from paged_kv_cache_401_amd import ops
+    from paged_kv_cache_401_amd import workloads as wl
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    w = wl.make_workload(FILL[args.workload], small=False, device=dev)
+    pool = ops.KVPool(w.num_blocks, w.Hkv, w.D, w.pool_dtype, device=dev, k_scale=w.k_scale,
+                      v_scale=w.v_scale, fill=0)
+    _, k, v, slots = w.ops[0]
+    st = torch.as_tensor(slots, dtype=torch.int32, device=dev)
+    n = int(slots.size)
+    nbytes = 2 * k.numel() * k.element_size() + 2 * k.numel() * ops.ELEM_BYTES[w.pool_dtype]
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        ops.reshape_and_cache(pool, k, v, st)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[2 * i].record(stream)
+        ops.reshape_and_cache(pool, k, v, st)
+        ev[2 * i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    ms = float(np.mean([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(args.steps)]))
+    gbps = nbytes / ms / 1e6
+    rec = {
+        "metric": "pa_reshape_and_cache bulk GB/s (K/V read + pool written) at 1 MI355X",
+        "value": round(gbps, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": DTYPE_NAME[w.pool_dtype],
+        "data": "synthetic (seeded N(0,1) K/V, scattered 16-token blocks)",
+        "config": {"workload": WORKLOAD_TEXT[args.workload], "tokens": n, "num_kv_heads": w.Hkv,
+                   "head_dim": w.D, "algorithmic_bytes": nbytes, "parallelism": "single GPU"},
+        "wall_ms_per_step": round(1e3 * wall, 4),
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "reshape_and_cache_kernel", "algorithmic_bytes_per_launch": nbytes},
+    }
+    if not args.no_cpu_baseline:
+        # the oracle's cache write of the first tokens (about a tenth), scaled to GB/s
+        m = max(16, n // 10)
+        kn = k[:m].cpu().contiguous()
+        vn = v[:m].cpu().contiguous()
+        from paged_kv_cache_401_amd.workloads import raw_numpy
+        kr, vr = raw_numpy(kn), raw_numpy(vn)
+        kp = oracle.new_pool(w.num_blocks, w.Hkv, w.D, w.pool_dtype)
+        vp = oracle.new_pool(w.num_blocks, w.Hkv, w.D, w.pool_dtype)
+        c0 = time.perf_counter()
+        oracle.reshape_and_cache(kp, vp, w.pool_dtype, w.num_blocks, w.Hkv, w.D, kr, vr, w.kv_in_dtype,
+                                 slots[:m], w.k_scale, w.v_scale)
+        cpu_s = time.perf_counter() - c0
+        rec["cpu_baseline"] = {"value": round(nbytes * m / n / cpu_s / 1e9, 4), "unit": "GB/s",
+                               "cores": 1, "kind": "oracle",  # the oracle's write loop is serial
+                               "sample": "first %d of %d tokens through the C oracle's cache write"
+                                         % (m, n), "seconds": round(cpu_s, 3)}
     print(json.dumps(rec), flush=True)
 
 
