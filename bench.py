@@ -82,6 +82,9 @@ def parse():
     ap.add_argument("--cpu-seqs", type=int, default=None,
                     help="sequences in the CPU-oracle sample (default: ~10-30 s of CPU work)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="decode workloads: also capture one step into a HIP graph and time its "
+                         "replays (reported as graph_ms_per_step)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="instead of the benchmark, run a plain device copy of BYTES bytes "
                          "--steps times (reference for hardware byte counters)")
@@ -300,10 +303,41 @@ def main():
     }
     if copy_rec is not None:
         rec["copy_blocks"] = copy_rec
+    if args.graph:
+        rec["graph"] = graph_step_time(step, args.steps, w.S)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"], rec["max_abs_err_vs_oracle_sample"] = cpu_baseline(
             w, args, out, pool)
     print(json.dumps(rec), flush=True)
+
+
+def graph_step_time(step, steps, num_seqs):
+    """The same step captured once into a HIP graph and replayed: the launch
+    cost of its kernels is paid once at capture."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    a.record()
+    for _ in range(steps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    ms = a.elapsed_time(b) / steps
+    return {"ms_per_step": round(ms, 5), "wall_ms_per_step": round(1e3 * wall, 5),
+            "decode_seqs_per_s": round(num_seqs / (ms * 1e-3), 1)}
 
 
 def run_prefill(args):
