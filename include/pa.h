@@ -29,7 +29,8 @@
  * Conventions for every entry point
  *   - Pointers are device pointers unless stated; the caller owns every
  *     buffer and keeps it alive until the enqueued work completes.  The
- *     library allocates no device memory and keeps no pointer after return.
+ *     library allocates no device memory (debug mode aside, see pa_set_debug)
+ *     and keeps no pointer after return.
  *   - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
  *     work on it and never synchronise the host.
  *   - Return value: PA_OK (0) or a negative pa_status.  On error nothing is
