@@ -208,6 +208,28 @@ def test_one_hot_probe_is_bit_exact(case, ptok):
                 assert np.array_equal(out[s, h], v[h // (Hq // Hkv)]), (case, s, h, targets[s])
 
 
+@pytest.mark.parametrize("group", [2, 4, 16, 32])
+@pytest.mark.parametrize("D,dt", [(64, oracle.BF16), (128, oracle.BF16), (128, oracle.FP8),
+                                  (64, oracle.F32)])
+@pytest.mark.parametrize("ptok", [0, 64])
+def test_decode_group_sizes(group, D, dt, ptok):
+    """Query groups at the edges of the matrix-core kernel (2 and 16 query
+    heads per KV head), between them (4), and past it (32: the vector-ALU
+    kernel), for both head dims and every pool type, on ragged contexts."""
+    Hkv = 2
+    ctx = [1, 17, 300, 129, 64]
+    rng = np.random.default_rng(group * 7 + D + dt)
+    in_dt = oracle.F32 if dt == oracle.F32 else oracle.BF16
+    w = wl._simple("groups", len(ctx), group * Hkv, Hkv, D, ctx, dt, in_dt, in_dt,
+                   float(np.float32(1 / math.sqrt(D))), 21, "cpu", rng, fp8_scales=dt == oracle.FP8)
+    kp, vp = oracle_pools(w)
+    ref = oracle_decode(w, kp, vp)
+    got = gpu_decode(w, gpu_pool(w, fill=0xFF), partition_tokens=ptok)
+    assert np.isfinite(got).all()
+    err = float(np.max(np.abs(got - ref)))
+    assert err <= tolerance(w), "max abs error %.3e" % err
+
+
 @pytest.mark.parametrize("Hq", [1, 2])
 def test_fp8_decode_all_codes_through_attention(Hq):
     """A one-hot probe on tokens whose V rows hold all 256 E4M3FN codes: the
