@@ -3,8 +3,10 @@
 A step is the whole hot path over one batch: the copy-on-write block copies
 (none for workloads without shared partial blocks), the cache write of every
 sequence's newest token, and paged decode attention (partition kernel plus
-split-K reduce when contexts span several partitions).  Inputs are synthetic
-and seeded and already resident in HBM when timing starts.
+split-K reduce when contexts span several partitions).  The newest tokens are
+written by the cache-write kernel before the decode call (default), or by the
+decode call itself with ``--append fused`` (pa_decode_append).  Inputs are
+synthetic and seeded and already resident in HBM when timing starts.
 
 Prints ONE JSON line.  ``value`` is KV-read GB/s over the whole step:
 algorithmic K+V bytes (sum of context lengths x KV heads x head dim x 2 x
@@ -85,6 +87,9 @@ def parse():
     ap.add_argument("--graph", action="store_true",
                     help="decode workloads: also capture one step into a HIP graph and time its "
                          "replays (reported as graph_ms_per_step)")
+    ap.add_argument("--append", choices=("separate", "fused"), default="separate",
+                    help="decode workloads: write the step's new tokens with the cache-write "
+                         "kernel before decoding (separate) or inside the decode call (fused)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="instead of the benchmark, run a plain device copy of BYTES bytes "
                          "--steps times (reference for hardware byte counters)")
@@ -197,12 +202,22 @@ def main():
     # blocks shared across sequences (prompts, beams): cached rather than streaming loads
     shared = bool(w.info.get("shared_kv", False))
 
+    # The step's new tokens are each sequence's last position: with --append
+    # fused the decode call writes them itself (pa_decode_append).
+    fused = args.append == "fused" and step_slots is not None
+    if fused:
+        last = np.array([int(w.block_tables[s][(c - 1) // 16]) * 16 + (c - 1) % 16
+                         for s, c in enumerate(w.context_lens)], np.int32)
+        assert np.array_equal(last, w.step_slots), "step tokens are not the last positions"
+    new_kv = dict(k_new=step_k, v_new=step_v) if fused else {}
+    write_first = step_slots is not None and not fused
+
     def step():
         ops.copy_blocks(pool, step_pairs)
-        if step_slots is not None:
+        if write_first:
             ops.reshape_and_cache(pool, step_k, step_v, step_slots)
         ops.decode(pool, q, tables, ctx, w.scale, out=out, partition_tokens=ptok,
-                   workspace=ws, shared_kv=shared)
+                   workspace=ws, shared_kv=shared, **new_kv)
 
     for _ in range(args.warmup):
         step()
@@ -221,11 +236,11 @@ def main():
     step_begin.record(stream)
     for i in range(args.steps):
         ops.copy_blocks(pool, step_pairs)
-        if step_slots is not None:
+        if write_first:
             ops.reshape_and_cache(pool, step_k, step_v, step_slots)
         ops.set_profile_events(evs[2 * i], evs[2 * i + 1])
         ops.decode(pool, q, tables, ctx, w.scale, out=out, partition_tokens=ptok, workspace=ws,
-                   shared_kv=shared)
+                   shared_kv=shared, **new_kv)
     step_end.record(stream)
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - wall0
@@ -285,6 +300,8 @@ def main():
                    "total_context_tokens": int(w.context_lens.sum()),
                    "partition_tokens": ptok_used, "kv_bytes": kv_bytes,
                    "kv_loads": "cached (shared blocks)" if shared else "non-temporal",
+                   "cache_write": ("none" if step_slots is None else
+                                   "in the decode call" if fused else "separate kernel"),
                    "parallelism": "single GPU"},
         "pct_hbm_peak_step": round(100.0 * value / HBM_PEAK_GBPS, 2),
         "decode_seqs_per_s": round(w.S / (ms_per_step * 1e-3), 1),

@@ -150,6 +150,32 @@ int pa_decode_ex(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t 
                  void *workspace, size_t workspace_bytes, uint32_t flags, void *stream);
 
 /*
+ * pa_decode_append -- one decode step: write every sequence's newest token,
+ * then attend as pa_decode_ex.  The newest token of sequence s sits at
+ * position context_lens[s] - 1 (its context includes it, as the step
+ * appends the token's K and V before attending: French page, second
+ * article, "what is the KV cache"); its slot follows from the block table
+ * (slot = block_tables[s][p / 16] * 16 + p % 16).  The result, pool bytes
+ * included, equals pa_reshape_and_cache of these tokens followed by
+ * pa_decode_ex.  The write is done by the attention kernel itself (one
+ * launch, no gap between a write kernel and the decode kernel) when one
+ * workgroup alone reads each sequence's last block per KV head -- the
+ * matrix-core kernel, or one query head per KV head -- and by a small
+ * kernel of its own just before otherwise.
+ *   k_new, v_new   [num_seqs][num_kv_heads][head_dim] of kv_dtype: the pool's
+ *                  dtype for 16/32-bit pools, PA_BF16 or PA_F32 for an FP8 pool
+ *                  (encoded as pa_reshape_and_cache does).  Sequences with
+ *                  context length 0, or whose last table entry is outside the
+ *                  pool, write nothing.
+ * Other arguments, flags and errors as pa_decode_ex.
+ */
+int pa_decode_append(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t num_seqs,
+                     int32_t num_q_heads, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                     const int32_t *context_lens, float scale, float *out, int32_t partition_tokens,
+                     void *workspace, size_t workspace_bytes, uint32_t flags, const void *k_new,
+                     const void *v_new, int32_t kv_dtype, void *stream);
+
+/*
  * pa_prefill -- causal (chunked) prefill attention over the paged pool.
  * Each sequence's chunk of new tokens is the last
  * n_s = query_start[s+1] - query_start[s] tokens of its context; their K/V

@@ -240,10 +240,16 @@ int pa_decode(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t num
                         PA_DECODE_STREAM_KV, stream);
 }
 
-int pa_decode_ex(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t num_seqs,
-                 int32_t num_q_heads, const int32_t *block_tables, int32_t max_blocks_per_seq,
-                 const int32_t *context_lens, float scale, float *out, int32_t partition_tokens,
-                 void *workspace, size_t workspace_bytes, uint32_t flags, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// pa_decode_ex, and pa_decode_append when k_new is not NULL
+int decode_impl(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t num_seqs,
+                int32_t num_q_heads, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                const int32_t *context_lens, float scale, float *out, int32_t partition_tokens,
+                void *workspace, size_t workspace_bytes, uint32_t flags, const void *k_new,
+                const void *v_new, int32_t kv_dtype, void *stream) {
     if (flags & ~(uint32_t)PA_DECODE_SHARED_KV)
         return fail(PA_ERR_SHAPE, "unknown decode flags 0x%x", flags);
     int rc = check_pool(pool);
@@ -268,6 +274,14 @@ int pa_decode_ex(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t 
         return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                     workspace ? workspace_bytes : (size_t)0);
     if (need > 0 && !aligned16(workspace)) return fail(PA_ERR_ALIGN, "workspace must be 16-byte aligned");
+    if (k_new || v_new) {
+        if (!k_new || !v_new) return fail(PA_ERR_NULL, "k_new and v_new must both be given");
+        const bool dtype_ok = pool->kv_dtype == PA_FP8_E4M3 ? (kv_dtype == PA_BF16 || kv_dtype == PA_F32)
+                                                            : kv_dtype == pool->kv_dtype;
+        if (!dtype_ok)
+            return fail(PA_ERR_DTYPE, "new-token dtype %d cannot be written to a kv_dtype %d pool", kv_dtype,
+                        pool->kv_dtype);
+    }
 
     pa::DecodeParams p{};
     p.k_pool = pool->k_pool;
@@ -288,6 +302,11 @@ int pa_decode_ex(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t 
     p.qk_scale_log2 = (float)((double)scale * kscale * 1.4426950408889634);
     p.out_scale = pool->kv_dtype == PA_FP8_E4M3 ? pool->v_scale : 1.0f;
     p.shared_kv = (flags & PA_DECODE_SHARED_KV) ? 1 : 0;
+    p.k_new = k_new;
+    p.v_new = v_new;
+    p.new_dtype = kv_dtype;
+    p.inv_k_scale = pool->kv_dtype == PA_FP8_E4M3 ? 1.0f / pool->k_scale : 1.0f;
+    p.inv_v_scale = pool->kv_dtype == PA_FP8_E4M3 ? 1.0f / pool->v_scale : 1.0f;
     if (need > 0) {
         const int64_t rows = (int64_t)num_seqs * num_q_heads * np;
         char *ws = static_cast<char *>(workspace);
@@ -306,6 +325,13 @@ int pa_decode_ex(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t 
         if (rc != PA_OK) return rc;
     }
     const bool mfma = pa::mfma_path_supported(pool->kv_dtype, pool->head_dim, p.group);
+    if (k_new && !mfma && p.group > 1) {
+        // several workgroups read each KV head's last block: the new tokens
+        // are written by a kernel of their own first
+        hipError_t e = pa::launch_append_tokens(pool->kv_dtype, pool->head_dim, p, st);
+        if (e != hipSuccess) return fail(PA_ERR_HIP, "append kernel: %s", hipGetErrorString(e));
+        p.k_new = p.v_new = nullptr;
+    }
     if (g_ev_before) {
         hipError_t e = hipEventRecord(g_ev_before, st);
         if (e != hipSuccess) return fail(PA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
@@ -323,6 +349,30 @@ int pa_decode_ex(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t 
         if (e != hipSuccess) return fail(PA_ERR_HIP, "decode reduce kernel: %s", hipGetErrorString(e));
     }
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_decode_ex(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t num_seqs,
+                 int32_t num_q_heads, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                 const int32_t *context_lens, float scale, float *out, int32_t partition_tokens,
+                 void *workspace, size_t workspace_bytes, uint32_t flags, void *stream) {
+    return decode_impl(pool, q, q_dtype, num_seqs, num_q_heads, block_tables, max_blocks_per_seq,
+                       context_lens, scale, out, partition_tokens, workspace, workspace_bytes, flags,
+                       nullptr, nullptr, 0, stream);
+}
+
+int pa_decode_append(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t num_seqs,
+                     int32_t num_q_heads, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                     const int32_t *context_lens, float scale, float *out, int32_t partition_tokens,
+                     void *workspace, size_t workspace_bytes, uint32_t flags, const void *k_new,
+                     const void *v_new, int32_t kv_dtype, void *stream) {
+    if (num_seqs > 0 && (!k_new || !v_new)) return fail(PA_ERR_NULL, "k_new and v_new must be non-NULL");
+    return decode_impl(pool, q, q_dtype, num_seqs, num_q_heads, block_tables, max_blocks_per_seq,
+                       context_lens, scale, out, partition_tokens, workspace, workspace_bytes, flags,
+                       k_new, v_new, kv_dtype, stream);
 }
 
 int pa_prefill(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t num_seqs,

@@ -11,74 +11,19 @@
 // move to CPU memory instead of whole sequences (French page, "how
 // PagedAttention solves this problem").
 #include "pa_internal.h"
+#include "pa_store.h"
 
 namespace pa {
 namespace {
 
-// fp32 -> OCP E4M3FN with round-to-nearest-even and saturation to +-448,
-// done on the bit pattern: NaN keeps its sign as S.1111.111; magnitudes at or
-// above 448 (infinity included) become 448; normal results keep the top three
-// mantissa bits and round on the remaining twenty; results below 2^-6 are
-// multiples of 2^-9 rounded from the full 24-bit significand.
-__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
-    const uint32_t u = __float_as_uint(x);
-    const uint32_t sign = (u >> 24) & 0x80u;
-    const uint32_t a = u & 0x7fffffffu;
-    if (a > 0x7f800000u) return sign | 0x7fu;        // NaN
-    if (a >= 0x43e00000u) return sign | 0x7eu;       // |x| >= 448
-    const uint32_t e = a >> 23;                      // biased fp32 exponent
-    if (e >= 121u) {                                 // |x| >= 2^-6: normal E4M3
-        const uint32_t mant = a & 0x7fffffu;
-        uint32_t code = ((e - 120u) << 3) | (mant >> 20);
-        const uint32_t rest = mant & 0xfffffu;
-        if (rest > 0x80000u || (rest == 0x80000u && (code & 1u))) code += 1u;
-        return sign | code;
-    }
-    if (e == 0u) return sign;                        // fp32 subnormal: rounds to 0
-    const uint32_t sig = (a & 0x7fffffu) | 0x800000u; // value = sig * 2^(e - 150)
-    const uint32_t shift = 141u - e;                 // code = value * 2^9 = sig >> shift
-    if (shift >= 32u) return sign;
-    uint32_t code = sig >> shift;
-    const uint32_t rest = sig & ((1u << shift) - 1u);
-    const uint32_t half = 1u << (shift - 1u);
-    if (rest > half || (rest == half && (code & 1u))) code += 1u;
-    return sign | code;
-}
-
-template <int IN>
-__device__ __forceinline__ float load_in(const void *base, int64_t idx) {
-    if constexpr (IN == kF32) {
-        return reinterpret_cast<const float *>(base)[idx];
-    } else {
-        const uint32_t h = reinterpret_cast<const uint16_t *>(base)[idx];
-        return __uint_as_float(h << 16);
-    }
-}
-
-// One element (token t, head g, dim d) of K and of V to its place in the tiles.
+// One element (token tok, head g, dim d) of K and of V to its slot.
 template <int POOL, int IN, int D>
 __device__ __forceinline__ void write_element(const CacheParams &p, int64_t tok, int g, int d, int32_t slot) {
-    constexpr int EB = POOL == kF32 ? 4 : (POOL == kBF16 ? 2 : 1);
-    constexpr int X = 16 / EB;   // K: elements per 16-byte run
-    constexpr int W = 4 / EB;    // V: head-dim elements per 16-byte cell
     if (slot < 0) return;
     const int64_t b = slot >> 4;
-    const int t = slot & 15;
     if (b >= p.num_blocks) return;
-    const int64_t idx = (tok * p.num_kv_heads + g) * D + d;
-    const int64_t tile = (b * p.num_kv_heads + g) * (int64_t)(kBlock * D);
-    const int64_t ko = tile + ((d / X) * kBlock + t) * X + (d % X);
-    const int64_t vo = tile + ((t >> 2) * (D / W) + d / W) * (4 * W) + (d % W) * 4 + (t & 3);
-    if constexpr (POOL == kFP8) {
-        reinterpret_cast<uint8_t *>(p.k_pool)[ko] = (uint8_t)f32_to_e4m3(load_in<IN>(p.k, idx) * p.inv_k_scale);
-        reinterpret_cast<uint8_t *>(p.v_pool)[vo] = (uint8_t)f32_to_e4m3(load_in<IN>(p.v, idx) * p.inv_v_scale);
-    } else if constexpr (POOL == kBF16) {
-        reinterpret_cast<uint16_t *>(p.k_pool)[ko] = reinterpret_cast<const uint16_t *>(p.k)[idx];
-        reinterpret_cast<uint16_t *>(p.v_pool)[vo] = reinterpret_cast<const uint16_t *>(p.v)[idx];
-    } else {
-        reinterpret_cast<uint32_t *>(p.k_pool)[ko] = reinterpret_cast<const uint32_t *>(p.k)[idx];
-        reinterpret_cast<uint32_t *>(p.v_pool)[vo] = reinterpret_cast<const uint32_t *>(p.v)[idx];
-    }
+    store_kv_element<POOL, IN, D>(p.k_pool, p.v_pool, p.k, p.v, (tok * p.num_kv_heads + g) * D + d, b,
+                                  p.num_kv_heads, g, slot & 15, d, p.inv_k_scale, p.inv_v_scale);
 }
 
 // Four consecutive input elements starting at element `idx` as fp8 codes
@@ -273,6 +218,19 @@ __global__ __launch_bounds__(kThreads) void swap_blocks_kernel(char *k_pool, cha
     }
 }
 
+// Workgroup (sequence, KV head): each sequence's newest token to the slot of
+// position context_len - 1, through its block table (a decode step whose
+// attention kernel cannot write it itself).
+template <int POOL, int D>
+__global__ __launch_bounds__(kThreads) void append_tokens_kernel(DecodeParams p) {
+    const int s = blockIdx.x, g = blockIdx.y;
+    int ctx = p.context_lens[s];
+    ctx = ctx < 0 ? 0 : (ctx > p.max_blocks_per_seq * kBlock ? p.max_blocks_per_seq * kBlock : ctx);
+    if (ctx == 0) return;
+    const int32_t *table = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
+    for (int d = threadIdx.x; d < D; d += kThreads) append_element<POOL, D>(p, table, s, g, ctx - 1, d);
+}
+
 template <int POOL, int IN, int D>
 hipError_t launch_rc(const CacheParams &p, hipStream_t stream) {
     const int64_t groups = (p.num_tokens + kBlock - 1) / kBlock;
@@ -295,6 +253,22 @@ hipError_t launch_reshape_and_cache(int pool_kv, int in_kv, int head_dim, const 
     if (pool_kv == kBF16) return launch_rc_d<kBF16, kBF16>(head_dim, p, stream);
     if (in_kv == kBF16) return launch_rc_d<kFP8, kBF16>(head_dim, p, stream);
     return launch_rc_d<kFP8, kF32>(head_dim, p, stream);
+}
+
+hipError_t launch_append_tokens(int kv, int head_dim, const DecodeParams &p, hipStream_t stream) {
+    if (p.num_seqs <= 0) return hipSuccess;
+    if (p.num_kv_heads > 65535) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)p.num_seqs, (unsigned)p.num_kv_heads);
+    if (kv == kF32)
+        head_dim == 64 ? append_tokens_kernel<kF32, 64><<<grid, dim3(kThreads), 0, stream>>>(p)
+                       : append_tokens_kernel<kF32, 128><<<grid, dim3(kThreads), 0, stream>>>(p);
+    else if (kv == kBF16)
+        head_dim == 64 ? append_tokens_kernel<kBF16, 64><<<grid, dim3(kThreads), 0, stream>>>(p)
+                       : append_tokens_kernel<kBF16, 128><<<grid, dim3(kThreads), 0, stream>>>(p);
+    else
+        head_dim == 64 ? append_tokens_kernel<kFP8, 64><<<grid, dim3(kThreads), 0, stream>>>(p)
+                       : append_tokens_kernel<kFP8, 128><<<grid, dim3(kThreads), 0, stream>>>(p);
+    return hipGetLastError();
 }
 
 hipError_t launch_copy_blocks(void *k_pool, void *v_pool, const int32_t *pairs, int32_t num_pairs,

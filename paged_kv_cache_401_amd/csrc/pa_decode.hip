@@ -28,6 +28,7 @@
 // selection: the values they read are never multiplied in.
 #include "pa_internal.h"
 #include "pa_mfma_util.h"
+#include "pa_store.h"
 
 #include <type_traits>
 
@@ -96,6 +97,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KV == 
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);   // the same, as a uniform value
     const int t = lane & 15;
     const int c = lane >> 4;
 
@@ -115,6 +117,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KV == 
     const int tok1 = min(ctx, tok0 + p.partition_tokens);
     const int blk0 = tok0 / kBlock;
     const int blk1 = (tok1 + kBlock - 1) / kBlock;
+    const int32_t *table = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
+
+    // A decode step's newest token (one query head per KV head here, so this
+    // workgroup alone reads KV head g's last block) is written by the
+    // wavefront that reads the last block of the partition holding position
+    // ctx - 1 (wavefronts take every fourth block).  It loads the token's
+    // inputs first, issues its block loads, and stores the token when the
+    // inputs arrive: its own later loads of the block see the stores (a
+    // wavefront's memory accesses stay in order), and nothing waits for them.
+    const bool writer = p.k_new != nullptr && tok1 == ctx && ctx > 0 && wv == (blk1 - 1 - blk0) % 4;
 
     // q elements matching this lane's K runs: fp32 values for an fp32 pool,
     // else the raw bf16 pairs (dims 2i, 2i+1 of run c + 4j in word i), which
@@ -151,7 +163,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KV == 
 #pragma unroll
         for (int w = 0; w < W; ++w) acc[jj][w] = 0.f;
 
-    const int32_t *table = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
     const char *kbase = static_cast<const char *>(p.k_pool);
     const char *vbase = static_cast<const char *>(p.v_pool);
 
@@ -291,7 +302,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KV == 
     // buffer half by half (K once its dot products are formed, V once it is
     // consumed), and every step issues the same loads (empty resources past
     // the end), so each wait covers exactly the loads it needs.
-    const int wv = __builtin_amdgcn_readfirstlane(wave);
     const int nk = blk1 - blk0 > wv ? (blk1 - blk0 - wv + 3) / 4 : 0;
     if (nk > 0) {
         const int32_t *wtable = table + blk0 + wv;
@@ -299,6 +309,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KV == 
             const int32_t b = wtable[4 * min(k, nk - 1)];
             return k < nk ? b : -1;
         };
+        // with two blocks or fewer the last one is loaded in the prologue: the
+        // token is stored before it then
+        const bool early = writer && nk <= 2;
+        NewToken<D> nt;
+        if (writer) nt = append_load<KV, D>(p, table, s, g, ctx - 1, lane);
+        if (early) append_store<KV, D>(p, nt, g, ctx - 1, lane);
         uint4 kb[2][NKL], vb[2][NVL];
         int32_t idb[2];
 #pragma unroll
@@ -307,6 +323,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KV == 
             load_k(idb[d], kb[d], kFenced);
             load_v(idb[d], vb[d], kFenced);
         }
+        if (writer && !early) append_store<KV, D>(p, nt, g, ctx - 1, lane);
         int32_t id_pre = id_at(2);
         auto step = [&](int d, int kk) {
             const int32_t id_after = id_pre;  // block kk + 2

@@ -36,6 +36,7 @@
 //     to -inf and their V operand elements to zero before the product.
 #include "pa_internal.h"
 #include "pa_mfma_util.h"
+#include "pa_store.h"
 
 #include <type_traits>
 
@@ -58,6 +59,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);   // the same, as a uniform value
     const int n = lane & 15;
     const int c = lane >> 4;
 
@@ -77,6 +79,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
     const int tok1 = min(ctx, tok0 + p.partition_tokens);
     const int blk0 = tok0 / kBlock;
     const int blk1 = (tok1 + kBlock - 1) / kBlock;
+    const int32_t *table = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
+
+    // A decode step's newest token is written by the wavefront that reads
+    // the last block of the partition holding position ctx - 1 (the only
+    // reader of that block for this KV head; wavefronts take every NW-th
+    // block).  It loads the token's inputs first, issues its block loads, and
+    // stores the token when the inputs arrive: its own later loads of the
+    // block see the stores (a wavefront's memory accesses stay in order), and
+    // nothing waits for them.
+    const bool writer = p.k_new != nullptr && tok1 == ctx && ctx > 0 && wv == (blk1 - 1 - blk0) % NW;
 
     // Q^T operands: head g*G + n (zero for n >= G), head dims per the K mapping
     bf16x8 qop[NQK];
@@ -102,7 +114,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    const int32_t *table = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
     const char *kbase = static_cast<const char *>(p.k_pool);
     const char *vbase = static_cast<const char *>(p.v_pool);
     const int koff = (c * kBlock + n) * 16;        // run c, token n
@@ -221,7 +232,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
     // keeps close to two blocks in flight in the registers of one.  Every step
     // issues the same loads (empty resources past the end), which lets each
     // wait cover exactly the loads it needs.
-    const int wv = __builtin_amdgcn_readfirstlane(wave);
     const int nk = blk1 - blk0 > wv ? (blk1 - blk0 - wv + NW - 1) / NW : 0;
     if (nk > 0) {
         const int32_t *wtable = table + blk0 + wv;
@@ -229,6 +239,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
             const int32_t b = wtable[NW * min(k, nk - 1)];
             return k < nk ? b : -1;
         };
+        // with two blocks or fewer the last one is loaded in the prologue: the
+        // token is stored before it then
+        const bool early = writer && nk <= 2;
+        NewToken<D> nt;
+        if (writer) nt = append_load<KV, D>(p, table, s, g, ctx - 1, lane);
+        if (early) append_store<KV, D>(p, nt, g, ctx - 1, lane);
         u32x4 kb[2][NKL], vb[2][NVL];
         int32_t idb[2];
 #pragma unroll
@@ -237,6 +253,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
             load_k(idb[d], kb[d], kFenced);
             load_v(idb[d], vb[d], kFenced);
         }
+        if (writer && !early) append_store<KV, D>(p, nt, g, ctx - 1, lane);
         int32_t id_pre = id_at(2);
         auto step = [&](int d, int kk) {
             const int32_t id_after = id_pre;  // block kk + 2

@@ -34,6 +34,13 @@ struct DecodeParams {
     float qk_scale_log2;       // scale * k_scale * log2(e)
     float out_scale;           // v_scale (1 for 16/32-bit pools)
     int32_t shared_kv;         // blocks shared across sequences: cached, not streaming, loads
+    // newest token of every sequence, written by the decode kernel itself to
+    // the slot of position context_len - 1 (k_new == nullptr: none)
+    const void *k_new;         // [S][Hkv][D] of new_dtype
+    const void *v_new;
+    int32_t new_dtype;         // kBF16 or kF32 (the pool's dtype unless fp8)
+    float inv_k_scale;         // fp32(1 / k_scale), fp8 pools only
+    float inv_v_scale;
 };
 
 struct PrefillParams {
@@ -74,6 +81,9 @@ hipError_t launch_decode_valu(int kv, int head_dim, const DecodeParams &p, hipSt
 hipError_t launch_decode_mfma(int kv, int head_dim, const DecodeParams &p, hipStream_t stream);
 bool mfma_path_supported(int kv, int head_dim, int group);
 hipError_t launch_decode_reduce(int head_dim, const DecodeParams &p, hipStream_t stream);
+// each sequence's newest token (p.k_new / p.v_new) to the slot of position
+// context_len - 1, as a kernel of its own
+hipError_t launch_append_tokens(int kv, int head_dim, const DecodeParams &p, hipStream_t stream);
 bool prefill_supported(int kv, int head_dim, int group);
 int prefill_tile_tokens(int head_dim, int group);  // chunk tokens per prefill workgroup
 hipError_t launch_prefill(int kv, int head_dim, const PrefillParams &p, hipStream_t stream);

@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 
 # every symbol include/pa.h declares
 EXPORTS = ("pa_pool_bytes", "pa_decode_partition_tokens", "pa_decode_workspace_size", "pa_decode",
-           "pa_decode_ex",
+           "pa_decode_ex", "pa_decode_append",
            "pa_prefill", "pa_reshape_and_cache", "pa_swap_blocks", "pa_copy_blocks",
            "pa_check_workspace_size", "pa_check_tables", "pa_check_query_start", "pa_check_slots",
            "pa_check_copy_pairs", "pa_check_swap_pairs", "pa_set_debug",
@@ -74,6 +74,9 @@ def lib() -> ctypes.CDLL:
     L.pa_decode.restype = ctypes.c_int
     L.pa_decode_ex.argtypes = [PD, P, I32, I32, I32, P, I32, P, F, P, I32, P, SZ, ctypes.c_uint32, P]
     L.pa_decode_ex.restype = ctypes.c_int
+    L.pa_decode_append.argtypes = [PD, P, I32, I32, I32, P, I32, P, F, P, I32, P, SZ, ctypes.c_uint32,
+                                   P, P, I32, P]
+    L.pa_decode_append.restype = ctypes.c_int
     L.pa_prefill.argtypes = [PD, P, I32, I32, I32, P, I32, P, I32, P, F, P, P]
     L.pa_prefill.restype = ctypes.c_int
     L.pa_reshape_and_cache.argtypes = [PD, P, P, I32, P, I32, P]
@@ -231,9 +234,13 @@ DECODE_STREAM_KV, DECODE_SHARED_KV = 0, 1
 def decode(pool: KVPool, q: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
            scale: float, out: torch.Tensor | None = None, partition_tokens: int = 0,
            workspace: torch.Tensor | None = None, stream=None,
-           shared_kv: bool = False) -> torch.Tensor:
+           shared_kv: bool = False, k_new: torch.Tensor | None = None,
+           v_new: torch.Tensor | None = None) -> torch.Tensor:
     """Paged decode attention; ``shared_kv`` marks batches whose sequences
-    share blocks (cached rather than streaming K/V loads; same result)."""
+    share blocks (cached rather than streaming K/V loads; same result).
+    With ``k_new``/``v_new`` ([num_seqs][num_kv_heads][head_dim]) each
+    sequence's newest token, at position context_len - 1, is written to the
+    pool first, in the same step (pa_decode_append)."""
     S, Hq, D = q.shape
     if D != pool.head_dim:
         raise ValueError("q head dim %d differs from the pool's %d" % (D, pool.head_dim))
@@ -250,12 +257,21 @@ def decode(pool: KVPool, q: torch.Tensor, block_tables: torch.Tensor, context_le
     wptr = workspace.data_ptr() if workspace is not None else None
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     d = pool.desc()
-    _check(lib().pa_decode_ex(ctypes.byref(d), _dev(q, "q"), TORCH_TO_PA[q.dtype], S, Hq,
-                              _dev(block_tables, "block_tables", torch.int32), mbs,
-                              _dev(context_lens, "context_lens", torch.int32), float(scale),
-                              _dev(out, "out", torch.float32), int(partition_tokens), wptr,
-                              wbytes, DECODE_SHARED_KV if shared_kv else DECODE_STREAM_KV,
-                              _stream(stream)))
+    flags = DECODE_SHARED_KV if shared_kv else DECODE_STREAM_KV
+    common = (ctypes.byref(d), _dev(q, "q"), TORCH_TO_PA[q.dtype], S, Hq,
+              _dev(block_tables, "block_tables", torch.int32), mbs,
+              _dev(context_lens, "context_lens", torch.int32), float(scale),
+              _dev(out, "out", torch.float32), int(partition_tokens), wptr, wbytes, flags)
+    if k_new is None and v_new is None:
+        _check(lib().pa_decode_ex(*common, _stream(stream)))
+        return out
+    shape = (S, pool.num_kv_heads, pool.head_dim)
+    if k_new is None or v_new is None or k_new.shape != shape or v_new.shape != shape:
+        raise ValueError("k_new and v_new must both be [num_seqs][num_kv_heads][head_dim]")
+    if k_new.dtype != v_new.dtype or k_new.dtype not in TORCH_TO_PA:
+        raise TypeError("k_new/v_new must both be float32 or bfloat16")
+    _check(lib().pa_decode_append(*common, _dev(k_new, "k_new"), _dev(v_new, "v_new"),
+                                  TORCH_TO_PA[k_new.dtype], _stream(stream)))
     return out
 
 

@@ -221,3 +221,17 @@ def test_debug_switch_and_status_text():
     finally:
         L.pa_set_debug(was)
     assert "index" in L.pa_strerror(ops.ERR_INDEX).decode()
+
+
+def test_decode_append_argument_rules():
+    L = ops.lib()
+    d = desc()
+    args = lambda k=16, v=16, dt=ops.BF16, S=1: (ctypes.byref(d), 16, ops.BF16, S, 8, 16, 4, 16, 0.1, 16, 0,
+                                                 None, 0, 0, k, v, dt, None)
+    assert L.pa_decode_append(*args(k=None)) == -1            # missing new tokens
+    assert L.pa_decode_append(*args(v=None)) == -1
+    assert L.pa_decode_append(*args(dt=ops.F32)) == -2        # fp32 tokens into a bf16 pool
+    assert L.pa_decode_append(*args(k=None, v=None, S=0)) == 0  # nothing to do
+    fp8 = desc(kv_dtype=ops.FP8)
+    assert L.pa_decode_append(ctypes.byref(fp8), 16, ops.BF16, 1, 8, 16, 4, 16, 0.1, 16, 0, None, 0, 0,
+                              16, 16, ops.FP8, None) == -2      # fp8 tokens are not an input type
