@@ -16,14 +16,65 @@
 namespace pa {
 namespace {
 
-// One element (token tok, head g, dim d) of K and of V to its slot.
+// One 16-byte K run of one token -- head dims r X .. r X + X - 1, X = 16 /
+// pool element bytes -- and the same dims of V, to the token's slot.  Both
+// inputs are read with vector loads before anything is stored, so a thread
+// makes one round trip to memory; the K run goes out as one 16-byte store,
+// the V elements (spread over the cells of the token's 4-token group) one by
+// one.  Stores are non-temporal, as for single elements.
 template <int POOL, int IN, int D>
-__device__ __forceinline__ void write_element(const CacheParams &p, int64_t tok, int g, int d, int32_t slot) {
+__device__ __forceinline__ void write_run(const CacheParams &p, int64_t tok, int g, int r, int32_t slot) {
+    typedef uint32_t w4 __attribute__((ext_vector_type(4)));
+    constexpr int EB = POOL == kF32 ? 4 : (POOL == kBF16 ? 2 : 1);
+    constexpr int IB = IN == kF32 ? 4 : 2;
+    constexpr int X = 16 / EB;                      // elements per K run
+    constexpr int W = 4 / EB;                       // V: dims per 16-byte cell
+    constexpr int NU = X * IB / 16;                 // 16-byte input units per run
     if (slot < 0) return;
     const int64_t b = slot >> 4;
     if (b >= p.num_blocks) return;
-    store_kv_element<POOL, IN, D>(p.k_pool, p.v_pool, p.k, p.v, (tok * p.num_kv_heads + g) * D + d, b,
-                                  p.num_kv_heads, g, slot & 15, d, p.inv_k_scale, p.inv_v_scale);
+    const int t = slot & 15;
+    const int64_t e = (tok * p.num_kv_heads + g) * D + r * X;   // first input element
+    w4 kin[NU], vin[NU];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+        kin[u] = reinterpret_cast<const w4 *>(static_cast<const char *>(p.k) + e * IB)[u];
+        vin[u] = reinterpret_cast<const w4 *>(static_cast<const char *>(p.v) + e * IB)[u];
+    }
+    // input element j of the run as pool bits
+    auto elem = [&](const w4 (&in)[NU], int j, float inv) -> uint32_t {
+        uint32_t word;
+        if constexpr (IN == kF32) word = in[j / 4][j % 4];
+        else word = (in[j / 8][(j % 8) / 2] >> (16 * (j % 2))) & 0xffffu;
+        if constexpr (POOL == kFP8)
+            return f32_to_e4m3((IN == kF32 ? __uint_as_float(word) : __uint_as_float(word << 16)) * inv);
+        else
+            return word;
+    };
+    const int64_t tile = (b * p.num_kv_heads + g) * (int64_t)(kBlock * D);   // elements
+    w4 kw;
+    if constexpr (POOL == kFP8) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            kw[q] = elem(kin, 4 * q, p.inv_k_scale) | (elem(kin, 4 * q + 1, p.inv_k_scale) << 8) |
+                    (elem(kin, 4 * q + 2, p.inv_k_scale) << 16) | (elem(kin, 4 * q + 3, p.inv_k_scale) << 24);
+    } else {
+        kw = kin[0];
+    }
+    __builtin_nontemporal_store(kw, reinterpret_cast<w4 *>(static_cast<char *>(p.k_pool) +
+                                                           (tile + (int64_t)(r * kBlock + t) * X) * EB));
+#pragma unroll
+    for (int j = 0; j < X; ++j) {
+        const int d = r * X + j;
+        const int64_t vo = tile + ((t >> 2) * (D / W) + d / W) * (4 * W) + (d % W) * 4 + (t & 3);
+        const uint32_t vraw = elem(vin, j, p.inv_v_scale);
+        if constexpr (POOL == kFP8)
+            __builtin_nontemporal_store((uint8_t)vraw, static_cast<uint8_t *>(p.v_pool) + vo);
+        else if constexpr (POOL == kBF16)
+            __builtin_nontemporal_store((uint16_t)vraw, static_cast<uint16_t *>(p.v_pool) + vo);
+        else
+            __builtin_nontemporal_store(vraw, static_cast<uint32_t *>(p.v_pool) + vo);
+    }
 }
 
 // Four consecutive input elements starting at element `idx` as fp8 codes
@@ -50,8 +101,9 @@ __device__ __forceinline__ uint32_t encode4(const void *base, int64_t idx, float
 // K unit (run r, token t) is the 16-byte run r of token t's input row
 // (converted for an fp8 pool), V cell (token group tg, dims W dw ..) is
 // gathered from four tokens' inputs.  Tokens of the window that no run
-// covers go to their slots element by element (a decode step's tokens, each
-// in a different sequence, or the partial last block of a prompt).  Runs are
+// covers go to their slots one K run per thread (write_run: a decode step's
+// tokens, each in a different sequence, or the partial last block of a
+// prompt).  Runs are
 // found by every wavefront alike: lane l looks at token w0 - 16 + l, and
 // ballots mark the tokens whose slot follows the previous one's.
 template <int POOL, int IN, int D>
@@ -79,9 +131,10 @@ __global__ __launch_bounds__(kThreads) void reshape_and_cache_kernel(CacheParams
     const uint32_t mine = (uint32_t)(starts >> 16) & 0xffffu;
 
     const int64_t nt = p.num_tokens - w0 < kBlock ? p.num_tokens - w0 : kBlock;
-    for (int e = threadIdx.x; e < nt * D; e += kThreads) {
-        const int t = e / D, d = e % D;
-        if (!((cov >> t) & 1u)) write_element<POOL, IN, D>(p, w0 + t, g, d, p.slot_mapping[w0 + t]);
+    constexpr int NR = D / X;                        // K runs per token
+    for (int e = threadIdx.x; e < nt * NR; e += kThreads) {
+        const int t = e / NR, r = e % NR;
+        if (!((cov >> t) & 1u)) write_run<POOL, IN, D>(p, w0 + t, g, r, p.slot_mapping[w0 + t]);
     }
     if (!mine) return;
     const int64_t i0 = w0 + __builtin_ctz(mine);    // the run's first token
