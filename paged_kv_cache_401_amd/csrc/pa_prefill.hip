@@ -125,6 +125,9 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
     }
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) minpos = min(minpos, __shfl_xor(minpos, o));
+    // the same in every lane: as a uniform value the per-block mask test is a
+    // scalar branch, not an exec-masked region issued on every block
+    minpos = __builtin_amdgcn_readfirstlane(minpos);
 
     // Q^T operands (zero for rows outside the chunk): head dims 8 (4 u + c) .. +7
     // for step u, matching the staged bf16 K runs
