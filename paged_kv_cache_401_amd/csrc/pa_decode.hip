@@ -101,9 +101,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KV == 
     const int t = lane & 15;
     const int c = lane >> 4;
 
-    int bid = blockIdx.x;
-    const int part = bid % p.max_partitions;
-    bid /= p.max_partitions;
+    // work order as in the matrix-core kernel: partition 0 of every row
+    // first, then each row's later partitions, rotated by row
+    int bid, part;
+    pair_and_partition(p.num_seqs * p.num_q_heads, p.max_partitions, bid, part);
     const int h = bid % p.num_q_heads;
     const int s = sequence_of_rank(p.context_lens, p.num_seqs, p.max_blocks_per_seq * kBlock,
                                    bid / p.num_q_heads);

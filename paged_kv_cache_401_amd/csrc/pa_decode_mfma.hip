@@ -63,9 +63,17 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
     const int n = lane & 15;
     const int c = lane >> 4;
 
-    int bid = blockIdx.x;
-    const int part = bid % p.max_partitions;
-    bid /= p.max_partitions;
+    // Work order: the first num_seqs x num_kv_heads workgroups take partition
+    // 0 of every (sequence, KV head) pair -- all real work, spread evenly over
+    // the eight XCDs (workgroup i runs on XCD i % 8).  The others take
+    // partitions 1.. of one pair each, rotated by the pair index, so the
+    // empty slots of pairs with fewer partitions than the longest stay mixed
+    // with real work rather than piling up at the end.  The plain order
+    // (partition fastest) had slowed long-tail batches up to 3x at some
+    // partition lengths.
+    const int pairs = p.num_seqs * p.num_kv_heads;
+    int bid, part;
+    pair_and_partition(pairs, p.max_partitions, bid, part);
     const int g = bid % p.num_kv_heads;
     const int s = sequence_of_rank(p.context_lens, p.num_seqs, p.max_blocks_per_seq * kBlock,
                                    bid / p.num_kv_heads);

@@ -116,6 +116,23 @@ __device__ __forceinline__ int sequence_of_rank(const int32_t *context_lens, int
     return hit ? (int)__builtin_ctzll(hit) : r;
 }
 
+// The work item of this workgroup in a grid of rows x max_partitions: the
+// first `rows` workgroups take partition 0 of rows 0..rows-1; workgroup
+// rows + j takes row j / (max_partitions - 1), partition
+// 1 + (j % (max_partitions - 1) + row) % (max_partitions - 1).
+__device__ __forceinline__ void pair_and_partition(int rows, int max_partitions, int &row, int &part) {
+    const int i = (int)blockIdx.x;
+    if (i < rows) {
+        row = i;
+        part = 0;
+    } else {
+        const int j = i - rows;
+        const int m = max_partitions - 1;
+        row = j / m;
+        part = 1 + (j % m + row) % m;
+    }
+}
+
 // four fp8 E4M3FN codes (one word) -> four bf16 in two words (exact):
 // lo = codes 0, 1 and hi = codes 2, 3
 __device__ __forceinline__ void e4m3x4_to_bf16(uint32_t w, uint32_t &lo, uint32_t &hi) {
