@@ -30,8 +30,9 @@
 //     4 consecutive tokens x W head dims, so lane (n, c) loads the cell of
 //     tokens 4c..4c+3 and head dims W (16 jj + n) .. +W-1 with one load.
 //   P^T is split into bf16 high and low parts (p = hi + lo to 16 significant
-//     bits); the 32-deep contraction takes [hi | lo] against [V | V], so one
-//     MFMA per 16 x 16 output tile carries P at ~16-bit precision.
+//     bits); each 16 x 16 output tile takes two 16-deep products of the same
+//     V operand (tokens 4c..4c+3), one against hi and one against lo, so P
+//     enters at ~16-bit precision.
 //   Tokens past the context are excluded by selection: their scores are set
 //     to -inf and their V operand elements to zero before the product.
 #include "pa_internal.h"
@@ -204,14 +205,20 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
             for (int t = 0; t < NT; ++t) acc[t] *= alpha;
         }
 
-        // P^T operand: [hi(p0..p3) | lo(p0..p3)]
-        const bf16x8 pop = p_operand_hi_lo(pr);
+        // P^T operands: hi(p0..p3) and lo(p0..p3), tokens 4c..4c+3
+        const u32x4 pw = as_u32x4(p_operand_hi_lo(pr));
+        const bf16x4 phi = as_bf16x4(pw[0], pw[1]);
+        const bf16x4 plo = as_bf16x4(pw[2], pw[3]);
 
-        // zero the V elements of tokens past the context (last block only)
+        // zero the V elements of tokens past the context (last block only;
+        // they may hold anything, NaN included)
         uint32_t keep01 = 0xffffffffu, keep23 = 0xffffffffu;
         if (nvalid < kBlock) v_keep_masks(c, nvalid, keep01, keep23);
 
-        // O^T += V^T . P^T, one MFMA per 16 x 16 tile
+        // O^T += V^T . P^T per 16 x 16 tile, as two 16-deep products (against
+        // hi, then lo) straight from the V registers: no [V | V] operand to
+        // assemble.  (Masking only inside a branch for the last block
+        // duplicated this loop and cost the kernel 20-35 registers.)
 #pragma unroll
         for (int jj = 0; jj < NVL; ++jj) {
 #pragma unroll
@@ -223,11 +230,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
                 } else {
                     e4m3x4_to_bf16(vr[jj][w], v01, v23);
                 }
-                v01 &= keep01;
-                v23 &= keep23;
-                const u32x4 a = {v01, v23, v01, v23};
-                acc[jj * W + w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), pop,
-                                                                          acc[jj * W + w], 0, 0, 0);
+                const bf16x4 a = as_bf16x4(v01 & keep01, v23 & keep23);
+                floatx4 &o = acc[jj * W + w];
+                o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, phi, o, 0, 0, 0);
+                o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, plo, o, 0, 0, 0);
             }
         }
     };

@@ -20,6 +20,13 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr float kNegInfF = -__builtin_inff();
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ u32x4 as_u32x4(bf16x8 v) { return __builtin_bit_cast(u32x4, v); }
+// two words of bf16 pairs as the 4-element operand of a 16-deep matrix-core product
+typedef short bf16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x4 as_bf16x4(uint32_t w0, uint32_t w1) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(bf16x4, u32x2{w0, w1});
+}
 
 // 16-byte load marked non-temporal: decode reads every K/V byte once, and on
 // MI355X streaming reads sustain ~7.1 TB/s this way against ~6.4 TB/s with
@@ -150,8 +157,8 @@ __device__ __forceinline__ void split_bf16(float p, uint32_t &hi, uint32_t &lo) 
     lo = __float_as_uint(p - __uint_as_float(u & 0xffff0000u)) >> 16;
 }
 
-// The P^T operand [hi(p0..p3) | lo(p0..p3)] of a 32-deep contraction that
-// multiplies it against [V | V] (tokens 4c..4c+3 twice)
+// P^T as [hi(p0..p3) | lo(p0..p3)]: the words of the two 16-deep operands
+// (hi, lo) of the P.V product, or of a 32-deep one against [V | V]
 __device__ __forceinline__ bf16x8 p_operand_hi_lo(const float (&pr)[4]) {
     uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
     split_bf16(pr[0], h0, l0);
