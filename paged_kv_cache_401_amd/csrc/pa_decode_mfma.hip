@@ -6,14 +6,15 @@
 // two products of decode attention become small dense contractions:
 //     S^T[16 tokens][16 heads]  = K[16][D] . Q^T[D][16]           (heads >= G are zero)
 //     O^T[D][16 heads]         += V^T[D][16 tokens] . P^T[16][16]
-// Both run on gfx950's v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  An
-// fp8 (E4M3FN) pool is widened to bf16 in registers, which is exact.
+// Both run on gfx950's bf16 matrix cores (v_mfma_f32_16x16x32_bf16 for the
+// scores, v_mfma_f32_16x16x16_bf16 for P.V) with fp32 accumulation.  An fp8
+// (E4M3FN) pool is widened to bf16 in registers, which is exact.
 //
 // Work split: one workgroup per (sequence, KV head, partition of
-// partition_tokens tokens); its four wavefronts (two for short split-K
-// partitions) take every fourth (second) block and keep their own
-// online-softmax state (running max m and sum l per head, base-2 exponent
-// domain), merged through LDS at the end.  Longer contexts
+// partition_tokens tokens); its four wavefronts take every fourth block and
+// keep their own online-softmax state (running max m and sum l per head,
+// base-2 exponent domain), merged through LDS at the end.  Short split-K
+// partitions go to one-wavefront workgroups that walk all of their blocks.  Longer contexts
 // leave per-partition (m, l, O) in the workspace for the reduce kernel.
 //
 // Operand layouts (lane = 16 c + n, n = lane % 16):
@@ -46,7 +47,7 @@ namespace {
 
 constexpr float kNegInf = kNegInfF;
 
-// NW wavefronts per workgroup (4, or 2 for short split-K partitions).
+// NW wavefronts per workgroup (4, or 1 for short split-K partitions).
 template <int KV, int D, bool STREAM, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) void decode_mfma_kernel(DecodeParams p) {
     constexpr int EB = KV == kBF16 ? 2 : 1;
@@ -338,17 +339,18 @@ hipError_t launch(const DecodeParams &p, hipStream_t stream) {
     const int64_t grid = (int64_t)p.num_seqs * p.num_kv_heads * p.max_partitions;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
     // Short split-K partitions (<= 512 tokens: <= 8 blocks per wavefront with
-    // four) go to two-wavefront workgroups, so each wavefront walks twice as
-    // many blocks per start-up and merge.
-    const bool two = p.max_partitions > 1 && p.partition_tokens <= 512;
+    // four) go to one-wavefront workgroups, which walk all of the partition's
+    // blocks and need no merge (fp8 long tail at 512-token partitions: four
+    // wavefronts 0.208 ms, two 0.196, one 0.191).
+    const bool one = p.max_partitions > 1 && p.partition_tokens <= 512;
     if (p.shared_kv) {
-        if (two)
-            decode_mfma_kernel<KV, D, false, 2><<<dim3((unsigned)grid), dim3(128), 0, stream>>>(p);
+        if (one)
+            decode_mfma_kernel<KV, D, false, 1><<<dim3((unsigned)grid), dim3(64), 0, stream>>>(p);
         else
             decode_mfma_kernel<KV, D, false, 4><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(p);
     } else {
-        if (two)
-            decode_mfma_kernel<KV, D, true, 2><<<dim3((unsigned)grid), dim3(128), 0, stream>>>(p);
+        if (one)
+            decode_mfma_kernel<KV, D, true, 1><<<dim3((unsigned)grid), dim3(64), 0, stream>>>(p);
         else
             decode_mfma_kernel<KV, D, true, 4><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(p);
     }
