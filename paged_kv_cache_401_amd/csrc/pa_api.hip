@@ -68,6 +68,34 @@ int64_t tile_bytes(const pa_pool_t *pool) {
 // contexts up to 4096 tokens; longer contexts are cut into 2048-token
 // partitions so that no workgroup walks an unbounded chain of blocks.  Small
 // batches split further (down to 256 tokens) until ~1024 workgroups exist.
+// SIMDs of the current device (four per compute unit), read once per device.
+int32_t simd_count() {
+    static std::atomic<int32_t> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1024;
+    int32_t v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return 1024;
+    v = 4 * cus;
+    cache[dev].store(v, std::memory_order_relaxed);
+    return v;
+}
+
+// Wavefronts per workgroup of the grouped (matrix-core) kernel.  One
+// wavefront walks all of a partition's blocks and needs no merge; four split
+// them and keep four times the loads in flight per (sequence, KV head).  One
+// is faster when partitions are short (<= 512 tokens: fp8 long tail 0.196 ->
+// 0.182 ms against two) and when the batch alone has at least two rows per
+// SIMD, so that one wavefront per row still fills the chip (70B-like batch,
+// 2048 rows: 0.660 -> 0.653 ms; beam search 0.141 -> 0.135 ms); with fewer
+// rows four are faster (parallel sampling, 1536 rows: 0.105 against 0.115).
+bool one_wave(int32_t num_seqs, int32_t num_kv_heads, int32_t max_partitions, int32_t ptok) {
+    if (max_partitions > 1 && ptok <= 512) return true;
+    return (int64_t)num_seqs * num_kv_heads >= 2 * (int64_t)simd_count();
+}
+
 int32_t auto_partition(const pa_pool_t *pool, int32_t num_seqs, int32_t num_q_heads,
                        int32_t max_blocks_per_seq) {
     const bool mfma = pa::mfma_path_supported(pool->kv_dtype, pool->head_dim,
@@ -298,6 +326,7 @@ int decode_impl(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t n
     p.max_blocks_per_seq = max_blocks_per_seq;
     p.partition_tokens = ptok;
     p.max_partitions = np;
+    p.one_wave = one_wave(num_seqs, pool->num_kv_heads, np, ptok) ? 1 : 0;
     const double kscale = pool->kv_dtype == PA_FP8_E4M3 ? (double)pool->k_scale : 1.0;
     p.qk_scale_log2 = (float)((double)scale * kscale * 1.4426950408889634);
     p.out_scale = pool->kv_dtype == PA_FP8_E4M3 ? pool->v_scale : 1.0f;

@@ -338,11 +338,10 @@ template <int KV, int D>
 hipError_t launch(const DecodeParams &p, hipStream_t stream) {
     const int64_t grid = (int64_t)p.num_seqs * p.num_kv_heads * p.max_partitions;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-    // Short split-K partitions (<= 512 tokens: <= 8 blocks per wavefront with
-    // four) go to one-wavefront workgroups, which walk all of the partition's
-    // blocks and need no merge (fp8 long tail at 512-token partitions: four
-    // wavefronts 0.208 ms, two 0.196, one 0.191).
-    const bool one = p.max_partitions > 1 && p.partition_tokens <= 512;
+    // one-wavefront workgroups walk all of a partition's blocks and need no
+    // merge; the caller picks them for short partitions and for batches with
+    // at least two (sequence, KV head) rows per SIMD
+    const bool one = p.one_wave != 0;
     if (p.shared_kv) {
         if (one)
             decode_mfma_kernel<KV, D, false, 1><<<dim3((unsigned)grid), dim3(64), 0, stream>>>(p);

@@ -31,6 +31,7 @@ struct DecodeParams {
     int32_t max_blocks_per_seq;
     int32_t partition_tokens;  // multiple of 16
     int32_t max_partitions;    // ceil(max_blocks_per_seq * 16 / partition_tokens)
+    int32_t one_wave;          // grouped kernel: one-wavefront workgroups instead of four
     float qk_scale_log2;       // scale * k_scale * log2(e)
     float out_scale;           // v_scale (1 for 16/32-bit pools)
     int32_t shared_kv;         // blocks shared across sequences: cached, not streaming, loads
