@@ -90,8 +90,7 @@ __device__ __forceinline__ uint32_t encode4(const void *base, int64_t idx, float
         x[0] = __uint_as_float(v.x << 16), x[1] = __uint_as_float(v.x & 0xffff0000u);
         x[2] = __uint_as_float(v.y << 16), x[3] = __uint_as_float(v.y & 0xffff0000u);
     }
-    return f32_to_e4m3(x[0] * inv) | (f32_to_e4m3(x[1] * inv) << 8) | (f32_to_e4m3(x[2] * inv) << 16) |
-           (f32_to_e4m3(x[3] * inv) << 24);
+    return f32x4_to_e4m3(x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv);
 }
 
 // Workgroup (window of 16 input tokens, KV head).  A run is 16 consecutive

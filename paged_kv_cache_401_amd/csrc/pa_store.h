@@ -15,34 +15,34 @@ namespace pa {
 // (vmcnt 0; the export and LDS/scalar counts left at their maximum)
 constexpr int kWaitVmem = 0x0F70;
 
-// fp32 -> OCP E4M3FN with round-to-nearest-even and saturation to +-448,
-// done on the bit pattern: NaN keeps its sign as S.1111.111; magnitudes at or
-// above 448 (infinity included) become 448; normal results keep the top three
-// mantissa bits and round on the remaining twenty; results below 2^-6 are
-// multiples of 2^-9 rounded from the full 24-bit significand.
+// fp32 -> OCP E4M3FN with round-to-nearest-even and saturation to +-448;
+// NaN keeps its sign as S.1111.111.  The hardware conversion rounds to
+// nearest even; a clamp to +-448 (v_med3_f32) first gives the saturation.
+// Checked on MI355X against a bit-level encoder of the same rule over every
+// fp32 bit pattern: equal for all finite and infinite inputs; NaN, which the
+// clamp would turn into +-448, is set apart.
+__device__ __forceinline__ float sat448(float x) { return __builtin_amdgcn_fmed3f(x, -448.f, 448.f); }
+
+__device__ __forceinline__ uint32_t e4m3_nan(float x) {
+    return ((__float_as_uint(x) >> 24) & 0x80u) | 0x7fu;
+}
+
 __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
-    const uint32_t u = __float_as_uint(x);
-    const uint32_t sign = (u >> 24) & 0x80u;
-    const uint32_t a = u & 0x7fffffffu;
-    if (a > 0x7f800000u) return sign | 0x7fu;        // NaN
-    if (a >= 0x43e00000u) return sign | 0x7eu;       // |x| >= 448
-    const uint32_t e = a >> 23;                      // biased fp32 exponent
-    if (e >= 121u) {                                 // |x| >= 2^-6: normal E4M3
-        const uint32_t mant = a & 0x7fffffu;
-        uint32_t code = ((e - 120u) << 3) | (mant >> 20);
-        const uint32_t rest = mant & 0xfffffu;
-        if (rest > 0x80000u || (rest == 0x80000u && (code & 1u))) code += 1u;
-        return sign | code;
+    const uint32_t code = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(x), 0.f, 0, false) & 0xffu;
+    return x != x ? e4m3_nan(x) : code;
+}
+
+// four values -> four codes, byte i = value i
+__device__ __forceinline__ uint32_t f32x4_to_e4m3(float x0, float x1, float x2, float x3) {
+    uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(x0), sat448(x1), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(x2), sat448(x3), w, true);
+    if ((x0 != x0) | (x1 != x1) | (x2 != x2) | (x3 != x3)) {
+        const float xs[4] = {x0, x1, x2, x3};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (xs[i] != xs[i]) w = (w & ~(0xffu << (8 * i))) | (e4m3_nan(xs[i]) << (8 * i));
     }
-    if (e == 0u) return sign;                        // fp32 subnormal: rounds to 0
-    const uint32_t sig = (a & 0x7fffffu) | 0x800000u; // value = sig * 2^(e - 150)
-    const uint32_t shift = 141u - e;                 // code = value * 2^9 = sig >> shift
-    if (shift >= 32u) return sign;
-    uint32_t code = sig >> shift;
-    const uint32_t rest = sig & ((1u << shift) - 1u);
-    const uint32_t half = 1u << (shift - 1u);
-    if (rest > half || (rest == half && (code & 1u))) code += 1u;
-    return sign | code;
+    return w;
 }
 
 template <int IN>
