@@ -18,9 +18,9 @@ constexpr int kWaitVmem = 0x0F70;
 // fp32 -> OCP E4M3FN with round-to-nearest-even and saturation to +-448;
 // NaN keeps its sign as S.1111.111.  The hardware conversion rounds to
 // nearest even; a clamp to +-448 (v_med3_f32) first gives the saturation.
-// Checked on MI355X against a bit-level encoder of the same rule over every
-// fp32 bit pattern: equal for all finite and infinite inputs; NaN, which the
-// clamp would turn into +-448, is set apart.
+// NaN, which the clamp would turn into +-448, is set apart.  The cache write
+// built on it is checked against a table-search encoder of the same rule on
+// every one of the 2^32 fp32 bit patterns.
 __device__ __forceinline__ float sat448(float x) { return __builtin_amdgcn_fmed3f(x, -448.f, 448.f); }
 
 __device__ __forceinline__ uint32_t e4m3_nan(float x) {
