@@ -230,6 +230,27 @@ def test_decode_group_sizes(group, D, dt, ptok):
     assert err <= tolerance(w), "max abs error %.3e" % err
 
 
+@pytest.mark.parametrize("D,dt", [(64, oracle.BF16), (128, oracle.BF16), (64, oracle.FP8),
+                                  (128, oracle.FP8)])
+@pytest.mark.parametrize("ptok", [0, 64])
+def test_decode_many_rows(D, dt, ptok):
+    """2048 (sequence, KV head) rows -- two per SIMD of an MI355X -- so the
+    grouped kernel runs one wavefront per workgroup (also with short split-K
+    partitions, ptok 64); ragged contexts up to 200 tokens, tail slots
+    poisoned with NaN."""
+    S, Hkv, G = 256, 8, 4
+    rng = np.random.default_rng(3 * D + dt + ptok)
+    ctx = rng.integers(1, 201, S)
+    w = wl._simple("many_rows", S, G * Hkv, Hkv, D, ctx, dt, oracle.BF16, oracle.BF16,
+                   float(np.float32(1 / math.sqrt(D))), 23, "cpu", rng, fp8_scales=dt == oracle.FP8)
+    kp, vp = oracle_pools(w)
+    ref = oracle_decode(w, kp, vp)
+    got = gpu_decode(w, gpu_pool(w, fill=0xFF), partition_tokens=ptok)
+    assert np.isfinite(got).all()
+    err = float(np.max(np.abs(got - ref)))
+    assert err <= tolerance(w), "max abs error %.3e" % err
+
+
 @pytest.mark.parametrize("Hq", [1, 2])
 def test_fp8_decode_all_codes_through_attention(Hq):
     """A one-hot probe on tokens whose V rows hold all 256 E4M3FN codes: the
