@@ -42,8 +42,19 @@ def group_workload(group):
                       oracle.BF16, float(np.float32(1 / math.sqrt(128))), 23, "cpu", rng)
 
 
+def many_rows_workload(D, dt):
+    """2048 (sequence, KV head) rows: the grouped kernel runs one wavefront
+    per workgroup."""
+    rng = np.random.default_rng(60 + D + dt)
+    ctx = rng.integers(1, 201, 256)
+    return wl._simple("many_rows", 256, 32, 8, D, ctx, dt, oracle.BF16, oracle.BF16,
+                      float(np.float32(1 / math.sqrt(D))), 29, "cpu", rng, fp8_scales=dt == oracle.FP8)
+
+
 CASES = {
     "gqa70b": lambda: wl.make_workload("gqa70b", small=True),      # matrix-core, bf16
+    "rows_d64": lambda: many_rows_workload(64, oracle.BF16),        # matrix-core, one wavefront
+    "rows_fp8": lambda: many_rows_workload(128, oracle.FP8),        # the same over an fp8 pool
     "fp8": lambda: wl.make_workload("fp8", small=True),            # matrix-core, fp8 from bf16
     "mha13b": lambda: wl.make_workload("mha13b", small=True),      # vector ALU, one head per KV head
     "tiny": lambda: wl.make_workload("tiny", small=True),          # vector ALU, fp32
@@ -58,7 +69,7 @@ def test_append_equals_write_then_decode(case, ptok):
     w = CASES[case]()
     ctx = w.context_lens.copy()
     tables = w.block_tables.copy()
-    if case in ("gqa70b", "mha13b", "fp8"):
+    if case in ("gqa70b", "mha13b", "fp8", "rows_d64", "rows_fp8"):
         ctx[1] = 0                        # an empty context writes nothing
     if case == "fp8":
         tables[2, (ctx[2] - 1) // 16] = w.num_blocks + 5   # an out-of-pool last block: skipped
