@@ -85,8 +85,20 @@ class BlockManager:
         seq = self.seqs[seq_id]
         if seq.on_host:
             raise RuntimeError("sequence %r is swapped out" % (seq_id,))
+        n = int(n)
+        if n < 0:
+            raise ValueError("cannot append %d tokens" % n)
+        # all or nothing: the blocks this call takes -- one per block boundary
+        # crossed, plus a copy of a shared, partly filled last block -- must
+        # all be free before anything changes
+        bs = self.block_size
+        need = -(-(seq.length + n) // bs) - -(-seq.length // bs)
+        if n > 0 and seq.length % bs != 0 and self.refcount[seq.table[-1]] > 1:
+            need += 1
+        if need > len(self.free):
+            raise NoFreeBlock("%d tokens need %d free blocks, %d left" % (n, need, len(self.free)))
         slots, pairs = [], []
-        for _ in range(int(n)):
+        for _ in range(n):
             pos = seq.length
             if pos % self.block_size == 0:
                 seq.table.append(self._allocate())
