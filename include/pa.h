@@ -88,7 +88,7 @@ typedef enum pa_status {
 typedef struct pa_pool {
     void *k_pool;
     void *v_pool;
-    int32_t num_blocks;
+    int32_t num_blocks;   /* 1 .. 2^27 - 1, so that every slot (block * 16 + position) is an int32 */
     int32_t num_kv_heads;
     int32_t block_size; /* must be 16 */
     int32_t head_dim;   /* 64 or 128 */

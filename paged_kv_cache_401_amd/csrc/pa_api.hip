@@ -46,6 +46,9 @@ int check_pool(const pa_pool_t *pool) {
     if (pool->num_blocks <= 0 || pool->num_kv_heads <= 0)
         return fail(PA_ERR_SHAPE, "num_blocks %d and num_kv_heads %d must be positive",
                     pool->num_blocks, pool->num_kv_heads);
+    if (pool->num_blocks > INT32_MAX / PA_BLOCK_SIZE)
+        return fail(PA_ERR_SHAPE, "num_blocks %d: slots (block * 16 + position) must fit int32",
+                    pool->num_blocks);
     if (!aligned16(pool->k_pool) || !aligned16(pool->v_pool))
         return fail(PA_ERR_ALIGN, "k_pool and v_pool must be 16-byte aligned");
     if (pool->kv_dtype == PA_FP8_E4M3) {
@@ -352,6 +355,21 @@ int decode_impl(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t n
                                            pool->num_blocks, report, st);
         });
         if (rc != PA_OK) return rc;
+        if (k_new) {
+            // the newest tokens' slots, then the cache write's slot check on them
+            const int64_t slot_bytes = (((int64_t)num_seqs * 4 + 255) / 256) * 256;
+            rc = debug_check("pa_decode_append", slot_bytes + pa::check_workspace_bytes(pool->num_blocks, 0),
+                             st, [&](int32_t *report, void *ws) {
+                                 int32_t *slots = static_cast<int32_t *>(ws);
+                                 hipError_t e = pa::launch_append_slots(block_tables, context_lens, num_seqs,
+                                                                        max_blocks_per_seq, pool->num_blocks,
+                                                                        slots, st);
+                                 if (e != hipSuccess) return e;
+                                 return pa::launch_check_slots(slots, num_seqs, pool->num_blocks,
+                                                               static_cast<char *>(ws) + slot_bytes, report, st);
+                             });
+            if (rc != PA_OK) return rc;
+        }
     }
     const bool mfma = pa::mfma_path_supported(pool->kv_dtype, pool->head_dim, p.group);
     if (k_new && !mfma && p.group > 1) {

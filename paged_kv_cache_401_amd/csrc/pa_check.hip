@@ -172,6 +172,26 @@ hipError_t zero_words(uint32_t *buf, int64_t words, hipStream_t stream) {
 
 }  // namespace
 
+// The slot each sequence's newest token goes to in a decode step that writes
+// it (position ctx - 1 through the table): -1 for an empty context or a
+// table entry outside the pool (the step writes nothing there; the tables
+// check reports the entry).
+__global__ __launch_bounds__(kThreads) void append_slots_kernel(const int32_t *tables,
+                                                                const int32_t *context_lens,
+                                                                int32_t num_seqs, int32_t mbs,
+                                                                int32_t num_blocks, int32_t *slots) {
+    const int64_t s = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (s >= num_seqs) return;
+    int64_t c = context_lens[s];
+    c = c < 0 ? 0 : (c > (int64_t)mbs * kBlock ? (int64_t)mbs * kBlock : c);
+    int32_t slot = -1;
+    if (c > 0) {
+        const int32_t b = tables[s * mbs + (c - 1) / kBlock];
+        if (b >= 0 && b < num_blocks) slot = b * kBlock + (int32_t)((c - 1) % kBlock);
+    }
+    slots[s] = slot;
+}
+
 int64_t check_workspace_bytes(int32_t num_blocks, int32_t num_host_slots) {
     const int64_t slots = 2 * bitmap_words((int64_t)num_blocks * kBlock);
     const int64_t copy = 3 * bitmap_words(num_blocks);
@@ -215,6 +235,15 @@ hipError_t launch_check_slots(const int32_t *slots, int32_t n, int32_t num_block
         repeated_slots_kernel<<<dim3(g), dim3(kThreads), 0, stream>>>(slots, n, num_slots, rep, report);
     }
     report_finish_kernel<<<1, 64, 0, stream>>>(report);
+    return hipGetLastError();
+}
+
+hipError_t launch_append_slots(const int32_t *tables, const int32_t *context_lens, int32_t num_seqs,
+                               int32_t mbs, int32_t num_blocks, int32_t *slots, hipStream_t stream) {
+    if (num_seqs <= 0) return hipSuccess;
+    const unsigned g = (unsigned)(((int64_t)num_seqs + kThreads - 1) / kThreads);
+    append_slots_kernel<<<dim3(g), dim3(kThreads), 0, stream>>>(tables, context_lens, num_seqs, mbs,
+                                                                 num_blocks, slots);
     return hipGetLastError();
 }
 

@@ -105,6 +105,8 @@ hipError_t launch_check_tables(const int32_t *tables, const int32_t *context_len
                                hipStream_t stream);
 hipError_t launch_check_query_start(const int32_t *qs, int32_t num_seqs, int32_t *report,
                                     hipStream_t stream);
+hipError_t launch_append_slots(const int32_t *tables, const int32_t *context_lens, int32_t num_seqs,
+                               int32_t mbs, int32_t num_blocks, int32_t *slots, hipStream_t stream);
 hipError_t launch_check_slots(const int32_t *slots, int32_t n, int32_t num_blocks, void *workspace,
                               int32_t *report, hipStream_t stream);
 hipError_t launch_check_pairs(const int32_t *pairs, int32_t n, int32_t num_blocks,

@@ -46,6 +46,7 @@ def test_pool_bytes_and_rejections():
 
 @pytest.mark.parametrize("field,value,status", [
     ("block_size", 8, -4), ("head_dim", 80, -4), ("kv_dtype", 7, -2), ("num_blocks", 0, -3),
+    ("num_blocks", 1 << 27, -3),
     ("k_pool", 0, -1), ("k_pool", 8, -6), ("k_scale", 0.0, -8)])
 def test_decode_rejects_bad_pool(field, value, status):
     L = ops.lib()

@@ -210,3 +210,38 @@ def test_debug_mode_refuses_broken_prefill_offsets(debug_mode):
     assert e.value.status == ops.ERR_INDEX and "query_start" in str(e.value)
     torch.cuda.synchronize()
     assert bool((out == 7.0).all())
+
+
+def test_debug_mode_checks_the_slots_of_an_append(debug_mode):
+    """pa_decode_append in debug mode: two sequences whose newest positions
+    fall on one slot (a shared last block nobody copied) are refused and
+    nothing changes; with distinct last blocks the call runs and equals the
+    same call outside debug mode."""
+    w = wl.make_workload("gqa70b", small=True)
+    q = w.q.to(DEV)
+    ctx = i32(w.context_lens)
+    gen = torch.Generator().manual_seed(9)
+    k_new = torch.randn((w.S, w.Hkv, w.D), generator=gen).to(torch.bfloat16).to(DEV)
+    v_new = torch.randn((w.S, w.Hkv, w.D), generator=gen).to(torch.bfloat16).to(DEV)
+
+    pool = gpu_pool(w)
+    k_before = pool.k.clone()
+    tables = w.block_tables.copy()
+    last = (int(w.context_lens[0]) - 1) // 16
+    assert w.context_lens[0] == w.context_lens[1]
+    tables[1, last] = tables[0, last]                  # both newest tokens -> one slot
+    out = torch.full((w.S, w.Hq, w.D), 7.0, device=DEV)
+    with pytest.raises(ops.PAError) as e:
+        ops.decode(pool, q, i32(tables), ctx, w.scale, out=out, k_new=k_new, v_new=v_new)
+    assert e.value.status == ops.ERR_INDEX and "slot repeated" in str(e.value)
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all()) and bool((pool.k == k_before).all())
+
+    got = ops.decode(pool, q, i32(w.block_tables), ctx, w.scale, k_new=k_new, v_new=v_new)
+    ops.set_debug(False)
+    ref_pool = gpu_pool(w)
+    ref = ops.decode(ref_pool, q, i32(w.block_tables), ctx, w.scale, k_new=k_new, v_new=v_new)
+    ops.set_debug(True)
+    torch.cuda.synchronize()
+    assert_same_bytes(got.cpu().numpy(), ref.cpu().numpy())
+    assert_same_bytes(pool.k.cpu().numpy(), ref_pool.k.cpu().numpy())
