@@ -118,7 +118,7 @@ def source_digest() -> str:
     is built from."""
     from paged_kv_cache_401_amd import build as pa_build
     h = hashlib.sha256()
-    for f in ("pa_decode_mfma.hip", "pa_mfma_util.h", "pa_internal.h"):
+    for f in ("pa_decode_mfma.hip", "pa_mfma_util.h", "pa_internal.h", "pa_store.h"):
         h.update(open(os.path.join(ROOT, "paged_kv_cache_401_amd", "csrc", f), "rb").read())
     h.update(" ".join(pa_build.common_flags()).replace(ROOT, "").encode())
     return h.hexdigest()[:16]
