@@ -154,7 +154,7 @@ __global__ __launch_bounds__(kThreads) void reshape_and_cache_kernel(CacheParams
         } else {
             w = *reinterpret_cast<const uint4 *>(static_cast<const char *>(p.k) + e * IB);
         }
-        kt[u] = w;
+        store16_nt(kt + u, w);
     }
     for (int u = threadIdx.x; u < K_UNITS; u += kThreads) {
         const int tg = u / (D / W), dw = u % (D / W);
@@ -187,16 +187,16 @@ __global__ __launch_bounds__(kThreads) void reshape_and_cache_kernel(CacheParams
             const uint32_t *src = static_cast<const uint32_t *>(p.v);
             w.x = src[e], w.y = src[e + step], w.z = src[e + 2 * step], w.w = src[e + 3 * step];
         }
-        vt[u] = w;
+        store16_nt(vt + u, w);
     }
 }
 
 // Workgroup (pair, pool, part): 16-byte copies of one part of the whole block
 // (all KV heads), U x 4 KiB per part; each thread issues its U loads before
-// its stores.  Source and destination never overlap (destinations are
-// distinct and none is a source).  Measured on MI355X: whole 32 KiB blocks
-// per workgroup (U = 8) are fastest for a few hundred pairs, 16 KiB parts
-// (U = 4) once thousands of pairs fill the chip.
+// its stores, which are non-temporal.  Source and destination never overlap
+// (destinations are distinct and none is a source).  Measured on MI355X:
+// whole 32 KiB blocks per workgroup (U = 8) are fastest for a few hundred
+// pairs, 16 KiB parts (U = 4) once thousands of pairs fill the chip.
 template <int U>
 __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(char *k_pool, char *v_pool,
                                                                const int32_t *pairs,
@@ -219,7 +219,7 @@ __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(char *k_pool, cha
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int64_t i = i0 + (int64_t)u * kThreads + threadIdx.x;
-        if (i < n) d[i] = v[u];
+        if (i < n) store16_nt(d + i, v[u]);
     }
 }
 

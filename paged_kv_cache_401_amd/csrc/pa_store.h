@@ -55,6 +55,14 @@ __device__ __forceinline__ float load_in(const void *base, int64_t idx) {
     }
 }
 
+// 16-byte store marked non-temporal.  For the pool's bulk writes (block
+// copies, whole-tile cache writes) it let copies of thousands of blocks run
+// at 7.7 TB/s read + write against 5.4 with plain stores.
+__device__ __forceinline__ void store16_nt(void *dst, uint4 v) {
+    typedef uint32_t w4 __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(w4{v.x, v.y, v.z, v.w}, static_cast<w4 *>(dst));
+}
+
 // Element d of one token's K and V, given as the pool's element bits (fp8
 // code, bf16 or fp32 bits), to position t of the tiles of block b, KV head g.
 // A lone token touches one 16-byte run per K run and spreads over the V
