@@ -364,23 +364,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KV == 
     }
     __syncthreads();
 
-    if (threadIdx.x < D) {
-        const int d = threadIdx.x;
+    // merge and write, 4 consecutive head dims per lane as one 16-byte
+    // store (the stores that end a work item cost far more than their bytes
+    // while the chip streams K/V): final outputs non-temporal, split-K
+    // partials cacheable for the reduce kernel that reads them next
+    constexpr int D4 = D / 4;
+    if (threadIdx.x < D4) {
+        const int d0 = 4 * threadIdx.x;
         const float M = fmaxf(fmaxf(sm_m[0], sm_m[1]), fmaxf(sm_m[2], sm_m[3]));
-        float L = 0.f, O = 0.f;
+        float L = 0.f;
+        float O[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
             const float f = sm_m[w] == kNegInf ? 0.f : exp2f(sm_m[w] - M);
             L += sm_l[w] * f;
-            O += sm_acc[w][d] * f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) O[e] += sm_acc[w][d0 + e] * f;
         }
         const int64_t row = (int64_t)s * p.num_q_heads + h;
         if (nparts <= 1) {
-            p.out[row * D + d] = L > 0.f ? (O / L) * p.out_scale : 0.f;
+            float r[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) r[e] = L > 0.f ? (O[e] / L) * p.out_scale : 0.f;
+            store16_nt(p.out + row * D + d0, __builtin_bit_cast(uint4, r));
         } else {
             const int64_t pr = row * p.max_partitions + part;
-            p.ws_acc[pr * D + d] = O;
-            if (d == 0) {
+            *reinterpret_cast<uint4 *>(p.ws_acc + pr * D + d0) = __builtin_bit_cast(uint4, O);
+            if (d0 == 0) {
                 p.ws_m[pr] = M;
                 p.ws_l[pr] = L;
             }

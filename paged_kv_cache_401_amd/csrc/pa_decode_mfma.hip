@@ -47,9 +47,22 @@ namespace {
 
 constexpr float kNegInf = kNegInfF;
 
-// NW wavefronts per workgroup (4, or 1 for short split-K partitions).
-template <int KV, int D, bool STREAM, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) void decode_mfma_kernel(DecodeParams p) {
+// LDS of one workgroup: the wavefronts' softmax states and numerators,
+// merged at the end of a work item
+template <int D, int NW>
+struct DecodeLds {
+    float m[NW][16];
+    float l[NW][16];
+    float acc[NW][D * 17];   // [wave][d][head], padded
+};
+
+// One work item: partition `part` of sequence s, KV head g, with context
+// length ctx (already clamped to the table's capacity), computed by the NW
+// wavefronts of the calling workgroup.  APPEND: the decode step's newest
+// tokens are written by this call (DecodeParams::k_new / v_new).
+template <int KV, int D, bool STREAM, int NW, bool APPEND>
+__device__ __forceinline__ void decode_item(const DecodeParams &p, int s, int g, int part, int ctx,
+                                            DecodeLds<D, NW> &sm) {
     constexpr int EB = KV == kBF16 ? 2 : 1;
     constexpr int TILE_BYTES = kBlock * D * EB;
     constexpr int NQK = D / 32;                   // QK steps (32-deep) per block
@@ -64,25 +77,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
     const int wv = __builtin_amdgcn_readfirstlane(wave);   // the same, as a uniform value
     const int n = lane & 15;
     const int c = lane >> 4;
-
-    // Work order: the first num_seqs x num_kv_heads workgroups take partition
-    // 0 of every (sequence, KV head) pair -- all real work, spread evenly over
-    // the eight XCDs (workgroup i runs on XCD i % 8).  The others take
-    // partitions 1.. of one pair each, rotated by the pair index, so the
-    // empty slots of pairs with fewer partitions than the longest stay mixed
-    // with real work rather than piling up at the end.  The plain order
-    // (partition fastest) had slowed long-tail batches up to 3x at some
-    // partition lengths.
-    const int pairs = p.num_seqs * p.num_kv_heads;
-    int bid, part;
-    pair_and_partition(pairs, p.max_partitions, bid, part);
-    const int g = bid % p.num_kv_heads;
-    const int s = sequence_of_rank(p.context_lens, p.num_seqs, p.max_blocks_per_seq * kBlock,
-                                   bid / p.num_kv_heads);
     const int G = p.group;
 
-    int ctx = p.context_lens[s];
-    ctx = ctx < 0 ? 0 : (ctx > p.max_blocks_per_seq * kBlock ? p.max_blocks_per_seq * kBlock : ctx);
     const int nparts = (ctx + p.partition_tokens - 1) / p.partition_tokens;
     if (part >= (nparts > 1 ? nparts : 1)) return;
     const int tok0 = part * p.partition_tokens;
@@ -98,7 +94,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
     // stores the token when the inputs arrive: its own later loads of the
     // block see the stores (a wavefront's memory accesses stay in order), and
     // nothing waits for them.
-    const bool writer = p.k_new != nullptr && tok1 == ctx && ctx > 0 && wv == (blk1 - 1 - blk0) % NW;
+    const bool writer = APPEND && tok1 == ctx && ctx > 0 && wv == (blk1 - 1 - blk0) % NW;
 
     // Q^T operands: head g*G + n (zero for n >= G), head dims per the K mapping
     bf16x8 qop[NQK];
@@ -290,11 +286,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
     // per-head totals of the lane-partial sums
     l = add_xor32(add_xor16(l));
 
-    __shared__ float sm_m[NW][16], sm_l[NW][16];
-    __shared__ float sm_acc[NW][D * LDS_STRIDE];
     if (c == 0) {
-        sm_m[wave][n] = m;
-        sm_l[wave][n] = l;
+        sm.m[wave][n] = m;
+        sm.l[wave][n] = l;
     }
 #pragma unroll
     for (int jj = 0; jj < NVL; ++jj)
@@ -303,30 +297,43 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int d = W * (16 * jj + 4 * c + i) + w;
-                sm_acc[wave][d * LDS_STRIDE + n] = acc[jj * W + w][i];
+                sm.acc[wave][d * LDS_STRIDE + n] = acc[jj * W + w][i];
             }
     __syncthreads();
 
-    for (int idx = threadIdx.x; idx < G * D; idx += 64 * NW) {
-        const int hh = idx / D;
-        const int d = idx % D;
-        float M = sm_m[0][hh];
+    // merge and write: each lane takes 4 consecutive head dims of one head
+    // and stores them with one 16-byte store.  The stores that end a work
+    // item cost far more than their bytes while the chip streams K/V (timed
+    // on MI355X: the 512-token fp8 long-tail batch ran 20 % faster with them
+    // switched off), so there are 4x fewer of them than with one per dim.
+    // Final outputs go out non-temporal; split-K partials stay cacheable,
+    // since the reduce kernel reads them right after.
+    constexpr int D4 = D / 4;
+    for (int idx = threadIdx.x; idx < G * D4; idx += 64 * NW) {
+        const int hh = idx / D4;
+        const int d0 = 4 * (idx % D4);
+        float M = sm.m[0][hh];
 #pragma unroll
-        for (int w = 1; w < NW; ++w) M = fmaxf(M, sm_m[w][hh]);
-        float L = 0.f, O = 0.f;
+        for (int w = 1; w < NW; ++w) M = fmaxf(M, sm.m[w][hh]);
+        float L = 0.f;
+        float O[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
-            const float f = sm_m[w][hh] == kNegInf ? 0.f : exp2f(sm_m[w][hh] - M);
-            L += sm_l[w][hh] * f;
-            O += sm_acc[w][d * LDS_STRIDE + hh] * f;
+            const float f = sm.m[w][hh] == kNegInf ? 0.f : exp2f(sm.m[w][hh] - M);
+            L += sm.l[w][hh] * f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) O[e] += sm.acc[w][(d0 + e) * LDS_STRIDE + hh] * f;
         }
         const int64_t row = (int64_t)s * p.num_q_heads + (int64_t)g * G + hh;
         if (nparts <= 1) {
-            p.out[row * D + d] = L > 0.f ? (O / L) * p.out_scale : 0.f;
+            float r[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) r[e] = L > 0.f ? (O[e] / L) * p.out_scale : 0.f;
+            store16_nt(p.out + row * D + d0, __builtin_bit_cast(uint4, r));
         } else {
             const int64_t pr = row * p.max_partitions + part;
-            p.ws_acc[pr * D + d] = O;
-            if (d == 0) {
+            *reinterpret_cast<uint4 *>(p.ws_acc + pr * D + d0) = __builtin_bit_cast(uint4, O);
+            if (d0 == 0) {
                 p.ws_m[pr] = M;
                 p.ws_l[pr] = L;
             }
@@ -334,26 +341,55 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
     }
 }
 
+__device__ __forceinline__ int clamp_ctx(const DecodeParams &p, int ctx) {
+    const int cap = p.max_blocks_per_seq * kBlock;
+    return ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
+}
+
+// One workgroup of NW wavefronts per (sequence, KV head, partition) slot of
+// a rows x max_partitions grid.
+template <int KV, int D, bool STREAM, int NW, bool APPEND>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) void decode_mfma_kernel(DecodeParams p) {
+    __shared__ DecodeLds<D, NW> sm;
+    // Work order: the first num_seqs x num_kv_heads workgroups take partition
+    // 0 of every (sequence, KV head) pair -- all real work, spread evenly over
+    // the eight XCDs (workgroup i runs on XCD i % 8).  The others take
+    // partitions 1.. of one pair each, rotated by the pair index, so the
+    // empty slots of pairs with fewer partitions than the longest stay mixed
+    // with real work rather than piling up at the end.  The plain order
+    // (partition fastest) had slowed long-tail batches up to 3x at some
+    // partition lengths.
+    int bid, part;
+    pair_and_partition(p.num_seqs * p.num_kv_heads, p.max_partitions, bid, part);
+    const int g = bid % p.num_kv_heads;
+    const int s = sequence_of_rank(p.context_lens, p.num_seqs, p.max_blocks_per_seq * kBlock,
+                                   bid / p.num_kv_heads);
+    decode_item<KV, D, STREAM, NW, APPEND>(p, s, g, part, clamp_ctx(p, p.context_lens[s]), sm);
+}
+
+template <int KV, int D, bool STREAM, bool APPEND>
+hipError_t launch_variant(const DecodeParams &p, int64_t grid, hipStream_t stream) {
+    // one-wavefront workgroups walk all of a partition's blocks and need no
+    // merge; the caller picks them for short partitions and for batches with
+    // at least two (sequence, KV head) rows per SIMD
+    if (p.one_wave == 0) {
+        decode_mfma_kernel<KV, D, STREAM, 4, APPEND><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(p);
+        return hipGetLastError();
+    }
+    decode_mfma_kernel<KV, D, STREAM, 1, APPEND><<<dim3((unsigned)grid), dim3(64), 0, stream>>>(p);
+    return hipGetLastError();
+}
+
 template <int KV, int D>
 hipError_t launch(const DecodeParams &p, hipStream_t stream) {
     const int64_t grid = (int64_t)p.num_seqs * p.num_kv_heads * p.max_partitions;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-    // one-wavefront workgroups walk all of a partition's blocks and need no
-    // merge; the caller picks them for short partitions and for batches with
-    // at least two (sequence, KV head) rows per SIMD
-    const bool one = p.one_wave != 0;
-    if (p.shared_kv) {
-        if (one)
-            decode_mfma_kernel<KV, D, false, 1><<<dim3((unsigned)grid), dim3(64), 0, stream>>>(p);
-        else
-            decode_mfma_kernel<KV, D, false, 4><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(p);
-    } else {
-        if (one)
-            decode_mfma_kernel<KV, D, true, 1><<<dim3((unsigned)grid), dim3(64), 0, stream>>>(p);
-        else
-            decode_mfma_kernel<KV, D, true, 4><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(p);
-    }
-    return hipGetLastError();
+    const bool append = p.k_new != nullptr;
+    if (p.shared_kv)
+        return append ? launch_variant<KV, D, false, true>(p, grid, stream)
+                      : launch_variant<KV, D, false, false>(p, grid, stream);
+    return append ? launch_variant<KV, D, true, true>(p, grid, stream)
+                  : launch_variant<KV, D, true, false>(p, grid, stream);
 }
 
 }  // namespace
