@@ -54,6 +54,10 @@ struct DecodeLds {
     float m[NW][16];
     float l[NW][16];
     float acc[NW][D * 17];   // [wave][d][head], padded
+    // the newest token's K and V as the pool stores them (head-dim order;
+    // used by the wavefront that writes it)
+    alignas(16) uint8_t tok_k[D * 2];
+    alignas(16) uint8_t tok_v[D * 2];
 };
 
 // One work item: partition `part` of sequence s, KV head g, with context
@@ -87,14 +91,17 @@ __device__ __forceinline__ void decode_item(const DecodeParams &p, int s, int g,
     const int blk1 = (tok1 + kBlock - 1) / kBlock;
     const int32_t *table = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
 
-    // A decode step's newest token is written by the wavefront that reads
-    // the last block of the partition holding position ctx - 1 (the only
-    // reader of that block for this KV head; wavefronts take every NW-th
-    // block).  It loads the token's inputs first, issues its block loads, and
-    // stores the token when the inputs arrive: its own later loads of the
-    // block see the stores (a wavefront's memory accesses stay in order), and
-    // nothing waits for them.
+    // A decode step's newest token (position ctx - 1) is written by the
+    // wavefront that reads the last block of the partition holding it (the
+    // only reader of that block for this KV head; wavefronts take every NW-th
+    // block).  Its lanes load the token's K runs and V cell elements in their
+    // own operand layout, encoded as the pool stores them, patch them into
+    // that block's registers when it arrives, and store them to the pool
+    // after the loop.  Stores issued before later loads would make every
+    // wait on those loads wait for the stores as well (one counter covers
+    // both, in issue order), and under full read traffic stores are slow.
     const bool writer = APPEND && tok1 == ctx && ctx > 0 && wv == (blk1 - 1 - blk0) % NW;
+    const int tn = (ctx - 1) & (kBlock - 1);   // the newest token's slot in its block
 
     // Q^T operands: head g*G + n (zero for n >= G), head dims per the K mapping
     bf16x8 qop[NQK];
@@ -250,12 +257,9 @@ __device__ __forceinline__ void decode_item(const DecodeParams &p, int s, int g,
             const int32_t b = wtable[NW * min(k, nk - 1)];
             return k < nk ? b : -1;
         };
-        // with two blocks or fewer the last one is loaded in the prologue: the
-        // token is stored before it then
-        const bool early = writer && nk <= 2;
+        // the newest token's inputs go out first (lane elements lane + 64 i)
         NewToken<D> nt;
-        if (writer) nt = append_load<KV, D>(p, table, s, g, ctx - 1, lane);
-        if (early) append_store<KV, D>(p, nt, g, ctx - 1, lane);
+        if (APPEND && writer) nt = append_load<KV, D>(p, table, s, g, ctx - 1, lane);
         u32x4 kb[2][NKL], vb[2][NVL];
         int32_t idb[2];
 #pragma unroll
@@ -264,11 +268,68 @@ __device__ __forceinline__ void decode_item(const DecodeParams &p, int s, int g,
             load_k(idb[d], kb[d], kFenced);
             load_v(idb[d], vb[d], kFenced);
         }
-        if (writer && !early) append_store<KV, D>(p, nt, g, ctx - 1, lane);
+        // ... and into LDS, encoded as the pool stores them, in head-dim
+        // order: waiting for the inputs holds none of the block loads above
+        if constexpr (APPEND) {
+            if (writer) {
+#pragma unroll
+                for (int i = 0; i < D / 64; ++i) {
+                    const int d = lane + 64 * i;
+                    if constexpr (KV == kBF16) {
+                        reinterpret_cast<uint16_t *>(sm.tok_k)[d] = (uint16_t)nt.k[i];
+                        reinterpret_cast<uint16_t *>(sm.tok_v)[d] = (uint16_t)nt.v[i];
+                    } else {
+                        const bool f32 = p.new_dtype == kF32;
+                        const float kx = f32 ? __uint_as_float(nt.k[i]) : __uint_as_float(nt.k[i] << 16);
+                        const float vx = f32 ? __uint_as_float(nt.v[i]) : __uint_as_float(nt.v[i] << 16);
+                        sm.tok_k[d] = (uint8_t)f32_to_e4m3(kx * p.inv_k_scale);
+                        sm.tok_v[d] = (uint8_t)f32_to_e4m3(vx * p.inv_v_scale);
+                    }
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            }
+        }
+        // The token into the registers of its block, as its own loads would
+        // return it once stored: lanes n == tn take K runs c + 4i (bytes
+        // 16 (c + 4i) of the staged K), lanes c == tn / 4 the elements of
+        // token tn % 4 in their V cells (element (w, r) of a cell sits at
+        // byte (4 w + r) EB; the staged V word at byte 4 (16 jj + n) holds
+        // the cell's W head dims).
+        auto patch = [&](u32x4 (&kr)[NKL], u32x4 (&vr)[NVL]) {
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            if (n == tn) {
+#pragma unroll
+                for (int i = 0; i < NKL; ++i) kr[i] = *reinterpret_cast<const u32x4 *>(sm.tok_k + 16 * (c + 4 * i));
+            }
+            if (c == (tn >> 2)) {
+                const int r = tn & 3;
+#pragma unroll
+                for (int jj = 0; jj < NVL; ++jj) {
+                    const uint32_t x = *reinterpret_cast<const uint32_t *>(sm.tok_v + 4 * (16 * jj + n));
+#pragma unroll
+                    for (int w = 0; w < W; ++w) {
+                        if constexpr (KV == kBF16) {
+                            const uint32_t e = (x >> (16 * w)) & 0xffffu;
+                            const uint32_t sh = 16u * (uint32_t)(r & 1);
+#pragma unroll
+                            for (int h = 0; h < 2; ++h)
+                                if ((r >> 1) == h)
+                                    vr[jj][2 * w + h] = (vr[jj][2 * w + h] & ~(0xffffu << sh)) | (e << sh);
+                        } else {
+                            const uint32_t e = (x >> (8 * w)) & 0xffu;
+                            const uint32_t sh = 8u * (uint32_t)r;
+                            vr[jj][w] = (vr[jj][w] & ~(0xffu << sh)) | (e << sh);
+                        }
+                    }
+                }
+            }
+        };
+
         int32_t id_pre = id_at(2);
         auto step = [&](int d, int kk) {
             const int32_t id_after = id_pre;  // block kk + 2
             id_pre = id_at(kk + 3);
+            if (APPEND && writer && blk0 + wv + NW * kk == blk1 - 1) patch(kb[d], vb[d]);
             const floatx4 sacc = qk(kb[d]);
             load_k(id_after, kb[d], kFree);
             if (valid(idb[d])) softmax_pv(sacc, vb[d], blk0 + wv + NW * kk);
@@ -281,6 +342,36 @@ __device__ __forceinline__ void decode_item(const DecodeParams &p, int s, int g,
             step(1, k + 1);
         }
         if (k < nk) step(0, k);
+
+        // the token to the pool (an id outside the pool is skipped): K runs
+        // as 16-byte stores, V elements one by one
+        if constexpr (APPEND) {
+            if (writer && nt.b >= 0) {
+                const int64_t tile0 = (nt.b * p.num_kv_heads + g) * TILE_BYTES;
+                char *kt = const_cast<char *>(kbase) + tile0;
+                char *vt = const_cast<char *>(vbase) + tile0;
+                if (n == tn) {
+#pragma unroll
+                    for (int i = 0; i < NKL; ++i)
+                        store16_nt(kt + ((c + 4 * i) * kBlock + tn) * 16,
+                                   *reinterpret_cast<const uint4 *>(sm.tok_k + 16 * (c + 4 * i)));
+                }
+                if (c == (tn >> 2)) {
+#pragma unroll
+                    for (int jj = 0; jj < NVL; ++jj) {
+                        const uint32_t x = *reinterpret_cast<const uint32_t *>(sm.tok_v + 4 * (16 * jj + n));
+#pragma unroll
+                        for (int w = 0; w < W; ++w) {
+                            const int off = ((tn >> 2) * (D / W) + 16 * jj + n) * 16 + (w * 4 + (tn & 3)) * EB;
+                            if constexpr (KV == kBF16)
+                                __builtin_nontemporal_store((uint16_t)(x >> (16 * w)), reinterpret_cast<uint16_t *>(vt + off));
+                            else
+                                __builtin_nontemporal_store((uint8_t)(x >> (8 * w)), reinterpret_cast<uint8_t *>(vt + off));
+                        }
+                    }
+                }
+            }
+        }
     }
 
     // per-head totals of the lane-partial sums
