@@ -114,12 +114,15 @@ def copy_probe(nbytes: int, steps: int) -> None:
 
 
 def source_digest() -> str:
-    """Digest of the sources and compile flags the matrix-core decode kernel
-    is built from."""
+    """Digest of the code (comments and blank lines dropped) and compile flags
+    the matrix-core decode kernel is built from."""
     from paged_kv_cache_401_amd import build as pa_build
     h = hashlib.sha256()
     for f in ("pa_decode_mfma.hip", "pa_mfma_util.h", "pa_internal.h", "pa_store.h"):
-        h.update(open(os.path.join(ROOT, "paged_kv_cache_401_amd", "csrc", f), "rb").read())
+        for ln in open(os.path.join(ROOT, "paged_kv_cache_401_amd", "csrc", f)).read().splitlines():
+            code = ln.split("//", 1)[0].rstrip()
+            if code:
+                h.update(code.encode() + b"\n")
     h.update(" ".join(pa_build.common_flags()).replace(ROOT, "").encode())
     return h.hexdigest()[:16]
 

@@ -94,10 +94,11 @@ __device__ __forceinline__ void decode_item(const DecodeParams &p, int s, int g,
     // A decode step's newest token (position ctx - 1) is written by the
     // wavefront that reads the last block of the partition holding it (the
     // only reader of that block for this KV head; wavefronts take every NW-th
-    // block).  Its lanes load the token's K runs and V cell elements in their
-    // own operand layout, encoded as the pool stores them, patch them into
-    // that block's registers when it arrives, and store them to the pool
-    // after the loop.  Stores issued before later loads would make every
+    // block).  It loads the token's inputs before its block loads and
+    // stages them in LDS, encoded as the pool stores them; when the block
+    // arrives, the lanes that hold the token's K runs and V cell elements
+    // take them from there into its registers, and after the loop they store
+    // them to the pool.  Stores issued before later loads would make every
     // wait on those loads wait for the stores as well (one counter covers
     // both, in issue order), and under full read traffic stores are slow.
     const bool writer = APPEND && tok1 == ctx && ctx > 0 && wv == (blk1 - 1 - blk0) % NW;
