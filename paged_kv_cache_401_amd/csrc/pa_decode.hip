@@ -403,7 +403,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KV == 
 // One wavefront per row (four rows per workgroup); lane i holds head dims
 // E*i .. E*i+E-1.  The partition weights are computed 64 at a time, one per
 // lane, and broadcast with readlane, so the partial numerators of eight
-// partitions are in flight at once.
+// partitions are in flight at once; the first four are loaded with the
+// partition maxima and sums, before the merged maximum is known.
 template <int D>
 __global__ __launch_bounds__(kThreads) void decode_reduce_kernel(DecodeParams p) {
     constexpr int E = D / 64;
@@ -419,8 +420,22 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_kernel(DecodeParams p)
     const float *ls = p.ws_l + row * p.max_partitions;
     const float *as = p.ws_acc + row * p.max_partitions * D + E * lane;
 
-    float M = kNegInf;
-    for (int i = lane; i < nparts; i += 64) M = fmaxf(M, ms[i]);
+    // Every load that does not depend on the merged maximum goes out at once:
+    // this lane's partition (m, l) and the first PRE partitions' numerators;
+    // only their use waits for M.
+    constexpr int PRE = 4;
+    const float m0 = lane < nparts ? ms[lane] : kNegInf;
+    const float l0 = lane < nparts ? ls[lane] : 0.f;
+    float pre[PRE][E];
+#pragma unroll
+    for (int u = 0; u < PRE; ++u) {
+        const float *a = as + (int64_t)u * D;
+#pragma unroll
+        for (int e = 0; e < E; ++e) pre[u][e] = u < nparts ? a[e] : 0.f;
+    }
+
+    float M = m0;
+    for (int i = lane + 64; i < nparts; i += 64) M = fmaxf(M, ms[i]);
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
 
@@ -428,29 +443,47 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_kernel(DecodeParams p)
     float O[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) O[e] = 0.f;
+    // numerator of partition base + j, weighted by lane j's weight f
+    auto add = [&](float f, int base, int j) {
+        const float fj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), j));
+        const float *a = as + (int64_t)(base + j) * D;
+        if constexpr (E == 2) {
+            const float2 v = *reinterpret_cast<const float2 *>(a);
+            O[0] += v.x * fj;
+            O[1] += v.y * fj;
+        } else {
+            O[0] += a[0] * fj;
+        }
+    };
     if (M != kNegInf) {
-        for (int base = 0; base < nparts; base += 64) {
+        {   // partitions 0..63, the first PRE of them preloaded
+            const float f = lane < nparts ? exp2f(m0 - M) : 0.f;
+            L += lane < nparts ? l0 * f : 0.f;
+            const int cnt = min(64, nparts);
+#pragma unroll
+            for (int u = 0; u < PRE; ++u) {
+                const float fj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), u));
+#pragma unroll
+                for (int e = 0; e < E; ++e) O[e] += u < cnt ? pre[u][e] * fj : 0.f;
+            }
+            int j = PRE;
+            for (; j + 8 <= cnt; j += 8) {
+#pragma unroll
+                for (int u = 0; u < 8; ++u) add(f, 0, j + u);
+            }
+            for (; j < cnt; ++j) add(f, 0, j);
+        }
+        for (int base = 64; base < nparts; base += 64) {
             const int i = base + lane;
             const float f = i < nparts ? exp2f(ms[i] - M) : 0.f;
             L += i < nparts ? ls[i] * f : 0.f;
             const int cnt = min(64, nparts - base);
-            auto add = [&](int j) {
-                const float fj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), j));
-                const float *a = as + (int64_t)(base + j) * D;
-                if constexpr (E == 2) {
-                    const float2 v = *reinterpret_cast<const float2 *>(a);
-                    O[0] += v.x * fj;
-                    O[1] += v.y * fj;
-                } else {
-                    O[0] += a[0] * fj;
-                }
-            };
             int j = 0;
             for (; j + 8 <= cnt; j += 8) {
 #pragma unroll
-                for (int u = 0; u < 8; ++u) add(j + u);
+                for (int u = 0; u < 8; ++u) add(f, base, j + u);
             }
-            for (; j < cnt; ++j) add(j);
+            for (; j < cnt; ++j) add(f, base, j);
         }
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) L += __shfl_xor(L, o);
