@@ -37,12 +37,22 @@ MUTATIONS = {
     "prefill_ignores_cached_prefix": ("int64_t pos = (int64_t)ctx[s] - n_new + i;",
                                       "int64_t pos = i;"),
     "prefill_query_rows_transposed": ("q, q_dt, qi * Hq + h, Hq, h,", "q, q_dt, qi + h * Hq, Hq, h,"),
+    # fp8 dequantisation inside attention: V scaled by K's scale, codes read
+    # without their scale, K's scale left out of the scores
+    "fp8_v_uses_k_scale": ("pool_dt, v_scale);", "pool_dt, k_scale);"),
+    "fp8_no_scale": ("return orc_fp8_decode(base[idx]) * fp8_scale;",
+                     "return orc_fp8_decode(base[idx]);"),
+    "fp8_k_scale_dropped": ("pool_dt, k_scale);", "pool_dt, 1.0);"),
+    "fp8_scale_inverted": ("return orc_fp8_decode(base[idx]) * fp8_scale;",
+                           "return orc_fp8_decode(base[idx]) / fp8_scale;"),
 }
 
 PIN_TESTS = [
     pins.test_worked_example_table_readback_and_waste,
     lambda: pins.test_workload_readback_through_tables("mha13b"),
     lambda: pins.test_paged_equals_dense_library_softmax("sampling_b"),
+    lambda: pins.test_paged_equals_dense_library_softmax("fp8"),
+    pins.test_fp8_scales_two_tokens_closed_form,
     pins.test_single_token_returns_its_value_exactly,
     pins.test_zero_query_gives_mean_of_values,
     pins.test_two_tokens_logistic_closed_form,
@@ -53,6 +63,7 @@ PIN_TESTS = [
     pins.test_fp8_encode_saturates_and_keeps_nan,
     pins.test_fp8_scatter_encodes_scaled_values,
     lambda: prefill_pins.test_prefill_equals_dense_causal_library_softmax("chunked_gqa70b"),
+    lambda: prefill_pins.test_prefill_equals_dense_causal_library_softmax("chunked_fp8"),
     lambda: prefill_pins.test_each_chunk_row_equals_decode_at_its_position("chunked_gqa70b"),
     prefill_pins.test_causality_future_tokens_do_not_matter,
 ]
