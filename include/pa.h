@@ -49,6 +49,17 @@
  *           W = 4 / elem_bytes (16-byte cells of 4 tokens x W dims, tokens fastest).
  * Both orders make each 16-lane quarter of a wavefront load 256 contiguous
  * bytes straight into matrix-core operand registers.
+ *
+ * This is NOT the plain row-major tile [16 slots][head_dim] (each token's head
+ * vector contiguous) of the glossary page's schematic pool [block][slot][dim]:
+ * the pages fix which block and slot a token occupies, not the byte order
+ * inside a block, and the order above lets the decode kernel take K and V
+ * from memory into matrix-core operands with no transpose (the plain order
+ * would need a transpose through LDS or registers per block).  Tiles written
+ * by pa_reshape_and_cache, pa_decode_append, pa_copy_blocks and
+ * pa_swap_blocks are always in this order; a caller that fills pool memory
+ * itself in the row-major order gets wrong results and must write through
+ * pa_reshape_and_cache instead.
  */
 #ifndef PA_H
 #define PA_H
@@ -108,7 +119,14 @@ int32_t pa_decode_partition_tokens(const pa_pool_t *pool, int32_t num_seqs,
                                    int32_t partition_tokens);
 
 /* Workspace bytes pa_decode needs for these arguments (0 when every context
- * fits one partition).  Holds fp32 partial results of the split-K passes. */
+ * fits one partition).  Holds fp32 partial results of the split-K passes.
+ * The context bound is given as max_blocks_per_seq, the capacity of one
+ * block-table row (pa_decode's argument of the same name), rather than as a
+ * longest context length: pa_decode sizes its grid from the table's
+ * capacity, max_blocks_per_seq * 16 tokens, so that is the bound the
+ * workspace must cover.  A caller that knows only its longest context n
+ * passes ceil(n / 16) and must then call pa_decode with block tables of that
+ * many columns. */
 size_t pa_decode_workspace_size(const pa_pool_t *pool, int32_t num_seqs, int32_t num_q_heads,
                                 int32_t max_blocks_per_seq, int32_t partition_tokens);
 
@@ -120,7 +138,8 @@ size_t pa_decode_workspace_size(const pa_pool_t *pool, int32_t num_seqs, int32_t
  *                  logical block; entries past ceil(ctx / 16) are never read.
  *   context_lens   int32 [num_seqs]: tokens attended (0 gives a zero row).
  *   scale          softmax scale applied to q . k.
- *   out            fp32 [num_seqs][num_q_heads][head_dim].
+ *   out            fp32 [num_seqs][num_q_heads][head_dim] (16-byte aligned;
+ *                  q too).
  *   partition_tokens  split-K partition length in tokens (multiple of 16),
  *                  0 = library's choice.  Contexts longer than one partition
  *                  are processed as independent partitions merged by a
@@ -165,8 +184,10 @@ int pa_decode_ex(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t 
  *   k_new, v_new   [num_seqs][num_kv_heads][head_dim] of kv_dtype: the pool's
  *                  dtype for 16/32-bit pools, PA_BF16 or PA_F32 for an FP8 pool
  *                  (encoded as pa_reshape_and_cache does).  Sequences with
- *                  context length 0, or whose last table entry is outside the
- *                  pool, write nothing.
+ *                  context length 0, a context longer than its table row
+ *                  (max_blocks_per_seq * 16; attended as that many tokens),
+ *                  or whose last table entry is outside the pool, write
+ *                  nothing.
  * Other arguments, flags and errors as pa_decode_ex.
  */
 int pa_decode_append(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t num_seqs,

@@ -275,12 +275,13 @@ int pa_decode(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t num
 
 namespace {
 
-// pa_decode_ex, and pa_decode_append when k_new is not NULL
+// pa_decode_ex, and pa_decode_append when k_new is not NULL.  `checks`:
+// debug mode may run its index checks (they allocate a buffer).
 int decode_impl(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t num_seqs,
                 int32_t num_q_heads, const int32_t *block_tables, int32_t max_blocks_per_seq,
                 const int32_t *context_lens, float scale, float *out, int32_t partition_tokens,
                 void *workspace, size_t workspace_bytes, uint32_t flags, const void *k_new,
-                const void *v_new, int32_t kv_dtype, void *stream) {
+                const void *v_new, int32_t kv_dtype, void *stream, bool checks = true) {
     if (flags & ~(uint32_t)PA_DECODE_SHARED_KV)
         return fail(PA_ERR_SHAPE, "unknown decode flags 0x%x", flags);
     int rc = check_pool(pool);
@@ -298,7 +299,8 @@ int decode_impl(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t n
     if (num_seqs == 0) return ok();
     if (!q || !block_tables || !context_lens || !out)
         return fail(PA_ERR_NULL, "q, block_tables, context_lens and out must be non-NULL");
-    if (!aligned16(q)) return fail(PA_ERR_ALIGN, "q must be 16-byte aligned");
+    // the kernels write out (and read q) with 16-byte accesses
+    if (!aligned16(q) || !aligned16(out)) return fail(PA_ERR_ALIGN, "q and out must be 16-byte aligned");
     int32_t np = 1;
     const size_t need = workspace_for(pool, num_seqs, num_q_heads, max_blocks_per_seq, ptok, &np);
     if (need > 0 && (!workspace || workspace_bytes < need))
@@ -349,7 +351,7 @@ int decode_impl(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t n
         p.ws_l = reinterpret_cast<float *>(ws + acc + ml);
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (debug_on()) {
+    if (checks && debug_on()) {
         rc = debug_check("pa_decode", 0, st, [&](int32_t *report, void *) {
             return pa::launch_check_tables(block_tables, context_lens, num_seqs, max_blocks_per_seq,
                                            pool->num_blocks, report, st);

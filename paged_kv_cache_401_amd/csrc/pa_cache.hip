@@ -273,12 +273,13 @@ __global__ __launch_bounds__(kThreads) void swap_blocks_kernel(char *k_pool, cha
 // Workgroup (sequence, KV head): each sequence's newest token to the slot of
 // position context_len - 1, through its block table (a decode step whose
 // attention kernel cannot write it itself).
+// A context longer than its table row can hold (the attention clamps it)
+// has no slot for its newest token: nothing is written.
 template <int POOL, int D>
 __global__ __launch_bounds__(kThreads) void append_tokens_kernel(DecodeParams p) {
     const int s = blockIdx.x, g = blockIdx.y;
-    int ctx = p.context_lens[s];
-    ctx = ctx < 0 ? 0 : (ctx > p.max_blocks_per_seq * kBlock ? p.max_blocks_per_seq * kBlock : ctx);
-    if (ctx == 0) return;
+    const int ctx = p.context_lens[s];
+    if (ctx <= 0 || ctx > p.max_blocks_per_seq * kBlock) return;
     const int32_t *table = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
     for (int d = threadIdx.x; d < D; d += kThreads) append_element<POOL, D>(p, table, s, g, ctx - 1, d);
 }

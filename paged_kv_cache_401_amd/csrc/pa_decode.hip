@@ -110,8 +110,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KV == 
                                    bid / p.num_q_heads);
     const int g = h / p.group;
 
-    int ctx = p.context_lens[s];
-    ctx = ctx < 0 ? 0 : (ctx > p.max_blocks_per_seq * kBlock ? p.max_blocks_per_seq * kBlock : ctx);
+    const int raw_ctx = p.context_lens[s];
+    const int ctx = raw_ctx < 0 ? 0 : (raw_ctx > p.max_blocks_per_seq * kBlock ? p.max_blocks_per_seq * kBlock : raw_ctx);
     const int nparts = (ctx + p.partition_tokens - 1) / p.partition_tokens;
     if (part >= (nparts > 1 ? nparts : 1)) return;
     const int tok0 = part * p.partition_tokens;
@@ -127,7 +127,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KV == 
     // inputs first, issues its block loads, and stores the token when the
     // inputs arrive: its own later loads of the block see the stores (a
     // wavefront's memory accesses stay in order), and nothing waits for them.
-    const bool writer = p.k_new != nullptr && tok1 == ctx && ctx > 0 && wv == (blk1 - 1 - blk0) % 4;
+    // A context longer than its table row (clamped above) has no slot for its
+    // newest token and writes nothing.
+    const bool writer = p.k_new != nullptr && tok1 == ctx && ctx > 0 && raw_ctx == ctx &&
+                        wv == (blk1 - 1 - blk0) % 4;
 
     // q elements matching this lane's K runs: fp32 values for an fp32 pool,
     // else the raw bf16 pairs (dims 2i, 2i+1 of run c + 4j in word i), which

@@ -63,10 +63,11 @@ struct DecodeLds {
 // One work item: partition `part` of sequence s, KV head g, with context
 // length ctx (already clamped to the table's capacity), computed by the NW
 // wavefronts of the calling workgroup.  APPEND: the decode step's newest
-// tokens are written by this call (DecodeParams::k_new / v_new).
+// tokens are written by this call (DecodeParams::k_new / v_new) unless
+// `clamped` (the context was longer than its table row: no slot to write).
 template <int KV, int D, bool STREAM, int NW, bool APPEND>
 __device__ __forceinline__ void decode_item(const DecodeParams &p, int s, int g, int part, int ctx,
-                                            DecodeLds<D, NW> &sm) {
+                                            bool clamped, DecodeLds<D, NW> &sm) {
     constexpr int EB = KV == kBF16 ? 2 : 1;
     constexpr int TILE_BYTES = kBlock * D * EB;
     constexpr int NQK = D / 32;                   // QK steps (32-deep) per block
@@ -101,7 +102,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams &p, int s, int g,
     // them to the pool.  Stores issued before later loads would make every
     // wait on those loads wait for the stores as well (one counter covers
     // both, in issue order), and under full read traffic stores are slow.
-    const bool writer = APPEND && tok1 == ctx && ctx > 0 && wv == (blk1 - 1 - blk0) % NW;
+    const bool writer = APPEND && !clamped && tok1 == ctx && ctx > 0 && wv == (blk1 - 1 - blk0) % NW;
     const int tn = (ctx - 1) & (kBlock - 1);   // the newest token's slot in its block
 
     // Q^T operands: head g*G + n (zero for n >= G), head dims per the K mapping
@@ -456,7 +457,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
     const int g = bid % p.num_kv_heads;
     const int s = sequence_of_rank(p.context_lens, p.num_seqs, p.max_blocks_per_seq * kBlock,
                                    bid / p.num_kv_heads);
-    decode_item<KV, D, STREAM, NW, APPEND>(p, s, g, part, clamp_ctx(p, p.context_lens[s]), sm);
+    const int raw_ctx = p.context_lens[s];
+    const int ctx = clamp_ctx(p, raw_ctx);
+    decode_item<KV, D, STREAM, NW, APPEND>(p, s, g, part, ctx, raw_ctx > ctx, sm);
 }
 
 template <int KV, int D, bool STREAM, bool APPEND>

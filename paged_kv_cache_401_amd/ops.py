@@ -251,6 +251,9 @@ def decode(pool: KVPool, q: torch.Tensor, block_tables: torch.Tensor, context_le
     mbs = block_tables.shape[1]
     if out is None:
         out = torch.empty((S, Hq, D), dtype=torch.float32, device=q.device)
+    elif tuple(out.shape) != (S, Hq, D):
+        raise ValueError("out must be [num_seqs][num_q_heads][head_dim] = %s, got %s"
+                         % ((S, Hq, D), tuple(out.shape)))
     need = decode_workspace_size(pool, S, Hq, mbs, partition_tokens)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -292,6 +295,9 @@ def prefill(pool: KVPool, q: torch.Tensor, query_start: torch.Tensor, max_query_
         raise TypeError("prefill q must be bfloat16")
     if out is None:
         out = torch.empty((T, Hq, D), dtype=torch.float32, device=q.device)
+    elif tuple(out.shape) != (T, Hq, D):
+        raise ValueError("out must be [total chunk tokens][num_q_heads][head_dim] = %s, got %s"
+                         % ((T, Hq, D), tuple(out.shape)))
     d = pool.desc()
     _check(lib().pa_prefill(ctypes.byref(d), _dev(q, "q"), BF16, S, Hq,
                             _dev(query_start, "query_start", torch.int32), int(max_query_len),

@@ -236,3 +236,11 @@ def test_decode_append_argument_rules():
     fp8 = desc(kv_dtype=ops.FP8)
     assert L.pa_decode_append(ctypes.byref(fp8), 16, ops.BF16, 1, 8, 16, 4, 16, 0.1, 16, 0, None, 0, 0,
                               16, 16, ops.FP8, None) == -2      # fp8 tokens are not an input type
+
+
+def test_decode_rejects_misaligned_out():
+    L = ops.lib()
+    d = desc()
+    assert L.pa_decode(ctypes.byref(d), 16, ops.BF16, 1, 8, 16, 4, 16, 0.1, 20, 0, None, 0,
+                       None) == -6
+    assert b"out" in L.pa_last_error()

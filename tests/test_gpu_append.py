@@ -138,3 +138,48 @@ def test_append_full_size_step_and_graph():
         g.replay()
         torch.cuda.synchronize()
         assert_same_bytes(out.cpu().numpy(), ref.cpu().numpy(), what="replay %d" % rep)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(16, 2), (2, 2), (64, 2)])
+@pytest.mark.parametrize("ptok", [0, 32])
+def test_append_overlong_context_writes_nothing(Hq, Hkv, ptok):
+    """A context longer than its table row (max_blocks_per_seq * 16) is
+    attended as that many tokens and has no slot for a newest token: the step
+    writes nothing for it -- no cached token is overwritten -- and writes the
+    other sequences' tokens as usual.  Matrix-core kernel (16 / 2 heads),
+    vector-ALU kernel with one head per KV head (2 / 2), and grouped heads on
+    the vector-ALU kernel with its separate write kernel (64 / 2)."""
+    rng = np.random.default_rng(77 + Hq)
+    w = wl._simple("overlong", 3, Hq, Hkv, 128, [64, 33, 128], oracle.BF16, oracle.BF16, oracle.BF16,
+                   float(np.float32(1 / math.sqrt(128))), 31, "cpu", rng)
+    tables = w.block_tables.copy()
+    assert tables.shape[1] * 16 == 128
+    ctx = w.context_lens.copy()
+    ctx[2] = 128 + 7                           # clamped to the row's 128 tokens, all written
+    gen = torch.Generator().manual_seed(9)
+    k_new = (torch.randn((w.S, w.Hkv, w.D), generator=gen) * 2).to(torch.bfloat16)
+    v_new = (torch.randn((w.S, w.Hkv, w.D), generator=gen) * 2).to(torch.bfloat16)
+    slots = last_slots(w, np.minimum(ctx, 128), tables)
+    slots[2] = -1                              # nothing is written for the over-long context
+
+    ref_pool = gpu_pool(w, fill=0xFF)
+    before_k, before_v = ref_pool.k.cpu().numpy(), ref_pool.v.cpu().numpy()
+    ops.reshape_and_cache(ref_pool, k_new.to(DEV), v_new.to(DEV), i32(slots))
+    ref = ops.decode(ref_pool, w.q.to(DEV), i32(tables), i32(ctx), w.scale, partition_tokens=ptok)
+
+    pool = gpu_pool(w, fill=0xFF)
+    got = ops.decode(pool, w.q.to(DEV), i32(tables), i32(ctx), w.scale, partition_tokens=ptok,
+                     k_new=k_new.to(DEV), v_new=v_new.to(DEV))
+    torch.cuda.synchronize()
+    gk, gv = pool.k.cpu().numpy(), pool.v.cpu().numpy()
+    assert_same_bytes(gk, ref_pool.k.cpu().numpy(), what="K pool")
+    assert_same_bytes(gv, ref_pool.v.cpu().numpy(), what="V pool")
+    assert_same_bytes(got.cpu().numpy(), ref.cpu().numpy(), what="outputs")
+    # the over-long sequence's blocks are unchanged; the others' last blocks changed
+    tile = Hkv * 16 * w.D * 2
+    for b in tables[2]:
+        sl = slice(int(b) * tile, (int(b) + 1) * tile)
+        assert np.array_equal(gk[sl], before_k[sl]) and np.array_equal(gv[sl], before_v[sl])
+    for s in (0, 1):
+        b = int(tables[s][(ctx[s] - 1) // 16])
+        assert not np.array_equal(gk[b * tile:(b + 1) * tile], before_k[b * tile:(b + 1) * tile])

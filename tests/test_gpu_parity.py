@@ -155,14 +155,18 @@ def test_decode_any_partition_size(name, ptok):
     assert float(np.max(np.abs(out - ref))) <= tolerance(w)
 
 
-def _one_hot(S, Hq, Hkv, D, ctx, pool_dt, targets, seed=0):
+def _one_hot(S, Hq, Hkv, D, ctx, pool_dt, targets, seed=0, k_scale=1.0, v_scale=1.0, scale=0.5):
     """K is zero except K[target_s][:, 0] = c; q = e_0; so the output of every
-    head is exactly that token's V row (times v_scale)."""
+    head is exactly that token's V row (times v_scale).  The target's score,
+    c * k_scale * scale, must be >= 200 so that every other weight is 0 in
+    fp32."""
     rng = np.random.default_rng(seed)
     in_dt = oracle.F32 if pool_dt == oracle.F32 else oracle.BF16
-    w = wl._simple("one_hot", S, Hq, Hkv, D, ctx, pool_dt, in_dt, in_dt, 0.5, seed, "cpu", rng)
+    w = wl._simple("one_hot", S, Hq, Hkv, D, ctx, pool_dt, in_dt, in_dt, scale, seed, "cpu", rng)
     _, k, v, slots = w.ops[0]
-    c = 448.0 if pool_dt == oracle.FP8 else 1000.0
+    # an fp8 K input of 448 * k_scale or more saturates to the code of 448
+    c = 448.0 * k_scale if pool_dt == oracle.FP8 else 1000.0
+    assert (448.0 if pool_dt == oracle.FP8 else c) * k_scale * scale >= 200
     k = torch.zeros_like(k)
     off = np.concatenate([[0], np.cumsum(w.context_lens)[:-1]])
     for s in range(S):
@@ -171,7 +175,7 @@ def _one_hot(S, Hq, Hkv, D, ctx, pool_dt, targets, seed=0):
     q[:, :, 0] = 1.0
     w.ops = [("write", k, v, slots)]
     w.q = q
-    w.k_scale = w.v_scale = 1.0
+    w.k_scale, w.v_scale = k_scale, v_scale
     vals = [v[off[s] + targets[s]] for s in range(S)]
     return w, vals
 
@@ -206,6 +210,33 @@ def test_one_hot_probe_is_bit_exact(case, ptok):
                 v = oracle.fp8_decode(codes.ravel()).reshape(v.shape)
             for h in range(Hq):
                 assert np.array_equal(out[s, h], v[h // (Hq // Hkv)]), (case, s, h, targets[s])
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(64, 8), (4, 4)])
+@pytest.mark.parametrize("ptok", [0, 16, 512])
+def test_one_hot_fp8_distinct_scales_exact(Hq, Hkv, ptok):
+    """fp8 pool with k_scale != v_scale != 1 (glossary page, related
+    techniques: 8-bit cache): k_scale enters the scores (the one-hot score
+    448 * k_scale * scale must reach 200 for every other weight to vanish)
+    and v_scale the output, which is exactly fp32(decode(code) * v_scale),
+    code = E4M3FN(fp32(v) * fp32(1 / v_scale)), through the matrix-core
+    (64 / 8 heads) and vector-ALU (4 / 4) kernels, with and without split-K."""
+    S, D = 4, 128
+    k_scale, v_scale, scale = 0.37, 0.0173, 2.0
+    ctx = [1, 1037, 4096, 700]
+    rng = np.random.default_rng(4)
+    for targets in ([n - 1 for n in ctx], [int(rng.integers(0, n)) for n in ctx]):
+        w, vals = _one_hot(S, Hq, Hkv, D, ctx, oracle.FP8, targets, k_scale=k_scale,
+                           v_scale=v_scale, scale=scale)
+        out = gpu_decode(w, gpu_pool(w, fill=0xFF), partition_tokens=ptok)
+        inv = np.float32(1.0) / np.float32(v_scale)
+        for s in range(S):
+            x = vals[s].float().numpy()                                 # [Hkv][D]
+            codes = oracle.fp8_encode((x * inv).astype(np.float32))
+            want = (oracle.fp8_decode(codes.ravel()).astype(np.float32).reshape(x.shape)
+                    * np.float32(v_scale)).astype(np.float64)
+            for h in range(Hq):
+                assert np.array_equal(out[s, h], want[h // (Hq // Hkv)]), (s, h, targets[s])
 
 
 @pytest.mark.parametrize("group", [2, 4, 16, 32])
