@@ -168,6 +168,29 @@ int pa_decode_ex(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t 
                  const int32_t *context_lens, float scale, float *out, int32_t partition_tokens,
                  void *workspace, size_t workspace_bytes, uint32_t flags, void *stream);
 
+/* Largest split-K scratch, in bytes, that pa_decode_noalloc keeps per device. */
+#define PA_DECODE_NOALLOC_MAX_SCRATCH ((size_t)64 << 20)
+
+/*
+ * pa_decode_noalloc -- pa_decode_ex for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, and harnesses
+ * that forbid hipMalloc.  Same arguments, flags, result and errors as
+ * pa_decode_ex, without the workspace: the split-K partial results go to a
+ * static array of PA_DECODE_NOALLOC_MAX_SCRATCH bytes in device memory, one
+ * per device, which the library takes on its first call on that device and
+ * holds until the process ends.  Calls needing more than that
+ * (pa_decode_workspace_size of the same arguments) return PA_ERR_WORKSPACE
+ * and enqueue nothing.  The call allocates nothing: no hipMalloc or hipFree,
+ * and debug mode's index checks, which allocate, are not run by it.  Every
+ * call on one device shares that device's array (nothing in it needs to
+ * start cleared): calls that overlap on one device -- on different streams,
+ * or from different host threads -- race and give undefined results.
+ */
+int pa_decode_noalloc(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t num_seqs,
+                      int32_t num_q_heads, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                      const int32_t *context_lens, float scale, float *out, int32_t partition_tokens,
+                      uint32_t flags, void *stream);
+
 /*
  * pa_decode_append -- one decode step: write every sequence's newest token,
  * then attend as pa_decode_ex.  The newest token of sequence s sits at

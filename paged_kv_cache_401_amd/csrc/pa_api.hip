@@ -275,6 +275,34 @@ int pa_decode(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t num
 
 namespace {
 
+// Split-K scratch of pa_decode_noalloc: one copy per device, at its own
+// device address.  Host code never uses the array's name as an address (on
+// the host it names a stand-in): the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+__device__ __align__(256) unsigned char scratch[PA_DECODE_NOALLOC_MAX_SCRATCH];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[64] = {};
+
+// The current device's copy of `scratch` (NULL and a failed status on error).
+int scratch_for_current_device(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= 64) return fail(PA_ERR_HIP, "device %d: at most 64 devices are supported", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(PA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return PA_OK;
+}
+
 // pa_decode_ex, and pa_decode_append when k_new is not NULL.  `checks`:
 // debug mode may run its index checks (they allocate a buffer).
 int decode_impl(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t num_seqs,
@@ -411,6 +439,35 @@ int pa_decode_ex(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t 
     return decode_impl(pool, q, q_dtype, num_seqs, num_q_heads, block_tables, max_blocks_per_seq,
                        context_lens, scale, out, partition_tokens, workspace, workspace_bytes, flags,
                        nullptr, nullptr, 0, stream);
+}
+
+int pa_decode_noalloc(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t num_seqs,
+                      int32_t num_q_heads, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                      const int32_t *context_lens, float scale, float *out, int32_t partition_tokens,
+                      uint32_t flags, void *stream) {
+    // the arguments' own checks first (as pa_decode_ex makes them), then the
+    // size of the partials against the static scratch
+    int rc = check_pool(pool);
+    if (rc == PA_OK) rc = check_heads(pool, num_seqs, num_q_heads, max_blocks_per_seq);
+    int32_t ptok = 0;
+    if (rc == PA_OK)
+        rc = resolve_partition(pool, num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens, &ptok);
+    if (rc != PA_OK) return rc;
+    const size_t need = workspace_for(pool, num_seqs, num_q_heads, max_blocks_per_seq, ptok, nullptr);
+    if (need > PA_DECODE_NOALLOC_MAX_SCRATCH)
+        return fail(PA_ERR_WORKSPACE,
+                    "split-K partials of %zu bytes exceed the %zu-byte static scratch of "
+                    "pa_decode_noalloc (use pa_decode_ex with a workspace, or longer partitions)",
+                    need, (size_t)PA_DECODE_NOALLOC_MAX_SCRATCH);
+    void *ws = nullptr;
+    if (need > 0 && num_seqs > 0) {
+        rc = scratch_for_current_device(&ws);
+        if (rc != PA_OK) return rc;
+    }
+    return decode_impl(pool, q, q_dtype, num_seqs, num_q_heads, block_tables, max_blocks_per_seq,
+                       context_lens, scale, out, partition_tokens, ws,
+                       ws ? (size_t)PA_DECODE_NOALLOC_MAX_SCRATCH : 0, flags, nullptr, nullptr, 0,
+                       stream, /*checks=*/false);
 }
 
 int pa_decode_append(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t num_seqs,

@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 
 # every symbol include/pa.h declares
 EXPORTS = ("pa_pool_bytes", "pa_decode_partition_tokens", "pa_decode_workspace_size", "pa_decode",
-           "pa_decode_ex", "pa_decode_append",
+           "pa_decode_ex", "pa_decode_noalloc", "pa_decode_append",
            "pa_prefill", "pa_reshape_and_cache", "pa_swap_blocks", "pa_copy_blocks",
            "pa_check_workspace_size", "pa_check_tables", "pa_check_query_start", "pa_check_slots",
            "pa_check_copy_pairs", "pa_check_swap_pairs", "pa_set_debug",
@@ -74,6 +74,8 @@ def lib() -> ctypes.CDLL:
     L.pa_decode.restype = ctypes.c_int
     L.pa_decode_ex.argtypes = [PD, P, I32, I32, I32, P, I32, P, F, P, I32, P, SZ, ctypes.c_uint32, P]
     L.pa_decode_ex.restype = ctypes.c_int
+    L.pa_decode_noalloc.argtypes = [PD, P, I32, I32, I32, P, I32, P, F, P, I32, ctypes.c_uint32, P]
+    L.pa_decode_noalloc.restype = ctypes.c_int
     L.pa_decode_append.argtypes = [PD, P, I32, I32, I32, P, I32, P, F, P, I32, P, SZ, ctypes.c_uint32,
                                    P, P, I32, P]
     L.pa_decode_append.restype = ctypes.c_int
@@ -275,6 +277,33 @@ def decode(pool: KVPool, q: torch.Tensor, block_tables: torch.Tensor, context_le
         raise TypeError("k_new/v_new must both be float32 or bfloat16")
     _check(lib().pa_decode_append(*common, _dev(k_new, "k_new"), _dev(v_new, "v_new"),
                                   TORCH_TO_PA[k_new.dtype], _stream(stream)))
+    return out
+
+
+def decode_noalloc(pool: KVPool, q: torch.Tensor, block_tables: torch.Tensor,
+                   context_lens: torch.Tensor, scale: float, out: torch.Tensor,
+                   partition_tokens: int = 0, stream=None, shared_kv: bool = False) -> torch.Tensor:
+    """pa_decode_noalloc: decode whose split-K partials go to the library's
+    static per-device scratch; ``out`` must be given ([num_seqs][num_q_heads]
+    [head_dim] fp32), as the call allocates nothing."""
+    S, Hq, D = q.shape
+    if D != pool.head_dim:
+        raise ValueError("q head dim %d differs from the pool's %d" % (D, pool.head_dim))
+    if q.dtype not in TORCH_TO_PA:
+        raise TypeError("q must be float32 or bfloat16")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.numel() != S:
+        raise ValueError("block_tables must be [num_seqs][max_blocks]; context_lens [num_seqs]")
+    if tuple(out.shape) != (S, Hq, D):
+        raise ValueError("out must be [num_seqs][num_q_heads][head_dim] = %s, got %s"
+                         % ((S, Hq, D), tuple(out.shape)))
+    d = pool.desc()
+    flags = DECODE_SHARED_KV if shared_kv else DECODE_STREAM_KV
+    _check(lib().pa_decode_noalloc(ctypes.byref(d), _dev(q, "q"), TORCH_TO_PA[q.dtype], S, Hq,
+                                   _dev(block_tables, "block_tables", torch.int32),
+                                   block_tables.shape[1],
+                                   _dev(context_lens, "context_lens", torch.int32), float(scale),
+                                   _dev(out, "out", torch.float32), int(partition_tokens), flags,
+                                   _stream(stream)))
     return out
 
 

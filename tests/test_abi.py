@@ -238,6 +238,24 @@ def test_decode_append_argument_rules():
                               16, 16, ops.FP8, None) == -2      # fp8 tokens are not an input type
 
 
+def test_decode_noalloc_argument_rules():
+    """The allocation-free decode checks its arguments like pa_decode_ex and
+    refuses partials larger than its static scratch before touching the GPU."""
+    L = ops.lib()
+    d = desc()
+    max_scratch = 64 << 20   # PA_DECODE_NOALLOC_MAX_SCRATCH
+    call = lambda S=1, Hq=8, mbs=4, ptok=0, flags=0: L.pa_decode_noalloc(
+        ctypes.byref(d), 16, ops.BF16, S, Hq, 16, mbs, 16, 0.1, 16, ptok, flags, None)
+    assert call(Hq=12) == -3                       # Hq % Hkv != 0
+    assert call(ptok=24) == -3                     # partition not a multiple of 16
+    assert call(flags=4) == -3                     # unknown flag
+    assert L.pa_decode_workspace_size(ctypes.byref(d), 64, 64, 2048, 16) > max_scratch
+    assert call(S=64, Hq=64, mbs=2048, ptok=16) == -5
+    assert b"static scratch" in L.pa_last_error()
+    assert L.pa_decode_noalloc(ctypes.byref(d), None, ops.BF16, 0, 8, None, 4, None, 0.1, None, 0,
+                               0, None) == 0       # zero sequences: nothing to do
+
+
 def test_decode_rejects_misaligned_out():
     L = ops.lib()
     d = desc()

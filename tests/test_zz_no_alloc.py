@@ -1,0 +1,84 @@
+"""pa_decode_noalloc, the decode entry point that allocates nothing (its
+split-K partials live in the library's static per-device scratch), against
+pa_decode_ex with a caller workspace: bit-identical outputs on two calls in
+a row, the second with a smaller input, so that the second call meets the
+first call's partials still in the scratch."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+from bitwise import assert_same_bytes
+from gpu_helpers import gpu_pool
+from paged_kv_cache_401_amd import ops
+from paged_kv_cache_401_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+MAX_SCRATCH = 64 << 20   # PA_DECODE_NOALLOC_MAX_SCRATCH in pa.h
+
+
+def _args(w):
+    dev = "cuda"
+    return (w.q.to(dev), torch.as_tensor(w.block_tables, dtype=torch.int32, device=dev),
+            torch.as_tensor(w.context_lens, dtype=torch.int32, device=dev))
+
+
+def _both(w, ptok, shared_kv=False):
+    pool = gpu_pool(w, fill=0xFF)
+    q, t, c = _args(w)
+    assert ops.decode_workspace_size(pool, w.S, w.Hq, w.max_blocks_per_seq, ptok) > 0
+    ref = ops.decode(pool, q, t, c, w.scale, partition_tokens=ptok, shared_kv=shared_kv)
+    out = torch.full((w.S, w.Hq, w.D), float("nan"), dtype=torch.float32, device="cuda")
+    ops.decode_noalloc(pool, q, t, c, w.scale, out, partition_tokens=ptok, shared_kv=shared_kv)
+    torch.cuda.synchronize()
+    return ref.cpu().numpy(), out.cpu().numpy()
+
+
+@pytest.mark.parametrize("name,ptok,seqs", [("fp8", 512, (5, 2)), ("mha13b", 64, (5, 3)),
+                                            ("gqa70b", 256, (3, 1)), ("sampling_b", 128, (2, 1))])
+def test_noalloc_equals_decode_ex_on_two_calls(name, ptok, seqs):
+    """Matrix-core (fp8, 64/8 heads; 70B-like; 40/8 heads) and vector-ALU
+    (13B-like) kernels with split-K partitions."""
+    for i, n in enumerate(seqs):
+        print("case %s ptok %d call %d: %d sequences" % (name, ptok, i, n), flush=True)
+        if name.startswith("sampling"):
+            w = wl.make_workload(name, small=True, num_seqs=n)
+        else:
+            w = wl.make_workload(name, small=True, num_seqs=n, seed=100 + i)
+        ref, out = _both(w, ptok, shared_kv=name.startswith("sampling"))
+        assert not np.isnan(out).any()
+        assert_same_bytes(out, ref, what="%s call %d" % (name, i))
+
+
+def test_noalloc_without_split_and_empty_batch():
+    """A batch that needs no partials, and an empty batch, through the same
+    entry point."""
+    w = wl.make_workload("gqa70b", small=True, num_seqs=2)
+    pool = gpu_pool(w)
+    q, t, c = _args(w)
+    ref = ops.decode(pool, q, t, c, w.scale, partition_tokens=4096)
+    out = torch.empty_like(ref)
+    ops.decode_noalloc(pool, q, t, c, w.scale, out, partition_tokens=4096)
+    torch.cuda.synchronize()
+    assert_same_bytes(out.cpu().numpy(), ref.cpu().numpy())
+    empty = torch.empty((0, w.Hq, w.D), dtype=torch.float32, device="cuda")
+    ops.decode_noalloc(pool, q[:0], t[:0], c[:0], w.scale, empty, partition_tokens=64)
+
+
+def test_noalloc_rejects_partials_beyond_the_scratch():
+    """Arguments whose partials exceed the static scratch are refused with
+    PA_ERR_WORKSPACE and nothing is enqueued."""
+    w = wl.make_workload("fp8", small=True, num_seqs=2)
+    pool = gpu_pool(w)
+    mbs = 2048
+    S = 64
+    need = ops.decode_workspace_size(pool, S, w.Hq, mbs, 16)
+    assert need > MAX_SCRATCH
+    L = ops.lib()
+    d = pool.desc()
+    rc = L.pa_decode_noalloc(ctypes.byref(d), 16, ops.BF16, S, w.Hq, 16, mbs, 16, 0.1, 16, 16, 0,
+                             None)
+    assert rc == -5 and b"static scratch" in L.pa_last_error()
+
