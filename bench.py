@@ -9,11 +9,15 @@ decode call itself with ``--append fused`` (pa_decode_append).  Inputs are
 synthetic and seeded and already resident in HBM when timing starts.
 
 Prints ONE JSON line.  ``value`` is KV-read GB/s over the whole step:
-algorithmic K+V bytes (sum of context lengths x KV heads x head dim x 2 x
-element bytes) divided by the step time.  ``roofline`` reports the decode
-partition kernel alone (HIP events recorded around that kernel on its
-stream) against the MI355X HBM peak of 8 TB/s.  ``cpu_baseline`` times the
-fp64 CPU oracle on a bounded sample of the same workload.
+algorithmic K+V bytes divided by the step time.  The algorithmic bytes are
+those of the distinct token slots the step reads (context tokens x KV heads x
+head dim x 2 x element bytes, a block shared by several sequences counted
+once); without shared blocks that is the sum over sequences.  ``roofline``
+reports the decode partition kernel alone (HIP events recorded around that
+kernel on its stream) against the MI355X HBM peak of 8 TB/s.
+``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the same
+workload.  The default run (the 70B-like layer) also times and checks the
+other decode configurations against the oracle (``configs``).
 """
 from __future__ import annotations
 
@@ -84,6 +88,9 @@ def parse():
     ap.add_argument("--cpu-seqs", type=int, default=None,
                     help="sequences in the CPU-oracle sample (default: ~10-30 s of CPU work)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="default workload: skip timing and checking the other decode "
+                         "configurations (the 'configs' record)")
     ap.add_argument("--graph", action="store_true",
                     help="decode workloads: also capture one step into a HIP graph and time its "
                          "replays (reported as graph_ms_per_step)")
@@ -166,22 +173,90 @@ def main():
     import numpy as np
     import torch
 
-    from paged_kv_cache_401_amd import ops
     from paged_kv_cache_401_amd import workloads as wl
 
-    dev = "cuda:0"
     torch.cuda.set_device(0)
     t0 = time.time()
-    w = wl.make_workload(args.workload, small=False, device=dev)
+    w = wl.make_workload(args.workload, small=False, device="cuda:0")
+    setup_s = time.time() - t0
     ptok = w.partition_tokens if args.partition_tokens is None else args.partition_tokens
+    r = decode_run(w, args.steps, args.warmup, ptok, args.append, graph=args.graph,
+                   flush_and_probe=True)
+    kv_bytes, uniq = w.kv_bytes(), w.unique_kv_bytes()
+    traffic = traffic_for(args.workload, r["kernel"], uniq)
+    rec = {
+        "metric": METRIC,
+        "value": round(uniq / (r["ms_per_step"] * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": DTYPE_NAME[w.pool_dtype],
+        "data": "synthetic (seeded N(0,1) q/K/V, scattered 16-token blocks)",
+        "config": {"workload": WORKLOAD_TEXT[args.workload], "num_seqs": w.S,
+                   "num_q_heads": w.Hq, "num_kv_heads": w.Hkv, "head_dim": w.D,
+                   "total_context_tokens": int(w.context_lens.sum()),
+                   "partition_tokens": r["partition_tokens"], "kv_bytes": kv_bytes,
+                   "unique_kv_bytes": uniq, "kv_loads": r["kv_loads"],
+                   "cache_write": r["cache_write"], "parallelism": "single GPU"},
+        "pct_hbm_peak_step": round(100.0 * uniq / (r["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+        "decode_seqs_per_s": round(w.S / (r["ms_per_step"] * 1e-3), 1),
+        "decode_kernel_ms": round(r["kernel_ms"], 5),
+        "decode_kernel_ms_min": round(float(np.min(r["kernel_ms_all"])), 5),
+        "decode_kernel_ms_p10_median_p90": [round(float(x), 5) for x in
+                                            np.percentile(r["kernel_ms_all"], [10, 50, 90])],
+        "wall_ms_per_step": round(r["wall_ms_per_step"], 5),
+        "logical_kv_GBps": round(kv_bytes / (r["kernel_ms"] * 1e-3) / 1e9, 2),
+    }
+    rec.update(r["extra"])
+    if "read_probe_GBps" in rec:
+        rec["decode_pct_of_read_probe"] = round(
+            100.0 * uniq / (r["kernel_ms"] * 1e-3) / 1e9 / rec["read_probe_GBps"], 2)
+    rec["roofline"] = {"bound": "hbm", "achieved": round(uniq / (r["kernel_ms"] * 1e-3) / 1e9, 2),
+                       "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                       "frac": round(uniq / (r["kernel_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                       "traffic": traffic, "kernel": r["kernel"],
+                       "algorithmic_bytes_per_launch": uniq,
+                       "bytes_note": "K+V bytes of the distinct token slots one launch reads "
+                                     "(blocks shared by several sequences counted once)"}
+    rec["setup_s"] = round(setup_s, 2)
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"], rec["max_abs_err_vs_oracle_sample"] = cpu_baseline(
+            w, args, r["out"], r["pool"])
+    if args.workload == "gqa70b" and not args.no_configs:
+        del r
+        torch.cuda.empty_cache()
+        rec["configs"] = other_configs(args)
+    print(json.dumps(rec), flush=True)
+
+
+def decode_run(w, steps, warmup, ptok, append="separate", graph=False, flush_and_probe=False):
+    """Time `steps` decode steps of workload `w` after `warmup` untimed ones.
+    A step: the copy-on-write copies of the workload's last step (beam search;
+    none otherwise), the cache write of every sequence's newest token (before
+    the decode call, or inside it with append="fused"), and the decode call
+    (partition kernel + split-K reduce).  HIP events on the launch stream
+    bracket the whole timed region and, every step, the partition kernel."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_401_amd import ops
+
+    dev = "cuda:0"
     pool = ops.KVPool(w.num_blocks, w.Hkv, w.D, w.pool_dtype, device=dev, k_scale=w.k_scale,
                       v_scale=w.v_scale, fill=0)
+    cow_pairs = None
     for op in w.ops:
         if op[0] == "write":
-            ops.reshape_and_cache(pool, op[1], op[2],
+            ops.reshape_and_cache(pool, op[1].to(dev), op[2].to(dev),
                                   torch.as_tensor(op[3], dtype=torch.int32, device=dev))
         else:
-            ops.copy_blocks(pool, torch.as_tensor(op[1], dtype=torch.int32, device=dev))
+            cow_pairs = torch.as_tensor(op[1], dtype=torch.int32, device=dev)
+            ops.copy_blocks(pool, cow_pairs)
     q = w.q.to(dev)
     tables = torch.as_tensor(w.block_tables, dtype=torch.int32, device=dev)
     ctx = torch.as_tensor(w.context_lens, dtype=torch.int32, device=dev)
@@ -200,18 +275,18 @@ def main():
     step_pairs = torch.as_tensor(np.zeros((0, 2), np.int32) if sp is None else sp,
                                  dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
-    setup_s = time.time() - t0
 
     # blocks shared across sequences (prompts, beams): cached rather than streaming loads
     shared = bool(w.info.get("shared_kv", False))
-
-    # The step's new tokens are each sequence's last position: with --append
-    # fused the decode call writes them itself (pa_decode_append).
-    fused = args.append == "fused" and step_slots is not None
+    # The step's new tokens are each sequence's last position: with fused
+    # appends the decode call writes them itself (pa_decode_append).
+    fused = append == "fused" and step_slots is not None
     if fused:
         last = np.array([int(w.block_tables[s][(c - 1) // 16]) * 16 + (c - 1) % 16
                          for s, c in enumerate(w.context_lens)], np.int32)
-        assert np.array_equal(last, w.step_slots), "step tokens are not the last positions"
+        if not np.array_equal(last, w.step_slots):
+            raise SystemExit("--append fused needs every sequence's newest token at its last "
+                             "position, in a block of its own")
     new_kv = dict(k_new=step_k, v_new=step_v) if fused else {}
     write_first = step_slots is not None and not fused
 
@@ -222,14 +297,14 @@ def main():
         ops.decode(pool, q, tables, ctx, w.scale, out=out, partition_tokens=ptok,
                    workspace=ws, shared_kv=shared, **new_kv)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
 
     # timed region: exactly `steps` steps, HIP events on the stream around the
     # decode partition kernel of every step, wall clock around the whole
     stream = torch.cuda.current_stream()
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
     for e in evs:  # materialise the HIP events before handing them to the library
         e.record(stream)
     step_begin = torch.cuda.Event(enable_timing=True)
@@ -237,7 +312,7 @@ def main():
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     step_begin.record(stream)
-    for i in range(args.steps):
+    for i in range(steps):
         ops.copy_blocks(pool, step_pairs)
         if write_first:
             ops.reshape_and_cache(pool, step_k, step_v, step_slots)
@@ -247,55 +322,76 @@ def main():
     step_end.record(stream)
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - wall0
-    gpu_ms = step_begin.elapsed_time(step_end)
-    kern_ms = [evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(args.steps)]
+    kern_ms = [evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(steps)]
+    res = {"pool": pool, "out": out, "kernel": ops.decode_variant(pool, w.Hq),
+           "partition_tokens": ptok_used, "ms_per_step": step_begin.elapsed_time(step_end) / steps,
+           "wall_ms_per_step": 1e3 * wall_s / steps, "kernel_ms": float(np.mean(kern_ms)),
+           "kernel_ms_all": kern_ms,
+           "kv_loads": "cached (shared blocks)" if shared else "non-temporal",
+           "cache_write": ("none" if step_slots is None else
+                           "in the decode call" if fused else "separate kernel"),
+           "extra": {}}
 
-    ms_per_step = gpu_ms / args.steps
-    kv_bytes = w.kv_bytes()
-    kern_avg_ms = float(np.mean(kern_ms))
-    achieved = kv_bytes / (kern_avg_ms * 1e-3) / 1e9
-    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
-    kernel_name = ops.decode_variant(pool, w.Hq)
-    traffic = traffic_for(args.workload, kernel_name, kv_bytes)
-
-    copy_rec = None
-    if step_pairs.shape[0]:
-        # the copy-on-write kernel alone: read + write bytes of K and V blocks
+    def time_copies(pairs, label):
+        """The copy-on-write kernel alone on `pairs`: read + write bytes of K
+        and V blocks (a copy leaves its source unchanged, so repeats are
+        idempotent)."""
         cb, ce = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ops.copy_blocks(pool, pairs)
         cb.record(stream)
-        for _ in range(args.steps):
-            ops.copy_blocks(pool, step_pairs)
+        for _ in range(steps):
+            ops.copy_blocks(pool, pairs)
         ce.record(stream)
         torch.cuda.synchronize()
-        copy_ms = cb.elapsed_time(ce) / args.steps
+        copy_ms = cb.elapsed_time(ce) / steps
         block_bytes = pool.nbytes // w.num_blocks
-        moved = 2 * 2 * int(step_pairs.shape[0]) * block_bytes
-        copy_rec = {"pairs": int(step_pairs.shape[0]), "block_bytes_per_pool": block_bytes,
-                    "ms": round(copy_ms, 5), "read_plus_write_GBps": round(moved / copy_ms / 1e6, 1)}
+        moved = 2 * 2 * int(pairs.shape[0]) * block_bytes
+        return {"pairs": int(pairs.shape[0]), "what": label, "block_bytes_per_pool": block_bytes,
+                "ms": round(copy_ms, 5), "read_plus_write_GBps": round(moved / copy_ms / 1e6, 1)}
 
-    # The same decode call once more per step with a 1 GiB read before each
-    # launch (untimed, outside the contract's timed steps): afterwards the
-    # 256 MB MALL holds clean lines of another buffer and nothing of the
-    # pool, so the kernel reads every byte from HBM.  (A 1 GiB write instead
-    # leaves dirty lines whose write-back then slows the decode itself.)
-    # Back-to-back steps above let a pool not much larger than the MALL, or
-    # blocks shared across steps, find part of themselves there.
+    if step_pairs.shape[0]:
+        res["extra"]["copy_blocks"] = time_copies(step_pairs, "the step's copy-on-write pairs")
+    elif cow_pairs is not None and cow_pairs.shape[0]:
+        res["extra"]["copy_blocks"] = time_copies(
+            cow_pairs, "the fork's copy-on-write pairs (shared partial prompt blocks)")
+    if graph:
+        res["extra"]["graph"] = graph_step_time(step, steps, w.S)
+    if flush_and_probe:
+        res["extra"].update(flushed_and_probe(w, pool, q, tables, ctx, out, ptok, ws, shared,
+                                              new_kv, steps))
+    return res
+
+
+def flushed_and_probe(w, pool, q, tables, ctx, out, ptok, ws, shared, new_kv, steps):
+    """The same decode call once more per step with a 1 GiB read before each
+    launch (untimed, outside the timed steps): afterwards the 256 MB MALL
+    holds clean lines of another buffer and nothing of the pool, so the
+    kernel reads every byte from HBM.  (A 1 GiB write instead leaves dirty
+    lines whose write-back then slows the decode itself.)  Back-to-back steps
+    let a pool not much larger than the MALL, or blocks shared across steps,
+    find part of themselves there.  Then the read bandwidth this GPU
+    sustains on a plain streaming read of the K pool."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_401_amd import ops
+
+    dev = "cuda:0"
+    stream = torch.cuda.current_stream()
     flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
     flush.sum()
     flush.sum()
-    fl_evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+    fl_evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
     for e in fl_evs:
         e.record(stream)
-    for i in range(args.steps):
+    for i in range(steps):
         flush.sum()
         ops.set_profile_events(fl_evs[2 * i], fl_evs[2 * i + 1])
         ops.decode(pool, q, tables, ctx, w.scale, out=out, partition_tokens=ptok, workspace=ws,
                    shared_kv=shared, **new_kv)
     torch.cuda.synchronize()
-    flushed_ms = [fl_evs[2 * i].elapsed_time(fl_evs[2 * i + 1]) for i in range(args.steps)]
+    flushed_ms = [fl_evs[2 * i].elapsed_time(fl_evs[2 * i + 1]) for i in range(steps)]
     del flush
-
-    # the read bandwidth this GPU sustains on a plain streaming read of the K pool
     sink = torch.zeros(16, dtype=torch.uint8, device=dev)
     for _ in range(3):
         ops.probe_read(pool.k, sink)
@@ -306,54 +402,93 @@ def main():
     pe.record(stream)
     torch.cuda.synchronize()
     probe_gbps = pool.k.numel() / (pb.elapsed_time(pe) / 10 * 1e-3) / 1e9
+    med = float(np.median(flushed_ms))
+    uniq = w.unique_kv_bytes()
+    return {"decode_kernel_ms_after_1GiB_read_p10_median_p90":
+                [round(float(x), 5) for x in np.percentile(flushed_ms, [10, 50, 90])],
+            "pct_hbm_peak_after_1GiB_read": round(100.0 * uniq / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+            "read_probe_GBps": round(probe_gbps, 1)}
 
-    rec = {
-        "metric": METRIC,
-        "value": round(value, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": DTYPE_NAME[w.pool_dtype],
-        "data": "synthetic (seeded N(0,1) q/K/V, scattered 16-token blocks)",
-        "config": {"workload": WORKLOAD_TEXT[args.workload], "num_seqs": w.S,
-                   "num_q_heads": w.Hq, "num_kv_heads": w.Hkv, "head_dim": w.D,
-                   "total_context_tokens": int(w.context_lens.sum()),
-                   "partition_tokens": ptok_used, "kv_bytes": kv_bytes,
-                   "kv_loads": "cached (shared blocks)" if shared else "non-temporal",
-                   "cache_write": ("none" if step_slots is None else
-                                   "in the decode call" if fused else "separate kernel"),
-                   "parallelism": "single GPU"},
-        "pct_hbm_peak_step": round(100.0 * value / HBM_PEAK_GBPS, 2),
-        "decode_seqs_per_s": round(w.S / (ms_per_step * 1e-3), 1),
-        "decode_kernel_ms": round(kern_avg_ms, 5),
-        "decode_kernel_ms_min": round(float(np.min(kern_ms)), 5),
-        "decode_kernel_ms_p10_median_p90": [round(float(x), 5) for x in np.percentile(kern_ms, [10, 50, 90])],
-        "decode_kernel_ms_after_1GiB_read_p10_median_p90": [round(float(x), 5) for x in
-                                                              np.percentile(flushed_ms, [10, 50, 90])],
-        "wall_ms_per_step": round(1e3 * wall_s / args.steps, 5),
-        "unique_kv_bytes": w.unique_kv_bytes(),
-        "decode_unique_GBps": round(w.unique_kv_bytes() / (kern_avg_ms * 1e-3) / 1e9, 2),
-        "read_probe_GBps": round(probe_gbps, 1),
-        "decode_pct_of_read_probe": round(100.0 * achieved / probe_gbps, 2),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "kernel": kernel_name,
-                     "algorithmic_bytes_per_launch": kv_bytes},
-        "setup_s": round(setup_s, 2),
-    }
-    if copy_rec is not None:
-        rec["copy_blocks"] = copy_rec
-    if args.graph:
-        rec["graph"] = graph_step_time(step, args.steps, w.S)
-    if not args.no_cpu_baseline:
-        rec["cpu_baseline"], rec["max_abs_err_vs_oracle_sample"] = cpu_baseline(
-            w, args, out, pool)
-    print(json.dumps(rec), flush=True)
+
+# The other decode configurations, timed and checked in the default run.
+CONFIG_RUNS = ("tiny", "mha13b", "sampling_a", "sampling_b", "fp8")
+
+
+def other_configs(args):
+    """Each other decode configuration once more, at full size: step and
+    partition-kernel times, GB/s on logical and on unique KV bytes (the
+    roofline fraction on unique bytes), and the max abs error against the
+    fp64 oracle on sampled sequences (every query head)."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_401_amd import workloads as wl
+
+    recs = {}
+    steps, warmup = max(5, args.steps // 2), max(2, args.warmup // 2)
+    for name in CONFIG_RUNS:
+        t0 = time.time()
+        w = wl.make_workload(name, small=False, device="cuda:0")
+        r = decode_run(w, steps, warmup, w.partition_tokens, "separate")
+        kv, uniq = w.kv_bytes(), w.unique_kv_bytes()
+        ctxs = w.context_lens
+        seqs = sorted({0, w.S - 1, int(np.argmax(ctxs)), int(np.argmin(ctxs)), w.S // 2})
+        err = sampled_error(w, r["out"], seqs)
+        rec = {"workload": WORKLOAD_TEXT[name], "dtype": DTYPE_NAME[w.pool_dtype],
+               "num_seqs": w.S, "steps": steps, "warmup": warmup,
+               "partition_tokens": r["partition_tokens"], "kernel": r["kernel"],
+               "kv_loads": r["kv_loads"], "cache_write": r["cache_write"],
+               "ms_per_step": round(r["ms_per_step"], 5),
+               "decode_kernel_ms": round(r["kernel_ms"], 5),
+               "decode_seqs_per_s": round(w.S / (r["ms_per_step"] * 1e-3), 1),
+               "kv_bytes": kv, "unique_kv_bytes": uniq,
+               "logical_kv_GBps": round(kv / (r["kernel_ms"] * 1e-3) / 1e9, 2),
+               "unique_kv_GBps": round(uniq / (r["kernel_ms"] * 1e-3) / 1e9, 2),
+               "roofline_frac": round(uniq / (r["kernel_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+               "step_unique_GBps": round(uniq / (r["ms_per_step"] * 1e-3) / 1e9, 2),
+               "max_abs_err_vs_oracle": err,
+               "oracle_rows": "sequences %s, every query head" % seqs,
+               "setup_s": round(time.time() - t0, 2)}
+        rec.update(r["extra"])
+        recs[name] = rec
+        del r, w
+        torch.cuda.empty_cache()
+    return recs
+
+
+def sampled_error(w, gpu_out, seqs):
+    """Max abs error of the GPU rows of `seqs` (every query head) against the
+    fp64 oracle, on an oracle pool holding what those rows read."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from paged_kv_cache_401_amd.workloads import raw_numpy
+
+    kp = oracle.new_pool(w.num_blocks, w.Hkv, w.D, w.pool_dtype)
+    vp = oracle.new_pool(w.num_blocks, w.Hkv, w.D, w.pool_dtype)
+    if len(w.ops) > 1:      # shared prompts: the whole cache history
+        for op in w.ops:
+            if op[0] == "write":
+                oracle.reshape_and_cache(kp, vp, w.pool_dtype, w.num_blocks, w.Hkv, w.D,
+                                         raw_numpy(op[1]), raw_numpy(op[2]), w.kv_in_dtype, op[3],
+                                         w.k_scale, w.v_scale)
+            else:
+                oracle.copy_blocks(kp, vp, w.pool_dtype, w.Hkv, w.D, op[1])
+    else:                   # independent sequences: only theirs
+        _, k, v, slots = w.ops[0]
+        off = np.concatenate([[0], np.cumsum(w.context_lens.astype(np.int64))])
+        idx = np.concatenate([np.arange(off[s], off[s + 1]) for s in seqs])
+        it = torch.as_tensor(idx, device=k.device)
+        oracle.reshape_and_cache(kp, vp, w.pool_dtype, w.num_blocks, w.Hkv, w.D,
+                                 raw_numpy(k.index_select(0, it)), raw_numpy(v.index_select(0, it)),
+                                 w.kv_in_dtype, slots[idx], w.k_scale, w.v_scale)
+    rows = [(s, h) for s in seqs for h in range(w.Hq)]
+    ref = oracle.paged_attention(kp, vp, w.pool_dtype, w.Hkv, w.D, raw_numpy(w.q), w.q_dtype,
+                                 w.S, w.Hq, w.block_tables, w.context_lens, w.scale, w.k_scale,
+                                 w.v_scale, rows=rows, threads=len(os.sched_getaffinity(0)))
+    got = gpu_out.cpu().numpy()[seqs].reshape(-1, w.D).astype(np.float64)
+    return float(np.max(np.abs(got - ref)))
 
 
 def graph_step_time(step, steps, num_seqs):

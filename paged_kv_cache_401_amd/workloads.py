@@ -498,9 +498,18 @@ def _sampling(name, small, device, seed, rng, num_prompts=None) -> Workload:
     seqs = [(p, j) for p in range(P) for j in range(n)]
     ctx = np.asarray([mgr.length(s) for s in seqs], dtype=np.int32)
     tables = _tables_from(mgr, seqs)
+    # a decode step's cache write: each sample's newest token, where it is a
+    # private one (a sample with no private token yet would write into the
+    # shared prompt block, which its next step copies first: slot -1 here)
+    last = np.cumsum(cont.ravel()) - 1
+    has = cont.ravel() > 0
+    step_slots = np.where(has, np.asarray(cslots + [-1], np.int32)[np.where(has, last, Nc)], -1)
+    li = torch.as_tensor(np.where(has, last, 0), device=kc.device)
+    step_k, step_v = (kc.index_select(0, li), vc.index_select(0, li)) if Nc else (None, None)
     w = Workload(name=name, S=P * n, Hq=Hq, Hkv=Hkv, D=D, pool_dtype=BF16, q_dtype=BF16,
                  kv_in_dtype=BF16, num_blocks=nb, context_lens=ctx, block_tables=tables, q=q,
-                 scale=_f32(1.0 / math.sqrt(D)), ops=ops)
+                 scale=_f32(1.0 / math.sqrt(D)), ops=ops, step_k=step_k, step_v=step_v,
+                 step_slots=step_slots.astype(np.int32) if Nc else None)
     w.info.update(shared_kv=True, manager=mgr, prompt_len=prompt, continuation=cont,
                   shared_prompt_blocks=shared_blocks,
                   physical_blocks=mgr.physical_blocks_in_use(),

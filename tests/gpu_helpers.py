@@ -19,13 +19,18 @@ def gpu_pool(w, fill=0, device="cuda"):
     return pool
 
 
-def gpu_decode(w, pool, partition_tokens=None, q=None, ctx=None, tables=None, device="cuda"):
+def gpu_decode(w, pool, partition_tokens=None, q=None, ctx=None, tables=None, device="cuda",
+               shared_kv=None):
+    """Decode through the C ABI in the launch configuration bench.py uses for
+    the workload: its partition size and, for batches whose sequences share
+    blocks, cached K/V loads (PA_DECODE_SHARED_KV)."""
     q = (w.q if q is None else q).to(device)
     t = torch.as_tensor(w.block_tables if tables is None else tables, dtype=torch.int32,
                         device=device)
     c = torch.as_tensor(w.context_lens if ctx is None else ctx, dtype=torch.int32, device=device)
     pt = w.partition_tokens if partition_tokens is None else partition_tokens
-    out = ops.decode(pool, q, t, c, w.scale, partition_tokens=pt)
+    shared = bool(w.info.get("shared_kv", False)) if shared_kv is None else shared_kv
+    out = ops.decode(pool, q, t, c, w.scale, partition_tokens=pt, shared_kv=shared)
     torch.cuda.synchronize()
     return out.cpu().numpy().astype(np.float64)
 

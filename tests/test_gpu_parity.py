@@ -384,7 +384,7 @@ def _sampled_rows(w, seqs):
     return [(s, h) for s in seqs for h in range(w.Hq)]
 
 
-@pytest.mark.parametrize("name", ["mha13b", "gqa70b", "fp8", "sampling_b"])
+@pytest.mark.parametrize("name", ["mha13b", "gqa70b", "fp8", "sampling_a", "sampling_b"])
 def test_full_size_sampled_rows(name):
     """The full-size workload in the launch configuration the benchmark uses,
     checked on sampled sequences (every head) against the oracle, and pool
