@@ -120,6 +120,62 @@ def copy_probe(nbytes: int, steps: int) -> None:
                       "read_plus_write_GBps": round(2 * src.numel() * 4 / dt / 1e9, 1)}), flush=True)
 
 
+class KernelTimer:
+    """HIP timing events for the partition kernel of every timed step, created
+    with a device-scope release (hipEventReleaseToDevice, the form HIP offers
+    for timing commands between events; timing needs no system-scope release
+    and its cache write-back).  The library has the kernel's dispatch record
+    them (pa_set_profile_events).  The events come from the HIP runtime this
+    process already runs (loaded by torch, shared with libpa.so)."""
+
+    RELEASE_TO_DEVICE = 0x40000000
+
+    def __init__(self, n: int):
+        import ctypes
+        path = None
+        for ln in open("/proc/self/maps"):
+            if "libamdhip64.so" in ln:
+                path = ln.split()[-1]
+                break
+        if path is None:
+            raise RuntimeError("the HIP runtime is not loaded")
+        self.hip = ctypes.CDLL(path)
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.events = []
+        for _ in range(2 * n):
+            ev = ctypes.c_void_p()
+            rc = self.hip.hipEventCreateWithFlags(ctypes.byref(ev), self.RELEASE_TO_DEVICE)
+            if rc != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed (%d)" % rc)
+            self.events.append(ev.value)
+
+    def pair(self, i):
+        return self.events[2 * i], self.events[2 * i + 1]
+
+    def record(self, k, stream):
+        """Record event k (of 2 n) on `stream` (a torch stream)."""
+        rc = self.hip.hipEventRecord(self.events[k], stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError("hipEventRecord failed (%d)" % rc)
+
+    def elapsed_ms(self, i) -> float:
+        import ctypes
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), *self.pair(i))
+        if rc != 0:
+            raise RuntimeError("hipEventElapsedTime failed (%d)" % rc)
+        return float(ms.value)
+
+    def close(self):
+        for ev in self.events:
+            self.hip.hipEventDestroy(ev)
+        self.events = []
+
+
 def source_digest() -> str:
     """Digest of the code (comments and blank lines dropped) and compile flags
     the matrix-core decode kernel is built from."""
@@ -301,12 +357,10 @@ def decode_run(w, steps, warmup, ptok, append="separate", graph=False, flush_and
         step()
     torch.cuda.synchronize()
 
-    # timed region: exactly `steps` steps, HIP events on the stream around the
+    # timed region: exactly `steps` steps, HIP events on the stream timing the
     # decode partition kernel of every step, wall clock around the whole
     stream = torch.cuda.current_stream()
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
-    for e in evs:  # materialise the HIP events before handing them to the library
-        e.record(stream)
+    timer = KernelTimer(steps)
     step_begin = torch.cuda.Event(enable_timing=True)
     step_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -316,13 +370,14 @@ def decode_run(w, steps, warmup, ptok, append="separate", graph=False, flush_and
         ops.copy_blocks(pool, step_pairs)
         if write_first:
             ops.reshape_and_cache(pool, step_k, step_v, step_slots)
-        ops.set_profile_events(evs[2 * i], evs[2 * i + 1])
+        ops.set_profile_events(*timer.pair(i))
         ops.decode(pool, q, tables, ctx, w.scale, out=out, partition_tokens=ptok, workspace=ws,
                    shared_kv=shared, **new_kv)
     step_end.record(stream)
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - wall0
-    kern_ms = [evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(steps)]
+    kern_ms = [timer.elapsed_ms(i) for i in range(steps)]
+    timer.close()
     res = {"pool": pool, "out": out, "kernel": ops.decode_variant(pool, w.Hq),
            "partition_tokens": ptok_used, "ms_per_step": step_begin.elapsed_time(step_end) / steps,
            "wall_ms_per_step": 1e3 * wall_s / steps, "kernel_ms": float(np.mean(kern_ms)),
@@ -381,16 +436,15 @@ def flushed_and_probe(w, pool, q, tables, ctx, out, ptok, ws, shared, new_kv, st
     flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
     flush.sum()
     flush.sum()
-    fl_evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
-    for e in fl_evs:
-        e.record(stream)
+    timer = KernelTimer(steps)
     for i in range(steps):
         flush.sum()
-        ops.set_profile_events(fl_evs[2 * i], fl_evs[2 * i + 1])
+        ops.set_profile_events(*timer.pair(i))
         ops.decode(pool, q, tables, ctx, w.scale, out=out, partition_tokens=ptok, workspace=ws,
                    shared_kv=shared, **new_kv)
     torch.cuda.synchronize()
-    flushed_ms = [fl_evs[2 * i].elapsed_time(fl_evs[2 * i + 1]) for i in range(steps)]
+    flushed_ms = [timer.elapsed_ms(i) for i in range(steps)]
+    timer.close()
     del flush
     sink = torch.zeros(16, dtype=torch.uint8, device=dev)
     for _ in range(3):
@@ -562,22 +616,21 @@ def run_prefill(args):
         ops.prefill(pool, q, qs, mql, bt, ctx, w.scale, out=out)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
-    for e in evs:
-        e.record(stream)
+    timer = KernelTimer(args.steps)
     b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     b0.record(stream)
     for i in range(args.steps):
         ops.reshape_and_cache(pool, ck, cv, cslots)
-        ops.set_profile_events(evs[2 * i], evs[2 * i + 1])
+        ops.set_profile_events(*timer.pair(i))
         ops.prefill(pool, q, qs, mql, bt, ctx, w.scale, out=out)
     b1.record(stream)
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - wall0
     ms_step = b0.elapsed_time(b1) / args.steps
-    kern = [evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(args.steps)]
+    kern = [timer.elapsed_ms(i) for i in range(args.steps)]
+    timer.close()
     kern_ms = float(np.mean(kern))
     flops = w.prefill_flops()
     achieved = flops / (kern_ms * 1e-3) / 1e12
@@ -650,19 +703,18 @@ def run_prefix(args):
             step()
         torch.cuda.synchronize()
         stream = torch.cuda.current_stream()
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
-        for e in evs:  # materialise the HIP events before handing them to the library
-            e.record(stream)
+        timer = KernelTimer(args.steps)
         b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         b0.record(stream)
         for i in range(args.steps):
             ops.reshape_and_cache(pool, k, v, slots_t)
-            ops.set_profile_events(evs[2 * i], evs[2 * i + 1])
+            ops.set_profile_events(*timer.pair(i))
             ops.prefill(pool, w.prefill_q, qs, mql, bt, ctx, w.scale, out=out)
         b1.record(stream)
         torch.cuda.synchronize()
-        kern = float(np.mean([evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(args.steps)]))
+        kern = float(np.mean([timer.elapsed_ms(i) for i in range(args.steps)]))
+        timer.close()
         runs[caching] = (w, b0.elapsed_time(b1) / args.steps, kern)
     w, ms, kern = runs[True]
     w0, ms0, _ = runs[False]
@@ -723,15 +775,16 @@ def run_fill(args):
     for _ in range(args.warmup):
         ops.reshape_and_cache(pool, k, v, st)
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+    timer = KernelTimer(args.steps)
     t0 = time.perf_counter()
     for i in range(args.steps):
-        ev[2 * i].record(stream)
+        timer.record(2 * i, stream)
         ops.reshape_and_cache(pool, k, v, st)
-        ev[2 * i + 1].record(stream)
+        timer.record(2 * i + 1, stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / args.steps
-    ms = float(np.mean([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(args.steps)]))
+    ms = float(np.mean([timer.elapsed_ms(i) for i in range(args.steps)]))
+    timer.close()
     gbps = nbytes / ms / 1e6
     rec = {
         "metric": "pa_reshape_and_cache bulk GB/s (K/V read + pool written) at 1 MI355X",

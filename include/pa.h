@@ -375,9 +375,10 @@ int pa_set_debug(int on);
 int pa_decode_variant(const pa_pool_t *pool, int32_t num_q_heads);
 
 /* Measurement aid: the next pa_decode or pa_prefill call on this host
- * thread records `before` (a hipEvent_t) just before its partition (or
- * prefill) kernel and `after` just after it, on the call's stream.  Pass
- * NULLs to clear. */
+ * thread stores its partition (or prefill) kernel's start time in `before`
+ * and its end time in `after` (hipEvent_t; hipEventElapsedTime gives the
+ * kernel's duration).  The kernel is launched with hipExtLaunchKernel, whose
+ * dispatch records the two events itself.  Pass NULLs to clear. */
 int pa_set_profile_events(void *before, void *after);
 
 /* Measurement aid: enqueue one streaming read of `bytes` bytes (rounded down

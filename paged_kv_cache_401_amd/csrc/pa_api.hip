@@ -86,17 +86,27 @@ int32_t simd_count() {
     return v;
 }
 
-// Wavefronts per workgroup of the grouped (matrix-core) kernel.  One
-// wavefront walks all of a partition's blocks and needs no merge; four split
-// them and keep four times the loads in flight per (sequence, KV head).  One
-// is faster when partitions are short (<= 512 tokens: fp8 long tail 0.196 ->
-// 0.182 ms against two) and when the batch alone has at least two rows per
-// SIMD, so that one wavefront per row still fills the chip (70B-like batch,
-// 2048 rows: 0.660 -> 0.653 ms; beam search 0.141 -> 0.135 ms); with fewer
-// rows four are faster (parallel sampling, 1536 rows: 0.105 against 0.115).
-bool one_wave(int32_t num_seqs, int32_t num_kv_heads, int32_t max_partitions, int32_t ptok) {
-    if (max_partitions > 1 && ptok <= 512) return true;
-    return (int64_t)num_seqs * num_kv_heads >= 2 * (int64_t)simd_count();
+// How the grouped (matrix-core) kernel maps work to wavefronts (unused by
+// the vector-ALU kernel).  Short split-K partitions (<= 512 tokens) go to
+// partition groups: one wavefront per partition, kGroupParts partitions of
+// a row per workgroup merged on chip, so a partial result per group instead
+// of one per partition reaches memory (the stores that end a work item cost
+// far more than their bytes while the chip streams K/V).  Otherwise one
+// wavefront walks all of a partition's blocks and needs no merge; it is
+// faster when the batch alone has at least two rows per SIMD, so that one
+// wavefront per row still fills the chip (70B-like batch, 2048 rows: 0.660
+// -> 0.653 ms; beam search 0.141 -> 0.135 ms); with fewer rows four
+// wavefronts per partition keep more loads in flight (parallel sampling,
+// 1536 rows: 0.105 against 0.115).
+int wave_mode(const pa_pool_t *pool, int32_t num_seqs, int32_t num_q_heads, int32_t raw_partitions,
+              int32_t ptok) {
+    if (raw_partitions > 1 && ptok <= 512) return pa::kPartGroups;
+    return (int64_t)num_seqs * pool->num_kv_heads >= 2 * (int64_t)simd_count() ? pa::kOneWave
+                                                                                : pa::kFourWaves;
+}
+
+bool grouped_kernel(const pa_pool_t *pool, int32_t num_q_heads) {
+    return pa::mfma_path_supported(pool->kv_dtype, pool->head_dim, num_q_heads / pool->num_kv_heads);
 }
 
 int32_t auto_partition(const pa_pool_t *pool, int32_t num_seqs, int32_t num_q_heads,
@@ -132,10 +142,31 @@ int check_heads(const pa_pool_t *pool, int32_t num_seqs, int32_t num_q_heads,
     return PA_OK;
 }
 
+// Partial results per row, the partitions merged into each (group_parts) and
+// the grouped kernel's wave mode for these arguments; the workspace holds
+// the partials.
+struct Split {
+    int32_t slots, group_parts, mode;
+};
+
+Split split_for(const pa_pool_t *pool, int32_t num_seqs, int32_t num_q_heads,
+                int32_t max_blocks_per_seq, int32_t ptok) {
+    const int64_t max_tokens = (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE;
+    const int32_t raw = (int32_t)((max_tokens + ptok - 1) / ptok);
+    Split sp{raw, 1, pa::kFourWaves};
+    if (grouped_kernel(pool, num_q_heads)) {
+        sp.mode = wave_mode(pool, num_seqs, num_q_heads, raw, ptok);
+        if (sp.mode == pa::kPartGroups) {
+            sp.group_parts = pa::kGroupParts;
+            sp.slots = (raw + pa::kGroupParts - 1) / pa::kGroupParts;
+        }
+    }
+    return sp;
+}
+
 size_t workspace_for(const pa_pool_t *pool, int32_t num_seqs, int32_t num_q_heads,
                      int32_t max_blocks_per_seq, int32_t ptok, int32_t *nparts_out) {
-    const int64_t max_tokens = (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE;
-    const int64_t np = (max_tokens + ptok - 1) / ptok;
+    const int64_t np = split_for(pool, num_seqs, num_q_heads, max_blocks_per_seq, ptok).slots;
     if (nparts_out) *nparts_out = (int32_t)np;
     if (np <= 1) return 0;
     const int64_t rows = (int64_t)num_seqs * num_q_heads * np;
@@ -357,9 +388,11 @@ int decode_impl(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t n
     p.group = num_q_heads / pool->num_kv_heads;
     p.num_seqs = num_seqs;
     p.max_blocks_per_seq = max_blocks_per_seq;
+    const Split sp = split_for(pool, num_seqs, num_q_heads, max_blocks_per_seq, ptok);
     p.partition_tokens = ptok;
-    p.max_partitions = np;
-    p.one_wave = one_wave(num_seqs, pool->num_kv_heads, np, ptok) ? 1 : 0;
+    p.group_parts = sp.group_parts;
+    p.max_partitions = sp.slots;
+    p.wave_mode = sp.mode;
     const double kscale = pool->kv_dtype == PA_FP8_E4M3 ? (double)pool->k_scale : 1.0;
     p.qk_scale_log2 = (float)((double)scale * kscale * 1.4426950408889634);
     p.out_scale = pool->kv_dtype == PA_FP8_E4M3 ? pool->v_scale : 1.0f;
@@ -409,18 +442,11 @@ int decode_impl(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t n
         if (e != hipSuccess) return fail(PA_ERR_HIP, "append kernel: %s", hipGetErrorString(e));
         p.k_new = p.v_new = nullptr;
     }
-    if (g_ev_before) {
-        hipError_t e = hipEventRecord(g_ev_before, st);
-        if (e != hipSuccess) return fail(PA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
-    }
-    hipError_t e = mfma ? pa::launch_decode_mfma(pool->kv_dtype, pool->head_dim, p, st)
-                        : pa::launch_decode_valu(pool->kv_dtype, pool->head_dim, p, st);
-    if (e != hipSuccess) return fail(PA_ERR_HIP, "decode partition kernel: %s", hipGetErrorString(e));
-    if (g_ev_after) {
-        e = hipEventRecord(g_ev_after, st);
-        if (e != hipSuccess) return fail(PA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
-    }
+    const pa::LaunchEvents ev{g_ev_before, g_ev_after};
     g_ev_before = g_ev_after = nullptr;
+    hipError_t e = mfma ? pa::launch_decode_mfma(pool->kv_dtype, pool->head_dim, p, st, &ev)
+                        : pa::launch_decode_valu(pool->kv_dtype, pool->head_dim, p, st, &ev);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "decode partition kernel: %s", hipGetErrorString(e));
     if (np > 1) {
         e = pa::launch_decode_reduce(pool->head_dim, p, st);
         if (e != hipSuccess) return fail(PA_ERR_HIP, "decode reduce kernel: %s", hipGetErrorString(e));
@@ -534,17 +560,10 @@ int pa_prefill(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t nu
             });
         if (rc != PA_OK) return rc;
     }
-    if (g_ev_before) {
-        hipError_t e = hipEventRecord(g_ev_before, st);
-        if (e != hipSuccess) return fail(PA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
-    }
-    hipError_t e = pa::launch_prefill(pool->kv_dtype, pool->head_dim, p, st);
-    if (e != hipSuccess) return fail(PA_ERR_HIP, "prefill kernel: %s", hipGetErrorString(e));
-    if (g_ev_after) {
-        e = hipEventRecord(g_ev_after, st);
-        if (e != hipSuccess) return fail(PA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
-    }
+    const pa::LaunchEvents ev{g_ev_before, g_ev_after};
     g_ev_before = g_ev_after = nullptr;
+    hipError_t e = pa::launch_prefill(pool->kv_dtype, pool->head_dim, p, st, &ev);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "prefill kernel: %s", hipGetErrorString(e));
     return ok();
 }
 

@@ -417,7 +417,8 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_kernel(DecodeParams p)
     const int s = (int)(row / p.num_q_heads);
     int ctx = p.context_lens[s];
     ctx = ctx < 0 ? 0 : (ctx > p.max_blocks_per_seq * kBlock ? p.max_blocks_per_seq * kBlock : ctx);
-    const int nparts = (ctx + p.partition_tokens - 1) / p.partition_tokens;
+    const int unit = p.partition_tokens * p.group_parts;   // tokens per partial result
+    const int nparts = (ctx + unit - 1) / unit;
     if (nparts <= 1) return;  // written by the partition kernel
     const float *ms = p.ws_m + row * p.max_partitions;
     const float *ls = p.ws_l + row * p.max_partitions;
@@ -497,27 +498,26 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_kernel(DecodeParams p)
 }
 
 template <int KV, int D>
-hipError_t launch_valu(const DecodeParams &p, hipStream_t stream) {
+hipError_t launch_valu(const DecodeParams &p, hipStream_t stream, const LaunchEvents *ev) {
     const int64_t grid = (int64_t)p.num_seqs * p.num_q_heads * p.max_partitions;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-    if (p.shared_kv)
-        decode_valu_kernel<KV, D, false><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(p);
-    else
-        decode_valu_kernel<KV, D, true><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(p);
-    return hipGetLastError();
+    const dim3 g((unsigned)grid), b(kThreads);
+    if (p.shared_kv) return launch_kernel(decode_valu_kernel<KV, D, false>, g, b, stream, ev, p);
+    return launch_kernel(decode_valu_kernel<KV, D, true>, g, b, stream, ev, p);
 }
 
 template <int KV>
-hipError_t launch_valu_d(int head_dim, const DecodeParams &p, hipStream_t stream) {
-    return head_dim == 64 ? launch_valu<KV, 64>(p, stream) : launch_valu<KV, 128>(p, stream);
+hipError_t launch_valu_d(int head_dim, const DecodeParams &p, hipStream_t stream, const LaunchEvents *ev) {
+    return head_dim == 64 ? launch_valu<KV, 64>(p, stream, ev) : launch_valu<KV, 128>(p, stream, ev);
 }
 
 }  // namespace
 
-hipError_t launch_decode_valu(int kv, int head_dim, const DecodeParams &p, hipStream_t stream) {
-    if (kv == kF32) return launch_valu_d<kF32>(head_dim, p, stream);
-    if (kv == kBF16) return launch_valu_d<kBF16>(head_dim, p, stream);
-    return launch_valu_d<kFP8>(head_dim, p, stream);
+hipError_t launch_decode_valu(int kv, int head_dim, const DecodeParams &p, hipStream_t stream,
+                              const LaunchEvents *ev) {
+    if (kv == kF32) return launch_valu_d<kF32>(head_dim, p, stream, ev);
+    if (kv == kBF16) return launch_valu_d<kBF16>(head_dim, p, stream, ev);
+    return launch_valu_d<kFP8>(head_dim, p, stream, ev);
 }
 
 hipError_t launch_decode_reduce(int head_dim, const DecodeParams &p, hipStream_t stream) {

@@ -58,16 +58,30 @@ struct DecodeLds {
     // used by the wavefront that writes it)
     alignas(16) uint8_t tok_k[D * 2];
     alignas(16) uint8_t tok_v[D * 2];
+    uint32_t done;           // wavefronts of a partition group that have finished
 };
 
-// One work item: partition `part` of sequence s, KV head g, with context
-// length ctx (already clamped to the table's capacity), computed by the NW
-// wavefronts of the calling workgroup.  APPEND: the decode step's newest
-// tokens are written by this call (DecodeParams::k_new / v_new) unless
-// `clamped` (the context was longer than its table row: no slot to write).
-template <int KV, int D, bool STREAM, int NW, bool APPEND>
-__device__ __forceinline__ void decode_item(const DecodeParams &p, int s, int g, int part, int ctx,
-                                            bool clamped, DecodeLds<D, NW> &sm) {
+// One wavefront's walk over its blocks j = jb + stride * k (k < nk) of
+// sequence s, KV head g, attending tokens below tok1 (its partition's end):
+// scores, online softmax and P.V accumulate into m (running maximum, base-2
+// domain), l (running sum, per-head total on return) and acc (numerators,
+// the MFMA C layout: lane (n, c) holds head n).  `writer`: this wavefront
+// reads the block holding position ctx - 1 and writes the decode step's
+// newest token (DecodeParams::k_new / v_new) into it (APPEND only); it stages
+// the token in tok_k / tok_v (LDS, 2 D bytes each).
+//
+// The newest token: the writer loads the token's inputs before its block
+// loads and stages them in LDS, encoded as the pool stores them; when the
+// block arrives, the lanes that hold the token's K runs and V cell elements
+// take them from there into its registers, and after the loop they store
+// them to the pool.  Stores issued before later loads would make every wait
+// on those loads wait for the stores as well (one counter covers both, in
+// issue order), and under full read traffic stores are slow.
+template <int KV, int D, bool STREAM, bool APPEND>
+__device__ __forceinline__ void walk_blocks(const DecodeParams &p, int s, int g, int jb, int stride,
+                                            int nk, int tok1, int ctx, bool writer, uint8_t *tok_k,
+                                            uint8_t *tok_v, float &m, float &l,
+                                            floatx4 (&acc)[D / 16]) {
     constexpr int EB = KV == kBF16 ? 2 : 1;
     constexpr int TILE_BYTES = kBlock * D * EB;
     constexpr int NQK = D / 32;                   // QK steps (32-deep) per block
@@ -75,35 +89,14 @@ __device__ __forceinline__ void decode_item(const DecodeParams &p, int s, int g,
     constexpr int W = 4 / EB;                     // V: head dims per 16-byte cell
     constexpr int NVL = D / W / 16;               // 16-byte V loads per lane per block
     constexpr int NT = D / 16;                    // 16 x 16 output tiles (= NVL * W)
-    constexpr int LDS_STRIDE = 17;                // [wave][d][head] with padding
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int wv = __builtin_amdgcn_readfirstlane(wave);   // the same, as a uniform value
     const int n = lane & 15;
     const int c = lane >> 4;
     const int G = p.group;
-
-    const int nparts = (ctx + p.partition_tokens - 1) / p.partition_tokens;
-    if (part >= (nparts > 1 ? nparts : 1)) return;
-    const int tok0 = part * p.partition_tokens;
-    const int tok1 = min(ctx, tok0 + p.partition_tokens);
-    const int blk0 = tok0 / kBlock;
-    const int blk1 = (tok1 + kBlock - 1) / kBlock;
     const int32_t *table = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
-
-    // A decode step's newest token (position ctx - 1) is written by the
-    // wavefront that reads the last block of the partition holding it (the
-    // only reader of that block for this KV head; wavefronts take every NW-th
-    // block).  It loads the token's inputs before its block loads and
-    // stages them in LDS, encoded as the pool stores them; when the block
-    // arrives, the lanes that hold the token's K runs and V cell elements
-    // take them from there into its registers, and after the loop they store
-    // them to the pool.  Stores issued before later loads would make every
-    // wait on those loads wait for the stores as well (one counter covers
-    // both, in issue order), and under full read traffic stores are slow.
-    const bool writer = APPEND && !clamped && tok1 == ctx && ctx > 0 && wv == (blk1 - 1 - blk0) % NW;
     const int tn = (ctx - 1) & (kBlock - 1);   // the newest token's slot in its block
+    const int jlast = (ctx - 1) / kBlock;      // ... and its block
 
     // Q^T operands: head g*G + n (zero for n >= G), head dims per the K mapping
     bf16x8 qop[NQK];
@@ -123,9 +116,8 @@ __device__ __forceinline__ void decode_item(const DecodeParams &p, int s, int g,
         }
     }
 
-    float m = kNegInf;
-    float l = 0.f;
-    floatx4 acc[NT];
+    m = kNegInf;
+    l = 0.f;
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
 
@@ -244,7 +236,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams &p, int s, int g,
         }
     };
 
-    // This wavefront's blocks are j = blk0 + wave + NW k, k = 0..nk-1; their ids
+    // This wavefront's blocks are j = jb + stride k, k = 0..nk-1; their ids
     // come from the table by scalar loads, one block ahead of their use.  Two
     // register buffers hold blocks k and k + 1; block k + 2 reuses block k's
     // buffer half by half: its K loads are issued as soon as block k's scores
@@ -252,11 +244,10 @@ __device__ __forceinline__ void decode_item(const DecodeParams &p, int s, int g,
     // keeps close to two blocks in flight in the registers of one.  Every step
     // issues the same loads (empty resources past the end), which lets each
     // wait cover exactly the loads it needs.
-    const int nk = blk1 - blk0 > wv ? (blk1 - blk0 - wv + NW - 1) / NW : 0;
     if (nk > 0) {
-        const int32_t *wtable = table + blk0 + wv;
+        const int32_t *wtable = table + jb;
         auto id_at = [&](int k) -> int32_t {
-            const int32_t b = wtable[NW * min(k, nk - 1)];
+            const int32_t b = wtable[stride * min(k, nk - 1)];
             return k < nk ? b : -1;
         };
         // the newest token's inputs go out first (lane elements lane + 64 i)
@@ -278,14 +269,14 @@ __device__ __forceinline__ void decode_item(const DecodeParams &p, int s, int g,
                 for (int i = 0; i < D / 64; ++i) {
                     const int d = lane + 64 * i;
                     if constexpr (KV == kBF16) {
-                        reinterpret_cast<uint16_t *>(sm.tok_k)[d] = (uint16_t)nt.k[i];
-                        reinterpret_cast<uint16_t *>(sm.tok_v)[d] = (uint16_t)nt.v[i];
+                        reinterpret_cast<uint16_t *>(tok_k)[d] = (uint16_t)nt.k[i];
+                        reinterpret_cast<uint16_t *>(tok_v)[d] = (uint16_t)nt.v[i];
                     } else {
                         const bool f32 = p.new_dtype == kF32;
                         const float kx = f32 ? __uint_as_float(nt.k[i]) : __uint_as_float(nt.k[i] << 16);
                         const float vx = f32 ? __uint_as_float(nt.v[i]) : __uint_as_float(nt.v[i] << 16);
-                        sm.tok_k[d] = (uint8_t)f32_to_e4m3(kx * p.inv_k_scale);
-                        sm.tok_v[d] = (uint8_t)f32_to_e4m3(vx * p.inv_v_scale);
+                        tok_k[d] = (uint8_t)f32_to_e4m3(kx * p.inv_k_scale);
+                        tok_v[d] = (uint8_t)f32_to_e4m3(vx * p.inv_v_scale);
                     }
                 }
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -301,13 +292,13 @@ __device__ __forceinline__ void decode_item(const DecodeParams &p, int s, int g,
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             if (n == tn) {
 #pragma unroll
-                for (int i = 0; i < NKL; ++i) kr[i] = *reinterpret_cast<const u32x4 *>(sm.tok_k + 16 * (c + 4 * i));
+                for (int i = 0; i < NKL; ++i) kr[i] = *reinterpret_cast<const u32x4 *>(tok_k + 16 * (c + 4 * i));
             }
             if (c == (tn >> 2)) {
                 const int r = tn & 3;
 #pragma unroll
                 for (int jj = 0; jj < NVL; ++jj) {
-                    const uint32_t x = *reinterpret_cast<const uint32_t *>(sm.tok_v + 4 * (16 * jj + n));
+                    const uint32_t x = *reinterpret_cast<const uint32_t *>(tok_v + 4 * (16 * jj + n));
 #pragma unroll
                     for (int w = 0; w < W; ++w) {
                         if constexpr (KV == kBF16) {
@@ -331,10 +322,10 @@ __device__ __forceinline__ void decode_item(const DecodeParams &p, int s, int g,
         auto step = [&](int d, int kk) {
             const int32_t id_after = id_pre;  // block kk + 2
             id_pre = id_at(kk + 3);
-            if (APPEND && writer && blk0 + wv + NW * kk == blk1 - 1) patch(kb[d], vb[d]);
+            if (APPEND && writer && jb + stride * kk == jlast) patch(kb[d], vb[d]);
             const floatx4 sacc = qk(kb[d]);
             load_k(id_after, kb[d], kFree);
-            if (valid(idb[d])) softmax_pv(sacc, vb[d], blk0 + wv + NW * kk);
+            if (valid(idb[d])) softmax_pv(sacc, vb[d], jb + stride * kk);
             load_v(id_after, vb[d], kFree);
             idb[d] = id_after;
         };
@@ -356,12 +347,12 @@ __device__ __forceinline__ void decode_item(const DecodeParams &p, int s, int g,
 #pragma unroll
                     for (int i = 0; i < NKL; ++i)
                         store16_nt(kt + ((c + 4 * i) * kBlock + tn) * 16,
-                                   *reinterpret_cast<const uint4 *>(sm.tok_k + 16 * (c + 4 * i)));
+                                   *reinterpret_cast<const uint4 *>(tok_k + 16 * (c + 4 * i)));
                 }
                 if (c == (tn >> 2)) {
 #pragma unroll
                     for (int jj = 0; jj < NVL; ++jj) {
-                        const uint32_t x = *reinterpret_cast<const uint32_t *>(sm.tok_v + 4 * (16 * jj + n));
+                        const uint32_t x = *reinterpret_cast<const uint32_t *>(tok_v + 4 * (16 * jj + n));
 #pragma unroll
                         for (int w = 0; w < W; ++w) {
                             const int off = ((tn >> 2) * (D / W) + 16 * jj + n) * 16 + (w * 4 + (tn & 3)) * EB;
@@ -378,53 +369,71 @@ __device__ __forceinline__ void decode_item(const DecodeParams &p, int s, int g,
 
     // per-head totals of the lane-partial sums
     l = add_xor32(add_xor16(l));
+}
 
+// One wavefront's (m, l, numerators) to slot `w` of the workgroup's LDS, in
+// [w][d][head] order.
+template <int D, int NW, int W>
+__device__ __forceinline__ void state_to_lds(DecodeLds<D, NW> &sm, int w, float m, float l,
+                                             const floatx4 (&acc)[D / 16]) {
+    constexpr int LDS_STRIDE = 17;
+    constexpr int NVL = D / W / 16;
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15;
+    const int c = lane >> 4;
     if (c == 0) {
-        sm.m[wave][n] = m;
-        sm.l[wave][n] = l;
+        sm.m[w][n] = m;
+        sm.l[w][n] = l;
     }
 #pragma unroll
     for (int jj = 0; jj < NVL; ++jj)
 #pragma unroll
-        for (int w = 0; w < W; ++w)
+        for (int ww = 0; ww < W; ++ww)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int d = W * (16 * jj + 4 * c + i) + w;
-                sm.acc[wave][d * LDS_STRIDE + n] = acc[jj * W + w][i];
+                const int d = W * (16 * jj + 4 * c + i) + ww;
+                sm.acc[w][d * LDS_STRIDE + n] = acc[jj * W + ww][i];
             }
-    __syncthreads();
+}
 
-    // merge and write: each lane takes 4 consecutive head dims of one head
-    // and stores them with one 16-byte store.  The stores that end a work
-    // item cost far more than their bytes while the chip streams K/V (timed
-    // on MI355X: the 512-token fp8 long-tail batch ran 20 % faster with them
-    // switched off), so there are 4x fewer of them than with one per dim.
-    // Final outputs go out non-temporal; split-K partials stay cacheable,
-    // since the reduce kernel reads them right after.
+// Merge the first `nw` wavefront states in LDS and write the result:
+// threads t0, t0 + tstride, ... each take 4 consecutive head dims of one
+// head and store them with one 16-byte store -- the final output row
+// (divided by the sum, times the value scale) when `final`, else the partial
+// (numerators, maximum, sum) of slot `slot` of the row.  The stores that end
+// a work item cost far more than their bytes while the chip streams K/V
+// (timed on MI355X: the 512-token fp8 long-tail batch ran 20 % faster with
+// them switched off), so there are 4x fewer of them than with one per dim.
+// Final outputs go out non-temporal; split-K partials stay cacheable, since
+// the reduce kernel reads them right after.
+template <int D, int NW>
+__device__ __forceinline__ void merge_and_store(const DecodeParams &p, const DecodeLds<D, NW> &sm, int s,
+                                                int g, int slot, bool final, int nw, int t0,
+                                                int tstride) {
+    constexpr int LDS_STRIDE = 17;
     constexpr int D4 = D / 4;
-    for (int idx = threadIdx.x; idx < G * D4; idx += 64 * NW) {
+    const int G = p.group;
+    for (int idx = t0; idx < G * D4; idx += tstride) {
         const int hh = idx / D4;
         const int d0 = 4 * (idx % D4);
         float M = sm.m[0][hh];
-#pragma unroll
-        for (int w = 1; w < NW; ++w) M = fmaxf(M, sm.m[w][hh]);
+        for (int w = 1; w < nw; ++w) M = fmaxf(M, sm.m[w][hh]);
         float L = 0.f;
         float O[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
+        for (int w = 0; w < nw; ++w) {
             const float f = sm.m[w][hh] == kNegInf ? 0.f : exp2f(sm.m[w][hh] - M);
             L += sm.l[w][hh] * f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) O[e] += sm.acc[w][(d0 + e) * LDS_STRIDE + hh] * f;
         }
         const int64_t row = (int64_t)s * p.num_q_heads + (int64_t)g * G + hh;
-        if (nparts <= 1) {
+        if (final) {
             float r[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) r[e] = L > 0.f ? (O[e] / L) * p.out_scale : 0.f;
             store16_nt(p.out + row * D + d0, __builtin_bit_cast(uint4, r));
         } else {
-            const int64_t pr = row * p.max_partitions + part;
+            const int64_t pr = row * p.max_partitions + slot;
             *reinterpret_cast<uint4 *>(p.ws_acc + pr * D + d0) = __builtin_bit_cast(uint4, O);
             if (d0 == 0) {
                 p.ws_m[pr] = M;
@@ -432,6 +441,37 @@ __device__ __forceinline__ void decode_item(const DecodeParams &p, int s, int g,
             }
         }
     }
+}
+
+// One work item: partition `part` of sequence s, KV head g, with context
+// length ctx (already clamped to the table's capacity), computed by the NW
+// wavefronts of the calling workgroup, which take every NW-th block and are
+// merged through LDS.  APPEND: the decode step's newest tokens are written
+// by this call unless `clamped` (the context was longer than its table row:
+// no slot to write).
+template <int KV, int D, bool STREAM, int NW, bool APPEND>
+__device__ __forceinline__ void decode_item(const DecodeParams &p, int s, int g, int part, int ctx,
+                                            bool clamped, DecodeLds<D, NW> &sm) {
+    constexpr int W = KV == kBF16 ? 2 : 4;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nparts = (ctx + p.partition_tokens - 1) / p.partition_tokens;
+    if (part >= (nparts > 1 ? nparts : 1)) return;
+    const int tok0 = part * p.partition_tokens;
+    const int tok1 = min(ctx, tok0 + p.partition_tokens);
+    const int blk0 = tok0 / kBlock;
+    const int blk1 = (tok1 + kBlock - 1) / kBlock;
+    // the newest token is written by the wavefront that reads the last
+    // block of the partition holding it (the only reader of that block for
+    // this KV head)
+    const bool writer = APPEND && !clamped && tok1 == ctx && ctx > 0 && wv == (blk1 - 1 - blk0) % NW;
+    const int nk = blk1 - blk0 > wv ? (blk1 - blk0 - wv + NW - 1) / NW : 0;
+    float m, l;
+    floatx4 acc[D / 16];
+    walk_blocks<KV, D, STREAM, APPEND>(p, s, g, blk0 + wv, NW, nk, tok1, ctx, writer, sm.tok_k,
+                                       sm.tok_v, m, l, acc);
+    state_to_lds<D, NW, W>(sm, wv, m, l, acc);
+    __syncthreads();
+    merge_and_store<D, NW>(p, sm, s, g, part, nparts <= 1, NW, threadIdx.x, 64 * NW);
 }
 
 __device__ __forceinline__ int clamp_ctx(const DecodeParams &p, int ctx) {
@@ -462,29 +502,86 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
     decode_item<KV, D, STREAM, NW, APPEND>(p, s, g, part, ctx, raw_ctx > ctx, sm);
 }
 
+// Partition groups: one workgroup of NG wavefronts per (sequence, KV head,
+// group of NG consecutive partitions) slot of a rows x max_partitions grid
+// (work order as above).  Wavefront w walks partition NG * group + w alone,
+// its blocks in order, with its own softmax state.  The wavefront that
+// finishes last -- counted with an LDS atomic, so that no wavefront waits for
+// another -- merges the group's states and writes them once: the output row
+// when the group covers the whole context, else the group's partial result
+// for the reduce kernel.  HBM so sees one partial per NG partitions instead
+// of one per partition, and contexts of up to NG partitions need no reduce.
+// Wavefronts with no partition (past the end of a short context) leave at
+// once, after the one barrier that publishes the cleared counter.
+template <int KV, int D, bool STREAM, int NG, bool APPEND>
+__global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(3))) void decode_group_kernel(DecodeParams p) {
+    __shared__ DecodeLds<D, NG> sm;
+    constexpr int W = KV == kBF16 ? 2 : 4;
+    int bid, grp;
+    pair_and_partition(p.num_seqs * p.num_kv_heads, p.max_partitions, bid, grp);
+    const int g = bid % p.num_kv_heads;
+    const int s = sequence_of_rank(p.context_lens, p.num_seqs, p.max_blocks_per_seq * kBlock,
+                                   bid / p.num_kv_heads);
+    const int raw_ctx = p.context_lens[s];
+    const int ctx = clamp_ctx(p, raw_ctx);
+    const int ptok = p.partition_tokens;
+    const int nparts = (ctx + ptok - 1) / ptok;
+    const int ngroups = (nparts + NG - 1) / NG;
+    if (grp >= (ngroups > 1 ? ngroups : 1)) return;     // the whole workgroup
+    if (threadIdx.x == 0) sm.done = 0u;
+    __syncthreads();
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // partitions of this group; an empty context has one (wavefront 0 writes
+    // its zero row)
+    const int nreal = nparts <= grp * NG ? 1 : min(NG, nparts - grp * NG);
+    if (wv >= nreal) return;
+    const int tok0 = (grp * NG + wv) * ptok;
+    const int tok1 = min(ctx, tok0 + ptok);
+    const int blk0 = tok0 / kBlock;
+    const int blk1 = (tok1 + kBlock - 1) / kBlock;
+    // the newest token is written by the wavefront whose partition holds it
+    const bool writer = APPEND && raw_ctx == ctx && tok1 == ctx && ctx > 0;
+    float m, l;
+    floatx4 acc[D / 16];
+    walk_blocks<KV, D, STREAM, APPEND>(p, s, g, blk0, 1, blk1 - blk0, tok1, ctx, writer, sm.tok_k,
+                                       sm.tok_v, m, l, acc);
+    state_to_lds<D, NG, W>(sm, wv, m, l, acc);
+    // this wavefront's state is in LDS before it counts itself as done; the
+    // last one to count sees every other state
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    uint32_t before = 0u;
+    if ((threadIdx.x & 63) == 0)
+        before = __hip_atomic_fetch_add(&sm.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    before = __builtin_amdgcn_readfirstlane(before);
+    if (before != (uint32_t)(nreal - 1)) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    merge_and_store<D, NG>(p, sm, s, g, grp, ngroups <= 1, nreal, threadIdx.x & 63, 64);
+}
+
 template <int KV, int D, bool STREAM, bool APPEND>
-hipError_t launch_variant(const DecodeParams &p, int64_t grid, hipStream_t stream) {
+hipError_t launch_variant(const DecodeParams &p, int64_t grid, hipStream_t stream, const LaunchEvents *ev) {
     // one-wavefront workgroups walk all of a partition's blocks and need no
-    // merge; the caller picks them for short partitions and for batches with
-    // at least two (sequence, KV head) rows per SIMD
-    if (p.one_wave == 0) {
-        decode_mfma_kernel<KV, D, STREAM, 4, APPEND><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(p);
-        return hipGetLastError();
-    }
-    decode_mfma_kernel<KV, D, STREAM, 1, APPEND><<<dim3((unsigned)grid), dim3(64), 0, stream>>>(p);
-    return hipGetLastError();
+    // merge; the caller picks them for batches with at least two (sequence,
+    // KV head) rows per SIMD, and partition groups for short partitions
+    const dim3 g((unsigned)grid);
+    if (p.wave_mode == kFourWaves)
+        return launch_kernel(decode_mfma_kernel<KV, D, STREAM, 4, APPEND>, g, dim3(256), stream, ev, p);
+    if (p.wave_mode == kOneWave)
+        return launch_kernel(decode_mfma_kernel<KV, D, STREAM, 1, APPEND>, g, dim3(64), stream, ev, p);
+    return launch_kernel(decode_group_kernel<KV, D, STREAM, kGroupParts, APPEND>, g, dim3(64 * kGroupParts),
+                         stream, ev, p);
 }
 
 template <int KV, int D>
-hipError_t launch(const DecodeParams &p, hipStream_t stream) {
+hipError_t launch(const DecodeParams &p, hipStream_t stream, const LaunchEvents *ev) {
     const int64_t grid = (int64_t)p.num_seqs * p.num_kv_heads * p.max_partitions;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
     const bool append = p.k_new != nullptr;
     if (p.shared_kv)
-        return append ? launch_variant<KV, D, false, true>(p, grid, stream)
-                      : launch_variant<KV, D, false, false>(p, grid, stream);
-    return append ? launch_variant<KV, D, true, true>(p, grid, stream)
-                  : launch_variant<KV, D, true, false>(p, grid, stream);
+        return append ? launch_variant<KV, D, false, true>(p, grid, stream, ev)
+                      : launch_variant<KV, D, false, false>(p, grid, stream, ev);
+    return append ? launch_variant<KV, D, true, true>(p, grid, stream, ev)
+                  : launch_variant<KV, D, true, false>(p, grid, stream, ev);
 }
 
 }  // namespace
@@ -494,9 +591,11 @@ bool mfma_path_supported(int kv, int head_dim, int group) {
            group <= 16;
 }
 
-hipError_t launch_decode_mfma(int kv, int head_dim, const DecodeParams &p, hipStream_t stream) {
-    if (kv == kBF16) return head_dim == 64 ? launch<kBF16, 64>(p, stream) : launch<kBF16, 128>(p, stream);
-    return head_dim == 64 ? launch<kFP8, 64>(p, stream) : launch<kFP8, 128>(p, stream);
+hipError_t launch_decode_mfma(int kv, int head_dim, const DecodeParams &p, hipStream_t stream,
+                              const LaunchEvents *ev) {
+    if (kv == kBF16)
+        return head_dim == 64 ? launch<kBF16, 64>(p, stream, ev) : launch<kBF16, 128>(p, stream, ev);
+    return head_dim == 64 ? launch<kFP8, 64>(p, stream, ev) : launch<kFP8, 128>(p, stream, ev);
 }
 
 }  // namespace pa

@@ -1,6 +1,7 @@
 // pa_internal.h -- launch interfaces shared by the library's translation units.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -10,6 +11,15 @@ enum KvType : int { kF32 = 0, kBF16 = 1, kFP8 = 2 };
 
 constexpr int kBlock = 16;       // tokens per block
 constexpr int kThreads = 256;    // threads per workgroup of every kernel (4 wavefronts)
+constexpr int kGroupParts = 4;   // partitions per workgroup of the grouped kernel's partition groups
+
+// How the grouped (matrix-core) decode kernel maps work to wavefronts.
+enum WaveMode : int {
+    kFourWaves = 0,   // one partition per workgroup, four wavefronts taking every 4th block
+    kOneWave = 1,     // one partition per one-wavefront workgroup
+    kPartGroups = 2,  // kGroupParts consecutive partitions per workgroup, one per wavefront,
+                      // merged on chip into one partial result
+};
 
 inline int elem_bytes(int kv) { return kv == kF32 ? 4 : (kv == kBF16 ? 2 : 1); }
 
@@ -29,9 +39,12 @@ struct DecodeParams {
     int32_t group;             // Hq / Hkv
     int32_t num_seqs;
     int32_t max_blocks_per_seq;
-    int32_t partition_tokens;  // multiple of 16
-    int32_t max_partitions;    // ceil(max_blocks_per_seq * 16 / partition_tokens)
-    int32_t one_wave;          // grouped kernel: one-wavefront workgroups instead of four
+    int32_t partition_tokens;  // tokens per partition (multiple of 16)
+    int32_t group_parts;       // partitions merged into one partial result (kGroupParts with
+                               // kPartGroups, else 1)
+    int32_t max_partitions;    // partial results per row: ceil(max_blocks_per_seq * 16 /
+                               // (partition_tokens * group_parts))
+    int32_t wave_mode;         // grouped kernel: WaveMode
     float qk_scale_log2;       // scale * k_scale * log2(e)
     float out_scale;           // v_scale (1 for 16/32-bit pools)
     int32_t shared_kv;         // blocks shared across sequences: cached, not streaming, loads
@@ -77,9 +90,31 @@ struct CacheParams {
     float inv_v_scale;
 };
 
-// Each launcher enqueues on `stream` and returns the launch status.
-hipError_t launch_decode_valu(int kv, int head_dim, const DecodeParams &p, hipStream_t stream);
-hipError_t launch_decode_mfma(int kv, int head_dim, const DecodeParams &p, hipStream_t stream);
+// Timing events of one kernel launch (a measurement aid): when `start` is
+// set, the kernel goes out through hipExtLaunchKernel, whose dispatch stores
+// the kernel's start and end times in `start` and `stop`.
+struct LaunchEvents {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+
+// Launch `kernel` (one by-value argument) on `stream`, timed by `ev` if given.
+template <class P>
+inline hipError_t launch_kernel(void (*kernel)(P), dim3 grid, dim3 block, hipStream_t stream,
+                                const LaunchEvents *ev, P arg) {
+    void *argv[] = {static_cast<void *>(&arg)};
+    if (ev && ev->start)
+        return hipExtLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, argv, 0, stream,
+                                  ev->start, ev->stop, 0);
+    return hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, argv, 0, stream);
+}
+
+// Each launcher enqueues on `stream` and returns the launch status; the
+// partition (and prefill) kernels' launches are timed by `ev` when given.
+hipError_t launch_decode_valu(int kv, int head_dim, const DecodeParams &p, hipStream_t stream,
+                              const LaunchEvents *ev = nullptr);
+hipError_t launch_decode_mfma(int kv, int head_dim, const DecodeParams &p, hipStream_t stream,
+                              const LaunchEvents *ev = nullptr);
 bool mfma_path_supported(int kv, int head_dim, int group);
 hipError_t launch_decode_reduce(int head_dim, const DecodeParams &p, hipStream_t stream);
 // each sequence's newest token (p.k_new / p.v_new) to the slot of position
@@ -87,7 +122,8 @@ hipError_t launch_decode_reduce(int head_dim, const DecodeParams &p, hipStream_t
 hipError_t launch_append_tokens(int kv, int head_dim, const DecodeParams &p, hipStream_t stream);
 bool prefill_supported(int kv, int head_dim, int group);
 int prefill_tile_tokens(int head_dim, int group);  // chunk tokens per prefill workgroup
-hipError_t launch_prefill(int kv, int head_dim, const PrefillParams &p, hipStream_t stream);
+hipError_t launch_prefill(int kv, int head_dim, const PrefillParams &p, hipStream_t stream,
+                          const LaunchEvents *ev = nullptr);
 hipError_t launch_reshape_and_cache(int pool_kv, int in_kv, int head_dim, const CacheParams &p,
                                     hipStream_t stream);
 hipError_t launch_copy_blocks(void *k_pool, void *v_pool, const int32_t *pairs, int32_t num_pairs,

@@ -357,11 +357,10 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
 }
 
 template <int KV, int D>
-hipError_t launch(const PrefillParams &p, hipStream_t stream) {
+hipError_t launch(const PrefillParams &p, hipStream_t stream, const LaunchEvents *ev) {
     const int64_t grid = (int64_t)p.num_tiles * p.num_seqs * p.num_kv_heads;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-    prefill_mfma_kernel<KV, D><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(p);
-    return hipGetLastError();
+    return launch_kernel(prefill_mfma_kernel<KV, D>, dim3((unsigned)grid), dim3(kThreads), stream, ev, p);
 }
 
 }  // namespace
@@ -373,9 +372,11 @@ bool prefill_supported(int kv, int head_dim, int group) {
            group <= kRowsPerTile;
 }
 
-hipError_t launch_prefill(int kv, int head_dim, const PrefillParams &p, hipStream_t stream) {
-    if (kv == kBF16) return head_dim == 64 ? launch<kBF16, 64>(p, stream) : launch<kBF16, 128>(p, stream);
-    return head_dim == 64 ? launch<kFP8, 64>(p, stream) : launch<kFP8, 128>(p, stream);
+hipError_t launch_prefill(int kv, int head_dim, const PrefillParams &p, hipStream_t stream,
+                          const LaunchEvents *ev) {
+    if (kv == kBF16)
+        return head_dim == 64 ? launch<kBF16, 64>(p, stream, ev) : launch<kBF16, 128>(p, stream, ev);
+    return head_dim == 64 ? launch<kFP8, 64>(p, stream, ev) : launch<kFP8, 128>(p, stream, ev);
 }
 
 }  // namespace pa

@@ -415,11 +415,11 @@ def decode_variant(pool: KVPool, num_q_heads: int) -> str:
 
 
 def set_profile_events(before, after) -> None:
-    """Record torch.cuda.Event ``before``/``after`` around the next decode's
-    partition kernel (pass None, None to clear)."""
-    b = before.cuda_event if before is not None else None
-    a = after.cuda_event if after is not None else None
-    _check(lib().pa_set_profile_events(b, a))
+    """Have the next decode's (or prefill's) partition kernel store its start
+    and end times in ``before``/``after``: torch.cuda.Event objects or raw
+    hipEvent_t handles (pass None, None to clear)."""
+    raw = lambda e: None if e is None else (e.cuda_event if hasattr(e, "cuda_event") else int(e))
+    _check(lib().pa_set_profile_events(raw(before), raw(after)))
 
 
 def probe_read(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:

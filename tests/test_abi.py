@@ -82,10 +82,17 @@ def test_decode_argument_rules():
 def test_workspace_size_formula():
     L = ops.lib()
     d = desc()
-    # 4 seqs x 64 heads x 8 partitions: acc (D floats) + m + l, each region 256-byte aligned
-    rows = 4 * 64 * 8
-    want = rows * 128 * 4 + 2 * ((rows * 4 + 255) // 256 * 256)
-    assert L.pa_decode_workspace_size(ctypes.byref(d), 4, 64, 256, 512) == want
+    ws = lambda rows: rows * 128 * 4 + 2 * ((rows * 4 + 255) // 256 * 256)
+    # one query head per KV head (vector-ALU kernel): 4 seqs x 8 heads x 8
+    # partitions of 512 tokens, acc (D floats) + m + l, each region 256-byte aligned
+    assert L.pa_decode_workspace_size(ctypes.byref(d), 4, 8, 256, 512) == ws(4 * 8 * 8)
+    # grouped heads (matrix-core kernel) with partitions of <= 512 tokens: four
+    # partitions merge on chip into one partial, so 8 partitions leave 2
+    assert L.pa_decode_workspace_size(ctypes.byref(d), 4, 64, 256, 512) == ws(4 * 64 * 2)
+    assert L.pa_decode_workspace_size(ctypes.byref(d), 4, 64, 256, 256) == ws(4 * 64 * 4)
+    assert L.pa_decode_workspace_size(ctypes.byref(d), 4, 64, 32, 128) == 0   # 4 partitions: one group
+    # longer partitions: one partial per partition
+    assert L.pa_decode_workspace_size(ctypes.byref(d), 4, 64, 256, 1024) == ws(4 * 64 * 4)
     assert L.pa_decode_workspace_size(ctypes.byref(d), 4, 64, 256, 4096) == 0
     assert L.pa_decode_partition_tokens(ctypes.byref(d), 4, 64, 256, 512) == 512
     auto = L.pa_decode_partition_tokens(ctypes.byref(d), 4, 64, 256, 0)

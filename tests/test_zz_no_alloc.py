@@ -36,11 +36,14 @@ def _both(w, ptok, shared_kv=False):
     return ref.cpu().numpy(), out.cpu().numpy()
 
 
-@pytest.mark.parametrize("name,ptok,seqs", [("fp8", 512, (5, 2)), ("mha13b", 64, (5, 3)),
-                                            ("gqa70b", 256, (3, 1)), ("sampling_b", 128, (2, 1))])
+@pytest.mark.parametrize("name,ptok,seqs", [("fp8", 128, (5, 2)), ("mha13b", 64, (5, 3)),
+                                            ("gqa70b", 256, (3, 1)), ("sampling_b", 128, (2, 1)),
+                                            ("gqa70b", 1024, (3, 1))])
 def test_noalloc_equals_decode_ex_on_two_calls(name, ptok, seqs):
     """Matrix-core (fp8, 64/8 heads; 70B-like; 40/8 heads) and vector-ALU
-    (13B-like) kernels with split-K partitions."""
+    (13B-like) kernels with split-K partials: partition groups (partitions of
+    <= 512 tokens, four merged per partial) and one partial per partition
+    (1024 tokens)."""
     for i, n in enumerate(seqs):
         print("case %s ptok %d call %d: %d sequences" % (name, ptok, i, n), flush=True)
         if name.startswith("sampling"):
