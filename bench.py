@@ -88,6 +88,10 @@ def parse():
     ap.add_argument("--cpu-seqs", type=int, default=None,
                     help="sequences in the CPU-oracle sample (default: ~10-30 s of CPU work)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode", choices=("auto", "plain", "prefix-shared"), default="auto",
+                    help="decode entry point: pa_decode_ex per sequence (plain), or "
+                         "pa_decode_prefix_shared over the groups of sequences forked from shared "
+                         "prompts (auto: prefix-shared for workloads with such groups)")
     ap.add_argument("--no-configs", action="store_true",
                     help="default workload: skip timing and checking the other decode "
                          "configurations (the 'configs' record)")
@@ -236,8 +240,10 @@ def main():
     w = wl.make_workload(args.workload, small=False, device="cuda:0")
     setup_s = time.time() - t0
     ptok = w.partition_tokens if args.partition_tokens is None else args.partition_tokens
+    prefix_shared = (args.decode == "prefix-shared" or
+                     (args.decode == "auto" and "group_sizes" in w.info and args.append == "separate"))
     r = decode_run(w, args.steps, args.warmup, ptok, args.append, graph=args.graph,
-                   flush_and_probe=True)
+                   flush_and_probe=True, prefix_shared=prefix_shared)
     kv_bytes, uniq = w.kv_bytes(), w.unique_kv_bytes()
     traffic = traffic_for(args.workload, r["kernel"], uniq)
     rec = {
@@ -290,13 +296,18 @@ def main():
     print(json.dumps(rec), flush=True)
 
 
-def decode_run(w, steps, warmup, ptok, append="separate", graph=False, flush_and_probe=False):
+def decode_run(w, steps, warmup, ptok, append="separate", graph=False, flush_and_probe=False,
+               prefix_shared=False):
     """Time `steps` decode steps of workload `w` after `warmup` untimed ones.
     A step: the copy-on-write copies of the workload's last step (beam search;
     none otherwise), the cache write of every sequence's newest token (before
     the decode call, or inside it with append="fused"), and the decode call
-    (partition kernel + split-K reduce).  HIP events on the launch stream
-    bracket the whole timed region and, every step, the partition kernel."""
+    (partition kernel + split-K reduce).  With `prefix_shared` (workloads
+    whose sequences come in groups forked from shared prompts) the decode
+    call is pa_decode_prefix_shared over those groups, and the plain decode
+    kernel is timed on the same pool for comparison.  HIP events on the
+    launch stream bracket the whole timed region and, every step, the
+    partition kernel."""
     import numpy as np
     import torch
 
@@ -345,13 +356,32 @@ def decode_run(w, steps, warmup, ptok, append="separate", graph=False, flush_and
                              "position, in a block of its own")
     new_kv = dict(k_new=step_k, v_new=step_v) if fused else {}
     write_first = step_slots is not None and not fused
+    groups = None
+    if prefix_shared:
+        from paged_kv_cache_401_amd.blocks import prefix_groups
+        if fused:
+            raise SystemExit("the prefix-shared decode takes its new tokens from the cache write")
+        mg = max(1, 16 // w.group)
+        st, pb = prefix_groups(w.block_tables, w.context_lens, w.info["group_sizes"], mg)
+        groups = (torch.as_tensor(np.asarray(st, np.int32), device=dev),
+                  torch.as_tensor(np.asarray(pb, np.int32), device=dev), mg)
+        sws = ops.decode_prefix_shared_workspace_size(pool, w.S, w.Hq, w.max_blocks_per_seq,
+                                                      len(pb), mg, ptok)
+        sws_t = torch.empty(max(sws, 16), dtype=torch.uint8, device=dev)
+
+    def decode_call():
+        if groups is None:
+            ops.decode(pool, q, tables, ctx, w.scale, out=out, partition_tokens=ptok,
+                       workspace=ws, shared_kv=shared, **new_kv)
+        else:
+            ops.decode_prefix_shared(pool, q, tables, ctx, groups[0], groups[1], groups[2], w.scale,
+                                     out=out, partition_tokens=ptok, workspace=sws_t)
 
     def step():
         ops.copy_blocks(pool, step_pairs)
         if write_first:
             ops.reshape_and_cache(pool, step_k, step_v, step_slots)
-        ops.decode(pool, q, tables, ctx, w.scale, out=out, partition_tokens=ptok,
-                   workspace=ws, shared_kv=shared, **new_kv)
+        decode_call()
 
     for _ in range(warmup):
         step()
@@ -371,31 +401,32 @@ def decode_run(w, steps, warmup, ptok, append="separate", graph=False, flush_and
         if write_first:
             ops.reshape_and_cache(pool, step_k, step_v, step_slots)
         ops.set_profile_events(*timer.pair(i))
-        ops.decode(pool, q, tables, ctx, w.scale, out=out, partition_tokens=ptok, workspace=ws,
-                   shared_kv=shared, **new_kv)
+        decode_call()
     step_end.record(stream)
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - wall0
     kern_ms = [timer.elapsed_ms(i) for i in range(steps)]
     timer.close()
-    res = {"pool": pool, "out": out, "kernel": ops.decode_variant(pool, w.Hq),
+    plan = ops.decode_plan(pool, w.S, w.Hq, w.max_blocks_per_seq, ptok)
+    res = {"pool": pool, "out": out,
+           "kernel": "decode_shared_kernel" if groups is not None else plan["kernel"],
            "partition_tokens": ptok_used, "ms_per_step": step_begin.elapsed_time(step_end) / steps,
            "wall_ms_per_step": 1e3 * wall_s / steps, "kernel_ms": float(np.mean(kern_ms)),
            "kernel_ms_all": kern_ms,
-           "kv_loads": "cached (shared blocks)" if shared else "non-temporal",
+           "kv_loads": ("non-temporal, shared blocks read once per group" if groups is not None
+                        else "cached (shared blocks)" if shared else "non-temporal"),
            "cache_write": ("none" if step_slots is None else
                            "in the decode call" if fused else "separate kernel"),
            "extra": {}}
 
-    def time_copies(pairs, label):
-        """The copy-on-write kernel alone on `pairs`: read + write bytes of K
-        and V blocks (a copy leaves its source unchanged, so repeats are
-        idempotent)."""
+    def time_copies(pairs, label, target):
+        """The copy-on-write kernel alone on `pairs` in pool `target`: read +
+        write bytes of K and V blocks."""
         cb, ce = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ops.copy_blocks(pool, pairs)
+        ops.copy_blocks(target, pairs)
         cb.record(stream)
         for _ in range(steps):
-            ops.copy_blocks(pool, pairs)
+            ops.copy_blocks(target, pairs)
         ce.record(stream)
         torch.cuda.synchronize()
         copy_ms = cb.elapsed_time(ce) / steps
@@ -405,19 +436,43 @@ def decode_run(w, steps, warmup, ptok, append="separate", graph=False, flush_and
                 "ms": round(copy_ms, 5), "read_plus_write_GBps": round(moved / copy_ms / 1e6, 1)}
 
     if step_pairs.shape[0]:
-        res["extra"]["copy_blocks"] = time_copies(step_pairs, "the step's copy-on-write pairs")
+        # the step's copies, each followed in the step by its token write
+        res["extra"]["copy_blocks"] = time_copies(step_pairs, "the step's copy-on-write pairs", pool)
     elif cow_pairs is not None and cow_pairs.shape[0]:
+        # the fork's copies, timed on a scratch pool of the same shape: the
+        # samples have since written their own tokens into the copies, which
+        # copying again would overwrite
+        scratch = ops.KVPool(w.num_blocks, w.Hkv, w.D, w.pool_dtype, device=dev, k_scale=w.k_scale,
+                             v_scale=w.v_scale, fill=0)
         res["extra"]["copy_blocks"] = time_copies(
-            cow_pairs, "the fork's copy-on-write pairs (shared partial prompt blocks)")
+            cow_pairs, "the fork's copy-on-write pairs (shared partial prompt blocks)", scratch)
+        del scratch
+    if groups is not None:
+        # the plain decode (one workgroup per sequence and KV head) on the same
+        # pool, its partition kernel timed the same way
+        res["extra"]["prefix_groups"] = {"groups": int(groups[1].numel()), "max_group_size": groups[2],
+                                         "shared_blocks_per_group": sorted(set(groups[1].tolist()))[:4]}
+        plain_out = torch.empty_like(out)
+        for _ in range(3):
+            ops.decode(pool, q, tables, ctx, w.scale, out=plain_out, partition_tokens=0, shared_kv=True)
+        timer = KernelTimer(steps)
+        for i in range(steps):
+            ops.set_profile_events(*timer.pair(i))
+            ops.decode(pool, q, tables, ctx, w.scale, out=plain_out, partition_tokens=0, shared_kv=True)
+        torch.cuda.synchronize()
+        res["extra"]["plain_decode_kernel_ms"] = round(float(np.mean([timer.elapsed_ms(i)
+                                                                      for i in range(steps)])), 5)
+        timer.close()
+        res["extra"]["plain_vs_prefix_shared_max_abs_diff"] = float(
+            (plain_out - out).abs().max().item())
     if graph:
         res["extra"]["graph"] = graph_step_time(step, steps, w.S)
     if flush_and_probe:
-        res["extra"].update(flushed_and_probe(w, pool, q, tables, ctx, out, ptok, ws, shared,
-                                              new_kv, steps))
+        res["extra"].update(flushed_and_probe(w, pool, decode_call, steps))
     return res
 
 
-def flushed_and_probe(w, pool, q, tables, ctx, out, ptok, ws, shared, new_kv, steps):
+def flushed_and_probe(w, pool, decode_call, steps):
     """The same decode call once more per step with a 1 GiB read before each
     launch (untimed, outside the timed steps): afterwards the 256 MB MALL
     holds clean lines of another buffer and nothing of the pool, so the
@@ -440,8 +495,7 @@ def flushed_and_probe(w, pool, q, tables, ctx, out, ptok, ws, shared, new_kv, st
     for i in range(steps):
         flush.sum()
         ops.set_profile_events(*timer.pair(i))
-        ops.decode(pool, q, tables, ctx, w.scale, out=out, partition_tokens=ptok, workspace=ws,
-                   shared_kv=shared, **new_kv)
+        decode_call()
     torch.cuda.synchronize()
     flushed_ms = [timer.elapsed_ms(i) for i in range(steps)]
     timer.close()
@@ -479,11 +533,12 @@ def other_configs(args):
     from paged_kv_cache_401_amd import workloads as wl
 
     recs = {}
-    steps, warmup = max(5, args.steps // 2), max(2, args.warmup // 2)
+    steps, warmup = args.steps, args.warmup
     for name in CONFIG_RUNS:
         t0 = time.time()
         w = wl.make_workload(name, small=False, device="cuda:0")
-        r = decode_run(w, steps, warmup, w.partition_tokens, "separate")
+        r = decode_run(w, steps, warmup, w.partition_tokens, "separate",
+                       prefix_shared="group_sizes" in w.info)
         kv, uniq = w.kv_bytes(), w.unique_kv_bytes()
         ctxs = w.context_lens
         seqs = sorted({0, w.S - 1, int(np.argmax(ctxs)), int(np.argmin(ctxs)), w.S // 2})

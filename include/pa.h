@@ -192,6 +192,51 @@ int pa_decode_noalloc(const pa_pool_t *pool, const void *q, int32_t q_dtype, int
                       uint32_t flags, void *stream);
 
 /*
+ * pa_decode_prefix_shared -- pa_decode_ex for a batch whose sequences come in
+ * groups that hold the same first blocks in their block tables: the samples
+ * of one prompt (parallel sampling), the beams of one request, requests over
+ * one cached system prompt ("PagedAttention" glossary page, sharing blocks
+ * between sequences: several tables name the same physical blocks of a
+ * shared prefix).  The result is that of pa_decode_ex for every sequence, up
+ * to fp32 rounding order; the shared blocks are read once per group and KV
+ * head instead of once per sequence, every query head of every member of a
+ * group being a column of one 16-column matrix-core tile.
+ *   group_start    int32 [num_groups + 1] (device): group i is sequences
+ *                  group_start[i] .. group_start[i+1] - 1; group_start[0] = 0,
+ *                  non-decreasing, group_start[num_groups] = num_seqs.  A
+ *                  sequence that shares nothing is a group of its own.
+ *   prefix_blocks  int32 [num_groups] (device): leading table entries every
+ *                  member of group i holds in common.  Only whole blocks
+ *                  inside every member's context count (the kernel takes at
+ *                  most min over members of floor(context_len / 16)).
+ *   max_group_size host-side bound on the members of any group (larger
+ *                  groups are cut to it); max_group_size * (num_q_heads /
+ *                  num_kv_heads) must be at most 16 (PA_ERR_SHAPE).
+ *   partition_tokens  0 = library's choice, else a multiple of 16 up to
+ *                  8192: a group's blocks (shared ones, then each member's
+ *                  own) are cut into partitions of this many tokens.
+ *   workspace      device buffer of >= pa_decode_prefix_shared_workspace_size
+ *                  bytes (may be NULL when that is 0).
+ * Pools: PA_BF16 or PA_FP8_E4M3 (PA_ERR_UNSUPPORTED for fp32); q_dtype
+ * PA_BF16.  Other arguments, flags and errors as pa_decode_ex.  The group
+ * arrays are device data the host does not read: members beyond the batch
+ * or max_group_size are left out.
+ */
+int pa_decode_prefix_shared(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t num_seqs,
+                            int32_t num_q_heads, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                            const int32_t *context_lens, const int32_t *group_start,
+                            const int32_t *prefix_blocks, int32_t num_groups, int32_t max_group_size,
+                            float scale, float *out, int32_t partition_tokens, void *workspace,
+                            size_t workspace_bytes, uint32_t flags, void *stream);
+
+/* Workspace bytes pa_decode_prefix_shared needs for these arguments (0 when
+ * every group's blocks fit one partition; 0 also on invalid arguments). */
+size_t pa_decode_prefix_shared_workspace_size(const pa_pool_t *pool, int32_t num_seqs,
+                                              int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                              int32_t num_groups, int32_t max_group_size,
+                                              int32_t partition_tokens);
+
+/*
  * pa_decode_append -- one decode step: write every sequence's newest token,
  * then attend as pa_decode_ex.  The newest token of sequence s sits at
  * position context_lens[s] - 1 (its context includes it, as the step
@@ -373,6 +418,16 @@ int pa_set_debug(int on);
  * kernel (one workgroup per KV head and its group of query heads).  Returns a
  * negative pa_status on invalid arguments. */
 int pa_decode_variant(const pa_pool_t *pool, int32_t num_q_heads);
+
+/* The launch pa_decode_ex makes for these arguments (for tooling and
+ * profiles): plan[0] = partition kernel (0 vector-ALU, one workgroup per
+ * query head; 1 matrix-core, one partition per workgroup; 2 matrix-core,
+ * four partitions per workgroup merged on chip), plan[1] = partition
+ * tokens, plan[2] = partial results per (sequence, query head) row (1: none,
+ * no merge kernel), plan[3] = partitions merged into each partial result.
+ * Returns a pa_status. */
+int pa_decode_plan(const pa_pool_t *pool, int32_t num_seqs, int32_t num_q_heads,
+                   int32_t max_blocks_per_seq, int32_t partition_tokens, int32_t plan[4]);
 
 /* Measurement aid: the next pa_decode or pa_prefill call on this host
  * thread stores its partition (or prefill) kernel's start time in `before`

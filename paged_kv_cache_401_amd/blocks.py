@@ -224,3 +224,31 @@ def blocks_for(n_tokens: int, block_size: int = BLOCK_SIZE) -> int:
 def unused_slots(n_tokens: int, block_size: int = BLOCK_SIZE) -> int:
     """Slots reserved but unused: only the unfilled part of the last block."""
     return blocks_for(n_tokens, block_size) * block_size - int(n_tokens)
+
+
+def prefix_groups(tables, context_lens, sizes, max_group: int):
+    """Inputs of the prefix-shared decode for a batch cut into groups of
+    consecutive sequences: ``sizes`` lists each group's member count in batch
+    order, and a group's shared prefix is the number of leading whole blocks
+    (full in every member's context) that every member's table names alike --
+    the blocks a fork left shared ("PagedAttention" glossary page, sharing
+    blocks between sequences).  Groups larger than ``max_group`` are cut.
+    Returns (group_start [G + 1], prefix_blocks [G]) as int lists."""
+    starts, prefix = [0], []
+    s = 0
+    for size in sizes:
+        size = int(size)
+        while size > 0:
+            m = min(size, max_group)
+            members = range(s, s + m)
+            whole = min(int(context_lens[t]) // BLOCK_SIZE for t in members)
+            k = 0
+            while k < whole and all(int(tables[t][k]) == int(tables[s][k]) for t in members):
+                k += 1
+            prefix.append(k)
+            s += m
+            starts.append(s)
+            size -= m
+    if s != len(context_lens):
+        raise ValueError("group sizes cover %d of %d sequences" % (s, len(context_lens)))
+    return starts, prefix

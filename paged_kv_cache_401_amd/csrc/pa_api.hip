@@ -176,6 +176,63 @@ size_t workspace_for(const pa_pool_t *pool, int32_t num_seqs, int32_t num_q_head
     return (size_t)(acc + 2 * ml);
 }
 
+// ---- decode of prefix-sharing groups ---------------------------------------
+
+// A group's block list is at most max_group members x max_blocks_per_seq
+// blocks (no shared prefix).  The library's partition length keeps each
+// group in one partition -- no partial results, no merge -- when the list
+// fits one workgroup's LDS list and the groups alone give enough workgroups;
+// otherwise it halves the length (down to 1024 tokens) until they do.
+int32_t shared_auto_partition(const pa_pool_t *pool, int32_t num_groups, int32_t max_group,
+                              int32_t max_blocks_per_seq) {
+    const int64_t list_tokens = (int64_t)max_group * max_blocks_per_seq * PA_BLOCK_SIZE;
+    const int64_t rows = (int64_t)num_groups * pool->num_kv_heads;
+    int64_t ptok = list_tokens < pa::kSharedListMax * PA_BLOCK_SIZE ? list_tokens
+                                                                    : pa::kSharedListMax * PA_BLOCK_SIZE;
+    while (ptok > 1024 && rows * ((list_tokens + ptok - 1) / ptok) < 512)
+        ptok = ((ptok / 2 + 15) / 16) * 16;
+    return (int32_t)(ptok < 16 ? 16 : ptok);
+}
+
+int check_shared_args(const pa_pool_t *pool, int32_t num_seqs, int32_t num_q_heads,
+                      int32_t max_blocks_per_seq, int32_t num_groups, int32_t max_group,
+                      int32_t partition_tokens, int32_t *ptok_out) {
+    int rc = check_pool(pool);
+    if (rc != PA_OK) return rc;
+    rc = check_heads(pool, num_seqs, num_q_heads, max_blocks_per_seq);
+    if (rc != PA_OK) return rc;
+    if (pool->kv_dtype == PA_F32)
+        return fail(PA_ERR_UNSUPPORTED, "prefix-shared decode needs a bf16 or fp8 pool");
+    const int32_t G = num_q_heads / pool->num_kv_heads;
+    if (num_groups < 0 || (num_seqs > 0 && num_groups == 0) || num_groups > num_seqs)
+        return fail(PA_ERR_SHAPE, "num_groups %d must be in [1, num_seqs %d]", num_groups, num_seqs);
+    if (max_group < 1 || (int64_t)max_group * G > 16)
+        return fail(PA_ERR_SHAPE, "max_group_size %d x query group %d must be in [1, 16]", max_group, G);
+    if (partition_tokens < 0 || partition_tokens % PA_BLOCK_SIZE != 0 ||
+        partition_tokens > pa::kSharedListMax * PA_BLOCK_SIZE)
+        return fail(PA_ERR_SHAPE, "partition_tokens %d must be 0 or a multiple of 16 up to %d",
+                    partition_tokens, pa::kSharedListMax * PA_BLOCK_SIZE);
+    *ptok_out = partition_tokens ? partition_tokens
+                                 : shared_auto_partition(pool, num_groups, max_group, max_blocks_per_seq);
+    return PA_OK;
+}
+
+// Partitions per group at most, and the workspace: fp32 partials per
+// (sequence, query head) row and partition, then each group's partition count.
+size_t shared_workspace_for(const pa_pool_t *pool, int32_t num_seqs, int32_t num_q_heads,
+                            int32_t max_blocks_per_seq, int32_t num_groups, int32_t max_group, int32_t ptok,
+                            int32_t *nparts_out) {
+    const int64_t list_tokens = (int64_t)max_group * max_blocks_per_seq * PA_BLOCK_SIZE;
+    const int64_t np = (list_tokens + ptok - 1) / ptok;
+    if (nparts_out) *nparts_out = (int32_t)np;
+    if (np <= 1) return 0;
+    const int64_t rows = (int64_t)num_seqs * num_q_heads * np;
+    const int64_t acc = ((rows * pool->head_dim * 4 + 255) / 256) * 256;
+    const int64_t ml = ((rows * 4 + 255) / 256) * 256;
+    const int64_t cnt = (((int64_t)num_groups * 4 + 255) / 256) * 256;
+    return (size_t)(acc + 2 * ml + cnt);
+}
+
 // ---- debug mode: index checks before every operation -------------------
 
 std::atomic<int> g_debug{-1};  // -1 until PA_DEBUG has been read
@@ -496,6 +553,98 @@ int pa_decode_noalloc(const pa_pool_t *pool, const void *q, int32_t q_dtype, int
                        stream, /*checks=*/false);
 }
 
+size_t pa_decode_prefix_shared_workspace_size(const pa_pool_t *pool, int32_t num_seqs, int32_t num_q_heads,
+                                              int32_t max_blocks_per_seq, int32_t num_groups,
+                                              int32_t max_group_size, int32_t partition_tokens) {
+    int32_t ptok = 0;
+    if (check_shared_args(pool, num_seqs, num_q_heads, max_blocks_per_seq, num_groups, max_group_size,
+                          partition_tokens, &ptok) != PA_OK)
+        return 0;
+    return shared_workspace_for(pool, num_seqs, num_q_heads, max_blocks_per_seq, num_groups, max_group_size,
+                                ptok, nullptr);
+}
+
+int pa_decode_prefix_shared(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t num_seqs,
+                            int32_t num_q_heads, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                            const int32_t *context_lens, const int32_t *group_start,
+                            const int32_t *prefix_blocks, int32_t num_groups, int32_t max_group_size,
+                            float scale, float *out, int32_t partition_tokens, void *workspace,
+                            size_t workspace_bytes, uint32_t flags, void *stream) {
+    if (flags & ~(uint32_t)PA_DECODE_SHARED_KV)
+        return fail(PA_ERR_SHAPE, "unknown decode flags 0x%x", flags);
+    int32_t ptok = 0;
+    int rc = check_shared_args(pool, num_seqs, num_q_heads, max_blocks_per_seq, num_groups, max_group_size,
+                               partition_tokens, &ptok);
+    if (rc != PA_OK) return rc;
+    if (q_dtype != PA_BF16)
+        return fail(PA_ERR_DTYPE, "q_dtype %d: prefix-shared decode takes PA_BF16 queries", q_dtype);
+    if (!isfinite(scale)) return fail(PA_ERR_RANGE, "scale is not finite");
+    if (num_seqs == 0) return ok();
+    if (!q || !block_tables || !context_lens || !out || !group_start || !prefix_blocks)
+        return fail(PA_ERR_NULL, "q, block_tables, context_lens, group_start, prefix_blocks and out "
+                                 "must be non-NULL");
+    if (!aligned16(q) || !aligned16(out)) return fail(PA_ERR_ALIGN, "q and out must be 16-byte aligned");
+    int32_t np = 1;
+    const size_t need = shared_workspace_for(pool, num_seqs, num_q_heads, max_blocks_per_seq, num_groups,
+                                             max_group_size, ptok, &np);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (need > 0 && !aligned16(workspace)) return fail(PA_ERR_ALIGN, "workspace must be 16-byte aligned");
+
+    pa::DecodeParams p{};
+    p.k_pool = pool->k_pool;
+    p.v_pool = pool->v_pool;
+    p.q = q;
+    p.out = out;
+    p.block_tables = block_tables;
+    p.context_lens = context_lens;
+    p.num_blocks = pool->num_blocks;
+    p.num_kv_heads = pool->num_kv_heads;
+    p.num_q_heads = num_q_heads;
+    p.group = num_q_heads / pool->num_kv_heads;
+    p.num_seqs = num_seqs;
+    p.max_blocks_per_seq = max_blocks_per_seq;
+    p.partition_tokens = ptok;
+    p.group_parts = 1;
+    p.max_partitions = np;
+    const double kscale = pool->kv_dtype == PA_FP8_E4M3 ? (double)pool->k_scale : 1.0;
+    p.qk_scale_log2 = (float)((double)scale * kscale * 1.4426950408889634);
+    p.out_scale = pool->kv_dtype == PA_FP8_E4M3 ? pool->v_scale : 1.0f;
+    p.shared_kv = (flags & PA_DECODE_SHARED_KV) ? 1 : 0;
+    p.group_start = group_start;
+    p.prefix_blocks = prefix_blocks;
+    p.num_groups = num_groups;
+    p.max_group = max_group_size;
+    if (need > 0) {
+        const int64_t rows = (int64_t)num_seqs * num_q_heads * np;
+        char *ws = static_cast<char *>(workspace);
+        const int64_t acc = ((rows * pool->head_dim * 4 + 255) / 256) * 256;
+        const int64_t ml = ((rows * 4 + 255) / 256) * 256;
+        p.ws_acc = reinterpret_cast<float *>(ws);
+        p.ws_m = reinterpret_cast<float *>(ws + acc);
+        p.ws_l = reinterpret_cast<float *>(ws + acc + ml);
+        p.ws_nparts = reinterpret_cast<int32_t *>(ws + acc + 2 * ml);
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (debug_on()) {
+        rc = debug_check("pa_decode_prefix_shared", 0, st, [&](int32_t *report, void *) {
+            return pa::launch_check_tables(block_tables, context_lens, num_seqs, max_blocks_per_seq,
+                                           pool->num_blocks, report, st);
+        });
+        if (rc != PA_OK) return rc;
+    }
+    const pa::LaunchEvents ev{g_ev_before, g_ev_after};
+    g_ev_before = g_ev_after = nullptr;
+    hipError_t e = pa::launch_decode_shared(pool->kv_dtype, pool->head_dim, p, st, &ev);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "prefix-shared decode kernel: %s", hipGetErrorString(e));
+    if (np > 1) {
+        e = pa::launch_decode_shared_reduce(pool->head_dim, p, st);
+        if (e != hipSuccess) return fail(PA_ERR_HIP, "prefix-shared reduce kernel: %s", hipGetErrorString(e));
+    }
+    return ok();
+}
+
 int pa_decode_append(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t num_seqs,
                      int32_t num_q_heads, const int32_t *block_tables, int32_t max_blocks_per_seq,
                      const int32_t *context_lens, float scale, float *out, int32_t partition_tokens,
@@ -757,6 +906,23 @@ int pa_decode_variant(const pa_pool_t *pool, int32_t num_q_heads) {
     if (rc != PA_OK) return rc;
     return pa::mfma_path_supported(pool->kv_dtype, pool->head_dim,
                                    num_q_heads / pool->num_kv_heads) ? 1 : 0;
+}
+
+int pa_decode_plan(const pa_pool_t *pool, int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
+                   int32_t partition_tokens, int32_t plan[4]) {
+    int rc = check_pool(pool);
+    if (rc == PA_OK) rc = check_heads(pool, num_seqs, num_q_heads, max_blocks_per_seq);
+    if (rc != PA_OK) return rc;
+    if (!plan) return fail(PA_ERR_NULL, "plan is NULL");
+    int32_t ptok = 0;
+    rc = resolve_partition(pool, num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens, &ptok);
+    if (rc != PA_OK) return rc;
+    const Split sp = split_for(pool, num_seqs, num_q_heads, max_blocks_per_seq, ptok);
+    plan[0] = !grouped_kernel(pool, num_q_heads) ? 0 : (sp.mode == pa::kPartGroups ? 2 : 1);
+    plan[1] = ptok;
+    plan[2] = sp.slots;
+    plan[3] = sp.group_parts;
+    return ok();
 }
 
 int pa_set_profile_events(void *before, void *after) {

@@ -403,23 +403,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KV == 
 
 // Merge the partitions of one (sequence, query head) row, in partition order:
 // M = max_p m_p, out = sum_p acc_p 2^(m_p - M) / sum_p l_p 2^(m_p - M).
-// One wavefront per row (four rows per workgroup); lane i holds head dims
-// E*i .. E*i+E-1.  The partition weights are computed 64 at a time, one per
-// lane, and broadcast with readlane, so the partial numerators of eight
-// partitions are in flight at once; the first four are loaded with the
-// partition maxima and sums, before the merged maximum is known.
+// One wavefront per row; lane i holds head dims E*i .. E*i+E-1.  The
+// partition weights are computed 64 at a time, one per lane, and broadcast
+// with readlane, so the partial numerators of eight partitions are in flight
+// at once; the first four are loaded with the partition maxima and sums,
+// before the merged maximum is known.
 template <int D>
-__global__ __launch_bounds__(kThreads) void decode_reduce_kernel(DecodeParams p) {
+__device__ __forceinline__ void reduce_row(const DecodeParams &p, int64_t row, int nparts) {
     constexpr int E = D / 64;
     const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);  // s * Hq + h
-    if (row >= (int64_t)p.num_seqs * p.num_q_heads) return;
-    const int s = (int)(row / p.num_q_heads);
-    int ctx = p.context_lens[s];
-    ctx = ctx < 0 ? 0 : (ctx > p.max_blocks_per_seq * kBlock ? p.max_blocks_per_seq * kBlock : ctx);
-    const int unit = p.partition_tokens * p.group_parts;   // tokens per partial result
-    const int nparts = (ctx + unit - 1) / unit;
-    if (nparts <= 1) return;  // written by the partition kernel
     const float *ms = p.ws_m + row * p.max_partitions;
     const float *ls = p.ws_l + row * p.max_partitions;
     const float *as = p.ws_acc + row * p.max_partitions * D + E * lane;
@@ -461,7 +453,7 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_kernel(DecodeParams p)
     };
     if (M != kNegInf) {
         {   // partitions 0..63, the first PRE of them preloaded
-            const float f = lane < nparts ? exp2f(m0 - M) : 0.f;
+            const float f = lane < nparts && m0 != kNegInf ? exp2f(m0 - M) : 0.f;
             L += lane < nparts ? l0 * f : 0.f;
             const int cnt = min(64, nparts);
 #pragma unroll
@@ -479,7 +471,8 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_kernel(DecodeParams p)
         }
         for (int base = 64; base < nparts; base += 64) {
             const int i = base + lane;
-            const float f = i < nparts ? exp2f(ms[i] - M) : 0.f;
+            const float mi = i < nparts ? ms[i] : kNegInf;
+            const float f = mi != kNegInf ? exp2f(mi - M) : 0.f;
             L += i < nparts ? ls[i] * f : 0.f;
             const int cnt = min(64, nparts - base);
             int j = 0;
@@ -495,6 +488,41 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_kernel(DecodeParams p)
     float *dst = p.out + row * D + E * lane;
 #pragma unroll
     for (int e = 0; e < E; ++e) dst[e] = L > 0.f ? (O[e] / L) * p.out_scale : 0.f;
+}
+
+// One wavefront per (sequence, query head) row with more than one partial
+// result (four rows per workgroup).
+template <int D>
+__global__ __launch_bounds__(kThreads) void decode_reduce_kernel(DecodeParams p) {
+    const int64_t row = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);  // s * Hq + h
+    if (row >= (int64_t)p.num_seqs * p.num_q_heads) return;
+    const int s = (int)(row / p.num_q_heads);
+    int ctx = p.context_lens[s];
+    ctx = ctx < 0 ? 0 : (ctx > p.max_blocks_per_seq * kBlock ? p.max_blocks_per_seq * kBlock : ctx);
+    const int unit = p.partition_tokens * p.group_parts;   // tokens per partial result
+    const int nparts = (ctx + unit - 1) / unit;
+    if (nparts <= 1) return;  // written by the partition kernel
+    reduce_row<D>(p, row, nparts);
+}
+
+// The shared-prefix kernel's merge: one wavefront per (group, member, query
+// head) row of a group that had more than one partition (the partition
+// kernel recorded each group's count).
+template <int D>
+__global__ __launch_bounds__(kThreads) void decode_shared_reduce_kernel(DecodeParams p) {
+    const int per_group = p.max_group * p.num_q_heads;
+    const int r = (int)blockIdx.y * (kThreads / 64) + (threadIdx.x >> 6);
+    if (r >= per_group) return;
+    const int gi = blockIdx.x;
+    const int s0 = p.group_start[gi];
+    int M = p.group_start[gi + 1] - s0;
+    if (s0 < 0 || s0 >= p.num_seqs) M = 0;
+    M = M < 0 ? 0 : min(M, min(p.max_group, p.num_seqs - s0));
+    const int member = r / p.num_q_heads;
+    if (member >= M) return;
+    const int nparts = p.ws_nparts[gi];
+    if (nparts <= 1) return;  // written by the partition kernel
+    reduce_row<D>(p, (int64_t)(s0 + member) * p.num_q_heads + r % p.num_q_heads, min(nparts, p.max_partitions));
 }
 
 template <int KV, int D>
@@ -518,6 +546,16 @@ hipError_t launch_decode_valu(int kv, int head_dim, const DecodeParams &p, hipSt
     if (kv == kF32) return launch_valu_d<kF32>(head_dim, p, stream, ev);
     if (kv == kBF16) return launch_valu_d<kBF16>(head_dim, p, stream, ev);
     return launch_valu_d<kFP8>(head_dim, p, stream, ev);
+}
+
+hipError_t launch_decode_shared_reduce(int head_dim, const DecodeParams &p, hipStream_t stream) {
+    const int per_group = p.max_group * p.num_q_heads;
+    const dim3 grid((unsigned)p.num_groups, (unsigned)((per_group + kThreads / 64 - 1) / (kThreads / 64)));
+    if (head_dim == 64)
+        decode_shared_reduce_kernel<64><<<grid, dim3(kThreads), 0, stream>>>(p);
+    else
+        decode_shared_reduce_kernel<128><<<grid, dim3(kThreads), 0, stream>>>(p);
+    return hipGetLastError();
 }
 
 hipError_t launch_decode_reduce(int head_dim, const DecodeParams &p, hipStream_t stream) {

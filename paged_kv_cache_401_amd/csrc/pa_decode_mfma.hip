@@ -61,14 +61,38 @@ struct DecodeLds {
     uint32_t done;           // wavefronts of a partition group that have finished
 };
 
-// One wavefront's walk over its blocks j = jb + stride * k (k < nk) of
-// sequence s, KV head g, attending tokens below tok1 (its partition's end):
-// scores, online softmax and P.V accumulate into m (running maximum, base-2
-// domain), l (running sum, per-head total on return) and acc (numerators,
-// the MFMA C layout: lane (n, c) holds head n).  `writer`: this wavefront
-// reads the block holding position ctx - 1 and writes the decode step's
-// newest token (DecodeParams::k_new / v_new) into it (APPEND only); it stages
-// the token in tok_k / tok_v (LDS, 2 D bytes each).
+// Where a wavefront's blocks come from: blocks j = jb + stride * k (k < nk)
+// of one sequence's block table, tokens below tok1 (its partition's end)
+// attended by every column (query head).
+struct TableBlocks {
+    static constexpr bool kColumnMask = false;
+    const int32_t *table;   // the sequence's table row
+    int jb, stride, nk, tok1;
+    // the physical block of step k (-1 past the end)
+    __device__ __forceinline__ int32_t id(int k) const {
+        const int32_t b = table[jb + stride * min(k, nk - 1)];
+        return k < nk ? b : -1;
+    }
+    // its position in the sequence's table
+    __device__ __forceinline__ int block(int k) const { return jb + stride * k; }
+    // tokens of step k's block attended (>= 1; 16 or more: all of them) and
+    // the columns [lo, hi) that attend it
+    __device__ __forceinline__ void mask(int k, int &nvalid, int &lo, int &hi) const {
+        nvalid = tok1 - block(k) * kBlock;
+        lo = 0;
+        hi = 16;
+    }
+};
+
+// One wavefront's walk over the blocks of `src` for KV head g: scores,
+// online softmax and P.V accumulate into m (running maximum, base-2 domain),
+// l (running sum, per-column total on return) and acc (numerators, the MFMA
+// C layout: lane (n, c) holds column n).  Column n is the query row qcol of
+// this lane (nullptr: an unused column, zero query); the first ncols
+// columns are real.  `writer`: this wavefront reads the block holding
+// position ctx - 1 of sequence s and writes the decode step's newest token
+// (DecodeParams::k_new / v_new) into it (APPEND only); it stages the token
+// in tok_k / tok_v (LDS, 2 D bytes each).
 //
 // The newest token: the writer loads the token's inputs before its block
 // loads and stages them in LDS, encoded as the pool stores them; when the
@@ -77,10 +101,10 @@ struct DecodeLds {
 // them to the pool.  Stores issued before later loads would make every wait
 // on those loads wait for the stores as well (one counter covers both, in
 // issue order), and under full read traffic stores are slow.
-template <int KV, int D, bool STREAM, bool APPEND>
-__device__ __forceinline__ void walk_blocks(const DecodeParams &p, int s, int g, int jb, int stride,
-                                            int nk, int tok1, int ctx, bool writer, uint8_t *tok_k,
-                                            uint8_t *tok_v, float &m, float &l,
+template <int KV, int D, bool STREAM, bool APPEND, class Src>
+__device__ __forceinline__ void walk_blocks(const DecodeParams &p, int s, int g, const Src &src,
+                                            const uint16_t *qcol, int ncols, int ctx, bool writer,
+                                            uint8_t *tok_k, uint8_t *tok_v, float &m, float &l,
                                             floatx4 (&acc)[D / 16]) {
     constexpr int EB = KV == kBF16 ? 2 : 1;
     constexpr int TILE_BYTES = kBlock * D * EB;
@@ -93,16 +117,15 @@ __device__ __forceinline__ void walk_blocks(const DecodeParams &p, int s, int g,
     const int lane = threadIdx.x & 63;
     const int n = lane & 15;
     const int c = lane >> 4;
-    const int G = p.group;
     const int32_t *table = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
     const int tn = (ctx - 1) & (kBlock - 1);   // the newest token's slot in its block
     const int jlast = (ctx - 1) / kBlock;      // ... and its block
+    const int nk = src.nk;
 
-    // Q^T operands: head g*G + n (zero for n >= G), head dims per the K mapping
+    // Q^T operands: column n's query row (zero for unused columns), head dims
+    // per the K mapping
     bf16x8 qop[NQK];
     {
-        const uint16_t *qrow = reinterpret_cast<const uint16_t *>(p.q) +
-                               ((int64_t)s * p.num_q_heads + (int64_t)g * G + n) * D;
 #pragma unroll
         for (int u = 0; u < NQK; ++u) {
             int d0;
@@ -111,7 +134,7 @@ __device__ __forceinline__ void walk_blocks(const DecodeParams &p, int s, int g,
             else
                 d0 = 16 * (c + 4 * (u >> 1)) + 8 * (u & 1);
             u32x4 v = {0u, 0u, 0u, 0u};
-            if (n < G) v = *reinterpret_cast<const u32x4 *>(qrow + d0);
+            if (qcol) v = *reinterpret_cast<const u32x4 *>(qcol + d0);
             qop[u] = as_bf16x8(v);
         }
     }
@@ -178,27 +201,36 @@ __device__ __forceinline__ void walk_blocks(const DecodeParams &p, int s, int g,
         return sacc;
     };
 
-    // online softmax and O^T += V^T . P^T for block j
-    auto softmax_pv = [&](floatx4 sacc, const u32x4 (&vr)[NVL], int j) {
-        // online softmax over this block (tokens 4c..4c+3 of head n in this lane)
-        const int nvalid = tok1 - j * kBlock;       // >= 1
+    // online softmax and O^T += V^T . P^T for a block whose first nvalid
+    // tokens are attended by columns [lo, hi)
+    auto softmax_pv = [&](floatx4 sacc, const u32x4 (&vr)[NVL], int nvalid, int lo, int hi) {
+        // online softmax over this block (tokens 4c..4c+3 of column n in this lane)
         float sc[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             sc[i] = sacc[i] * p.qk_scale_log2;
             if (4 * c + i >= nvalid) sc[i] = kNegInf;
+            if constexpr (Src::kColumnMask) {
+                if (n < lo || n >= hi) sc[i] = kNegInf;
+            }
         }
         float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
         bm = max_xor32(max_xor16(bm));
         const float m_new = fmaxf(m, bm);
-        const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+        // A masked column may meet a block before any token it attends: its
+        // maximum is still -inf, and -inf - (-inf) would be NaN; exponents
+        // against 0 keep its sum and numerators at 0.  (With every column
+        // attending every block, the first block makes every maximum finite.)
+        float m_ref = m_new;
+        if constexpr (Src::kColumnMask) m_ref = m_new == kNegInf ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m - m_ref);
         float pr[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(sc[i] - m_new);
+        for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(sc[i] - m_ref);
         m = m_new;
         l = l * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-        // rescale the numerators only when some real head's maximum moved
-        if (__builtin_amdgcn_ballot_w64(n < G && alpha != 1.f) != 0) {
+        // rescale the numerators only when some real column's maximum moved
+        if (__builtin_amdgcn_ballot_w64(n < ncols && alpha != 1.f) != 0) {
 #pragma unroll
             for (int t = 0; t < NT; ++t) acc[t] *= alpha;
         }
@@ -245,11 +277,7 @@ __device__ __forceinline__ void walk_blocks(const DecodeParams &p, int s, int g,
     // issues the same loads (empty resources past the end), which lets each
     // wait cover exactly the loads it needs.
     if (nk > 0) {
-        const int32_t *wtable = table + jb;
-        auto id_at = [&](int k) -> int32_t {
-            const int32_t b = wtable[stride * min(k, nk - 1)];
-            return k < nk ? b : -1;
-        };
+        auto id_at = [&](int k) -> int32_t { return src.id(k); };
         // the newest token's inputs go out first (lane elements lane + 64 i)
         NewToken<D> nt;
         if (APPEND && writer) nt = append_load<KV, D>(p, table, s, g, ctx - 1, lane);
@@ -322,10 +350,14 @@ __device__ __forceinline__ void walk_blocks(const DecodeParams &p, int s, int g,
         auto step = [&](int d, int kk) {
             const int32_t id_after = id_pre;  // block kk + 2
             id_pre = id_at(kk + 3);
-            if (APPEND && writer && jb + stride * kk == jlast) patch(kb[d], vb[d]);
+            if (APPEND && writer && src.block(kk) == jlast) patch(kb[d], vb[d]);
             const floatx4 sacc = qk(kb[d]);
             load_k(id_after, kb[d], kFree);
-            if (valid(idb[d])) softmax_pv(sacc, vb[d], jb + stride * kk);
+            if (valid(idb[d])) {
+                int nvalid, lo, hi;
+                src.mask(kk, nvalid, lo, hi);
+                softmax_pv(sacc, vb[d], nvalid, lo, hi);
+            }
             load_v(id_after, vb[d], kFree);
             idb[d] = id_after;
         };
@@ -371,6 +403,15 @@ __device__ __forceinline__ void walk_blocks(const DecodeParams &p, int s, int g,
     l = add_xor32(add_xor16(l));
 }
 
+// This lane's query row for column n = lane % 16 of sequence s, KV head g:
+// query head g G + n, none for n >= G.
+template <int D>
+__device__ __forceinline__ const uint16_t *query_column(const DecodeParams &p, int s, int g) {
+    const int n = threadIdx.x & 15;
+    if (n >= p.group) return nullptr;
+    return reinterpret_cast<const uint16_t *>(p.q) + ((int64_t)s * p.num_q_heads + (int64_t)g * p.group + n) * D;
+}
+
 // One wavefront's (m, l, numerators) to slot `w` of the workgroup's LDS, in
 // [w][d][head] order.
 template <int D, int NW, int W>
@@ -396,11 +437,12 @@ __device__ __forceinline__ void state_to_lds(DecodeLds<D, NW> &sm, int w, float 
             }
 }
 
-// Merge the first `nw` wavefront states in LDS and write the result:
-// threads t0, t0 + tstride, ... each take 4 consecutive head dims of one
-// head and store them with one 16-byte store -- the final output row
-// (divided by the sum, times the value scale) when `final`, else the partial
-// (numerators, maximum, sum) of slot `slot` of the row.  The stores that end
+// Merge the first `nw` wavefront states in LDS and write the result of
+// columns 0 .. ncols-1, column hh being query head g G + hh % G of sequence
+// s + hh / G: threads t0, t0 + tstride, ... each take 4 consecutive head
+// dims of one column and store them with one 16-byte store -- the final
+// output row (divided by the sum, times the value scale) when `final`, else
+// the partial (numerators, maximum, sum) of slot `slot` of the row.  The stores that end
 // a work item cost far more than their bytes while the chip streams K/V
 // (timed on MI355X: the 512-token fp8 long-tail batch ran 20 % faster with
 // them switched off), so there are 4x fewer of them than with one per dim.
@@ -409,11 +451,11 @@ __device__ __forceinline__ void state_to_lds(DecodeLds<D, NW> &sm, int w, float 
 template <int D, int NW>
 __device__ __forceinline__ void merge_and_store(const DecodeParams &p, const DecodeLds<D, NW> &sm, int s,
                                                 int g, int slot, bool final, int nw, int t0,
-                                                int tstride) {
+                                                int tstride, int ncols) {
     constexpr int LDS_STRIDE = 17;
     constexpr int D4 = D / 4;
     const int G = p.group;
-    for (int idx = t0; idx < G * D4; idx += tstride) {
+    for (int idx = t0; idx < ncols * D4; idx += tstride) {
         const int hh = idx / D4;
         const int d0 = 4 * (idx % D4);
         float M = sm.m[0][hh];
@@ -426,7 +468,7 @@ __device__ __forceinline__ void merge_and_store(const DecodeParams &p, const Dec
 #pragma unroll
             for (int e = 0; e < 4; ++e) O[e] += sm.acc[w][(d0 + e) * LDS_STRIDE + hh] * f;
         }
-        const int64_t row = (int64_t)s * p.num_q_heads + (int64_t)g * G + hh;
+        const int64_t row = (int64_t)(s + hh / G) * p.num_q_heads + (int64_t)g * G + hh % G;
         if (final) {
             float r[4];
 #pragma unroll
@@ -465,13 +507,14 @@ __device__ __forceinline__ void decode_item(const DecodeParams &p, int s, int g,
     // this KV head)
     const bool writer = APPEND && !clamped && tok1 == ctx && ctx > 0 && wv == (blk1 - 1 - blk0) % NW;
     const int nk = blk1 - blk0 > wv ? (blk1 - blk0 - wv + NW - 1) / NW : 0;
+    const TableBlocks src{p.block_tables + (int64_t)s * p.max_blocks_per_seq, blk0 + wv, NW, nk, tok1};
     float m, l;
     floatx4 acc[D / 16];
-    walk_blocks<KV, D, STREAM, APPEND>(p, s, g, blk0 + wv, NW, nk, tok1, ctx, writer, sm.tok_k,
-                                       sm.tok_v, m, l, acc);
+    walk_blocks<KV, D, STREAM, APPEND>(p, s, g, src, query_column<D>(p, s, g), p.group, ctx, writer,
+                                       sm.tok_k, sm.tok_v, m, l, acc);
     state_to_lds<D, NW, W>(sm, wv, m, l, acc);
     __syncthreads();
-    merge_and_store<D, NW>(p, sm, s, g, part, nparts <= 1, NW, threadIdx.x, 64 * NW);
+    merge_and_store<D, NW>(p, sm, s, g, part, nparts <= 1, NW, threadIdx.x, 64 * NW, p.group);
 }
 
 __device__ __forceinline__ int clamp_ctx(const DecodeParams &p, int ctx) {
@@ -541,10 +584,11 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(3))) vo
     const int blk1 = (tok1 + kBlock - 1) / kBlock;
     // the newest token is written by the wavefront whose partition holds it
     const bool writer = APPEND && raw_ctx == ctx && tok1 == ctx && ctx > 0;
+    const TableBlocks src{p.block_tables + (int64_t)s * p.max_blocks_per_seq, blk0, 1, blk1 - blk0, tok1};
     float m, l;
     floatx4 acc[D / 16];
-    walk_blocks<KV, D, STREAM, APPEND>(p, s, g, blk0, 1, blk1 - blk0, tok1, ctx, writer, sm.tok_k,
-                                       sm.tok_v, m, l, acc);
+    walk_blocks<KV, D, STREAM, APPEND>(p, s, g, src, query_column<D>(p, s, g), p.group, ctx, writer,
+                                       sm.tok_k, sm.tok_v, m, l, acc);
     state_to_lds<D, NG, W>(sm, wv, m, l, acc);
     // this wavefront's state is in LDS before it counts itself as done; the
     // last one to count sees every other state
@@ -555,7 +599,139 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(3))) vo
     before = __builtin_amdgcn_readfirstlane(before);
     if (before != (uint32_t)(nreal - 1)) return;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    merge_and_store<D, NG>(p, sm, s, g, grp, ngroups <= 1, nreal, threadIdx.x & 63, 64);
+    merge_and_store<D, NG>(p, sm, s, g, grp, ngroups <= 1, nreal, threadIdx.x & 63, 64, p.group);
+}
+
+// Blocks of one partition of a prefix-sharing group, from the list its
+// workgroup built in LDS: entry v names the physical block and which tokens
+// and columns attend it ((first column << 16) | (end column << 8) | tokens).
+// The wavefront takes entries jb + stride k (k < nk).
+struct ListBlocks {
+    static constexpr bool kColumnMask = true;
+    const int32_t *ids;
+    const int32_t *info;
+    int jb, stride, nk;
+    __device__ __forceinline__ int32_t id(int k) const {
+        const int32_t b = __builtin_amdgcn_readfirstlane(ids[jb + stride * min(k, nk - 1)]);
+        return k < nk ? b : -1;
+    }
+    __device__ __forceinline__ int block(int) const { return -1; }
+    __device__ __forceinline__ void mask(int k, int &nvalid, int &lo, int &hi) const {
+        const int x = __builtin_amdgcn_readfirstlane(info[jb + stride * k]);
+        nvalid = x & 0xff;
+        hi = (x >> 8) & 0xff;
+        lo = x >> 16;
+    }
+};
+
+template <int D, int NW>
+struct SharedLds {
+    DecodeLds<D, NW> st;
+    int32_t ids[kSharedListMax];
+    int32_t info[kSharedListMax];
+    int32_t member_ctx[16];
+    int32_t member_cum[17];   // suffix blocks of the members before member m
+};
+
+// Decode of prefix-sharing groups: one workgroup of NW wavefronts per
+// (group, KV head, partition) slot of a (groups x KV heads) x max_partitions
+// grid (work order as above).  The members of a group hold the same first
+// pb blocks in their tables -- a prompt shared by parallel samples or beams,
+// a cached system prompt (glossary page, sharing blocks between sequences).
+// Every query head of every member is a column of one 16-column matrix-core
+// tile (members x G <= 16), so each shared block is read once for the whole
+// group; each member's own blocks after the shared ones are attended by that
+// member's columns only (the others' scores are -inf there).  The group's
+// blocks, shared ones first, then member 0's own, member 1's, ..., form a
+// list cut into partitions of partition_tokens / 16 blocks; the workgroup
+// lists its partition's blocks in LDS and its wavefronts take every NW-th
+// entry.  A group with one partition writes its output rows at once, else
+// one partial per member row for the shared reduce kernel.
+template <int KV, int D, bool STREAM, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) void decode_shared_kernel(DecodeParams p) {
+    __shared__ SharedLds<D, NW> sm;
+    constexpr int W = KV == kBF16 ? 2 : 4;
+    int bid, part;
+    pair_and_partition(p.num_groups * p.num_kv_heads, p.max_partitions, bid, part);
+    const int gi = bid / p.num_kv_heads;
+    const int g = bid % p.num_kv_heads;
+    const int G = p.group;
+    const int lane = threadIdx.x & 63;
+    const int cap = p.max_blocks_per_seq * kBlock;
+    // the group's members (device data: clamped to the batch and max_group)
+    const int s0 = p.group_start[gi];
+    int M = p.group_start[gi + 1] - s0;
+    if (s0 < 0 || s0 >= p.num_seqs) M = 0;
+    M = M < 0 ? 0 : min(M, min(p.max_group, p.num_seqs - s0));
+    M = __builtin_amdgcn_readfirstlane(M);
+    if (M == 0) return;
+    // members' context lengths, the shared whole blocks (at most what every
+    // member holds) and each member's own blocks after them
+    int myctx = 0x7fffffff;
+    if (lane < M) {
+        const int c = p.context_lens[s0 + lane];
+        myctx = c < 0 ? 0 : (c > cap ? cap : c);
+    }
+    int minctx = myctx;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) minctx = min(minctx, __shfl_xor(minctx, o));
+    minctx = __builtin_amdgcn_readfirstlane(minctx);
+    int pb = p.prefix_blocks[gi];
+    pb = __builtin_amdgcn_readfirstlane(max(0, min(pb, minctx / kBlock)));
+    const int own = lane < M ? (myctx + kBlock - 1) / kBlock - pb : 0;
+    int cum = own;   // inclusive prefix sum over members
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+        const int t = __shfl_up(cum, o);
+        if (lane >= o) cum += t;
+    }
+    const int total = pb + __builtin_amdgcn_readlane(cum, 15);
+    const int B = p.partition_tokens / kBlock;
+    const int nparts = (total + B - 1) / B;
+    if (part >= (nparts > 1 ? nparts : 1)) return;   // the whole workgroup
+    if (threadIdx.x < 16) {
+        sm.member_ctx[threadIdx.x] = lane < M ? myctx : 0;
+        sm.member_cum[threadIdx.x] = cum - own;   // exclusive
+    }
+    if (threadIdx.x == 16) sm.member_cum[16] = total - pb;
+    if (part == 0 && g == 0 && threadIdx.x == 0 && p.ws_nparts) p.ws_nparts[gi] = nparts;
+    __syncthreads();
+    // this partition's blocks: shared ones (every member's columns) or
+    // member m's own (its columns), with the tokens attended
+    const int v0 = part * B;
+    const int nv = min(total, v0 + B) - v0;
+    const int32_t *tables = p.block_tables;
+    for (int t = threadIdx.x; t < nv; t += 64 * NW) {
+        const int v = v0 + t;
+        int mem = 0, j = v, lo = 0, hi = M * G, nvalid = kBlock;
+        if (v >= pb) {
+            const int u = v - pb;
+            for (int mm = 1; mm < M; ++mm)
+                if (u >= sm.member_cum[mm]) mem = mm;
+            j = pb + u - sm.member_cum[mem];
+            lo = mem * G;
+            hi = lo + G;
+            nvalid = min(kBlock, sm.member_ctx[mem] - j * kBlock);
+        }
+        sm.ids[t] = tables[(int64_t)(s0 + mem) * p.max_blocks_per_seq + j];
+        sm.info[t] = (lo << 16) | (hi << 8) | nvalid;
+    }
+    __syncthreads();
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nk = nv > wv ? (nv - wv + NW - 1) / NW : 0;
+    const ListBlocks src{sm.ids, sm.info, wv, NW, nk};
+    // column n: query head g G + n % G of member n / G
+    const int n = lane & 15;
+    const uint16_t *qcol = n < M * G ? reinterpret_cast<const uint16_t *>(p.q) +
+                                           ((int64_t)(s0 + n / G) * p.num_q_heads + (int64_t)g * G + n % G) * D
+                                     : nullptr;
+    float m, l;
+    floatx4 acc[D / 16];
+    walk_blocks<KV, D, STREAM, false>(p, s0, g, src, qcol, M * G, 1, false, sm.st.tok_k, sm.st.tok_v, m, l,
+                                      acc);
+    state_to_lds<D, NW, W>(sm.st, wv, m, l, acc);
+    __syncthreads();
+    merge_and_store<D, NW>(p, sm.st, s0, g, part, nparts <= 1, NW, threadIdx.x, 64 * NW, M * G);
 }
 
 template <int KV, int D, bool STREAM, bool APPEND>
@@ -584,7 +760,23 @@ hipError_t launch(const DecodeParams &p, hipStream_t stream, const LaunchEvents 
                   : launch_variant<KV, D, true, false>(p, grid, stream, ev);
 }
 
+template <int KV, int D>
+hipError_t launch_shared(const DecodeParams &p, hipStream_t stream, const LaunchEvents *ev) {
+    const int64_t grid = (int64_t)p.num_groups * p.num_kv_heads * p.max_partitions;
+    if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+    const dim3 g((unsigned)grid), b(256);
+    if (p.shared_kv) return launch_kernel(decode_shared_kernel<KV, D, false, 4>, g, b, stream, ev, p);
+    return launch_kernel(decode_shared_kernel<KV, D, true, 4>, g, b, stream, ev, p);
+}
+
 }  // namespace
+
+hipError_t launch_decode_shared(int kv, int head_dim, const DecodeParams &p, hipStream_t stream,
+                                const LaunchEvents *ev) {
+    if (kv == kBF16)
+        return head_dim == 64 ? launch_shared<kBF16, 64>(p, stream, ev) : launch_shared<kBF16, 128>(p, stream, ev);
+    return head_dim == 64 ? launch_shared<kFP8, 64>(p, stream, ev) : launch_shared<kFP8, 128>(p, stream, ev);
+}
 
 bool mfma_path_supported(int kv, int head_dim, int group) {
     return (kv == kBF16 || kv == kFP8) && (head_dim == 64 || head_dim == 128) && group >= 2 &&

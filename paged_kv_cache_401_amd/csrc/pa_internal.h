@@ -55,7 +55,19 @@ struct DecodeParams {
     int32_t new_dtype;         // kBF16 or kF32 (the pool's dtype unless fp8)
     float inv_k_scale;         // fp32(1 / k_scale), fp8 pools only
     float inv_v_scale;
+    // groups of sequences sharing the first blocks of their tables (the
+    // shared-prefix kernel only): members of group i are sequences
+    // group_start[i] .. group_start[i+1]-1, sharing prefix_blocks[i] blocks
+    const int32_t *group_start;   // [num_groups + 1]
+    const int32_t *prefix_blocks; // [num_groups]
+    int32_t num_groups;
+    int32_t max_group;            // members per group at most (max_group * group <= 16)
+    int32_t *ws_nparts;           // [num_groups] partitions of each group (split runs only)
 };
+
+// Blocks per partition of the shared-prefix kernel at most: a workgroup
+// lists its partition's blocks in LDS.
+constexpr int kSharedListMax = 512;
 
 struct PrefillParams {
     const void *k_pool;
@@ -117,6 +129,10 @@ hipError_t launch_decode_mfma(int kv, int head_dim, const DecodeParams &p, hipSt
                               const LaunchEvents *ev = nullptr);
 bool mfma_path_supported(int kv, int head_dim, int group);
 hipError_t launch_decode_reduce(int head_dim, const DecodeParams &p, hipStream_t stream);
+// decode of prefix-sharing groups (matrix-core), and its split-K merge
+hipError_t launch_decode_shared(int kv, int head_dim, const DecodeParams &p, hipStream_t stream,
+                                const LaunchEvents *ev = nullptr);
+hipError_t launch_decode_shared_reduce(int head_dim, const DecodeParams &p, hipStream_t stream);
 // each sequence's newest token (p.k_new / p.v_new) to the slot of position
 // context_len - 1, as a kernel of its own
 hipError_t launch_append_tokens(int kv, int head_dim, const DecodeParams &p, hipStream_t stream);

@@ -23,11 +23,12 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 
 # every symbol include/pa.h declares
 EXPORTS = ("pa_pool_bytes", "pa_decode_partition_tokens", "pa_decode_workspace_size", "pa_decode",
-           "pa_decode_ex", "pa_decode_noalloc", "pa_decode_append",
+           "pa_decode_ex", "pa_decode_noalloc", "pa_decode_append", "pa_decode_prefix_shared",
+           "pa_decode_prefix_shared_workspace_size",
            "pa_prefill", "pa_reshape_and_cache", "pa_swap_blocks", "pa_copy_blocks",
            "pa_check_workspace_size", "pa_check_tables", "pa_check_query_start", "pa_check_slots",
            "pa_check_copy_pairs", "pa_check_swap_pairs", "pa_set_debug",
-           "pa_decode_variant", "pa_set_profile_events",
+           "pa_decode_variant", "pa_decode_plan", "pa_set_profile_events",
            "pa_probe_read", "pa_strerror", "pa_last_error", "pa_build_info")
 
 # index fault kinds of the pa_check_* reports (PA_FAULT_* in pa.h)
@@ -76,6 +77,11 @@ def lib() -> ctypes.CDLL:
     L.pa_decode_ex.restype = ctypes.c_int
     L.pa_decode_noalloc.argtypes = [PD, P, I32, I32, I32, P, I32, P, F, P, I32, ctypes.c_uint32, P]
     L.pa_decode_noalloc.restype = ctypes.c_int
+    L.pa_decode_prefix_shared.argtypes = [PD, P, I32, I32, I32, P, I32, P, P, P, I32, I32, F, P, I32, P,
+                                          SZ, ctypes.c_uint32, P]
+    L.pa_decode_prefix_shared.restype = ctypes.c_int
+    L.pa_decode_prefix_shared_workspace_size.argtypes = [PD, I32, I32, I32, I32, I32, I32]
+    L.pa_decode_prefix_shared_workspace_size.restype = SZ
     L.pa_decode_append.argtypes = [PD, P, I32, I32, I32, P, I32, P, F, P, I32, P, SZ, ctypes.c_uint32,
                                    P, P, I32, P]
     L.pa_decode_append.restype = ctypes.c_int
@@ -103,6 +109,8 @@ def lib() -> ctypes.CDLL:
     L.pa_set_debug.restype = ctypes.c_int
     L.pa_decode_variant.argtypes = [PD, I32]
     L.pa_decode_variant.restype = ctypes.c_int
+    L.pa_decode_plan.argtypes = [PD, I32, I32, I32, I32, P]
+    L.pa_decode_plan.restype = ctypes.c_int
     L.pa_set_profile_events.argtypes = [P, P]
     L.pa_set_profile_events.restype = ctypes.c_int
     L.pa_probe_read.argtypes = [P, SZ, P, P]
@@ -280,6 +288,55 @@ def decode(pool: KVPool, q: torch.Tensor, block_tables: torch.Tensor, context_le
     return out
 
 
+def decode_prefix_shared_workspace_size(pool: KVPool, num_seqs, num_q_heads, max_blocks_per_seq,
+                                        num_groups, max_group_size, partition_tokens=0) -> int:
+    d = pool.desc()
+    return int(lib().pa_decode_prefix_shared_workspace_size(
+        ctypes.byref(d), int(num_seqs), int(num_q_heads), int(max_blocks_per_seq), int(num_groups),
+        int(max_group_size), int(partition_tokens)))
+
+
+def decode_prefix_shared(pool: KVPool, q: torch.Tensor, block_tables: torch.Tensor,
+                         context_lens: torch.Tensor, group_start: torch.Tensor,
+                         prefix_blocks: torch.Tensor, max_group_size: int, scale: float,
+                         out: torch.Tensor | None = None, partition_tokens: int = 0,
+                         workspace: torch.Tensor | None = None, stream=None,
+                         shared_kv: bool = False) -> torch.Tensor:
+    """pa_decode_prefix_shared: decode of a batch in groups of consecutive
+    sequences that share their first ``prefix_blocks[i]`` table entries
+    (``group_start`` int32 [G + 1] and ``prefix_blocks`` int32 [G] on the GPU,
+    e.g. from ``blocks.prefix_groups``)."""
+    S, Hq, D = q.shape
+    if D != pool.head_dim:
+        raise ValueError("q head dim %d differs from the pool's %d" % (D, pool.head_dim))
+    if q.dtype != torch.bfloat16:
+        raise TypeError("q must be bfloat16")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.numel() != S:
+        raise ValueError("block_tables must be [num_seqs][max_blocks]; context_lens [num_seqs]")
+    G = prefix_blocks.numel()
+    if group_start.numel() != G + 1:
+        raise ValueError("group_start must hold num_groups + 1 offsets")
+    mbs = block_tables.shape[1]
+    if out is None:
+        out = torch.empty((S, Hq, D), dtype=torch.float32, device=q.device)
+    elif tuple(out.shape) != (S, Hq, D):
+        raise ValueError("out must be [num_seqs][num_q_heads][head_dim] = %s, got %s"
+                         % ((S, Hq, D), tuple(out.shape)))
+    d = pool.desc()
+    need = decode_prefix_shared_workspace_size(pool, S, Hq, mbs, G, max_group_size, partition_tokens)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wptr = workspace.data_ptr() if workspace is not None else None
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    flags = DECODE_SHARED_KV if shared_kv else DECODE_STREAM_KV
+    _check(lib().pa_decode_prefix_shared(
+        ctypes.byref(d), _dev(q, "q"), BF16, S, Hq, _dev(block_tables, "block_tables", torch.int32), mbs,
+        _dev(context_lens, "context_lens", torch.int32), _dev(group_start, "group_start", torch.int32),
+        _dev(prefix_blocks, "prefix_blocks", torch.int32), G, int(max_group_size), float(scale),
+        _dev(out, "out", torch.float32), int(partition_tokens), wptr, wbytes, flags, _stream(stream)))
+    return out
+
+
 def decode_noalloc(pool: KVPool, q: torch.Tensor, block_tables: torch.Tensor,
                    context_lens: torch.Tensor, scale: float, out: torch.Tensor,
                    partition_tokens: int = 0, stream=None, shared_kv: bool = False) -> torch.Tensor:
@@ -412,6 +469,20 @@ def decode_variant(pool: KVPool, num_q_heads: int) -> str:
     if r < 0:
         raise PAError(r, lib().pa_last_error().decode())
     return "decode_mfma_kernel" if r == 1 else "decode_valu_kernel"
+
+
+DECODE_KERNELS = ("decode_valu_kernel", "decode_mfma_kernel", "decode_group_kernel")
+
+
+def decode_plan(pool: KVPool, num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens=0) -> dict:
+    """The launch pa_decode_ex makes: its partition kernel, partition tokens,
+    partial results per row and partitions merged into each."""
+    plan = (ctypes.c_int32 * 4)()
+    d = pool.desc()
+    _check(lib().pa_decode_plan(ctypes.byref(d), int(num_seqs), int(num_q_heads),
+                                int(max_blocks_per_seq), int(partition_tokens), plan))
+    return {"kernel": DECODE_KERNELS[plan[0]], "partition_tokens": plan[1],
+            "partials_per_row": plan[2], "partitions_per_partial": plan[3]}
 
 
 def set_profile_events(before, after) -> None:

@@ -511,9 +511,63 @@ def _sampling(name, small, device, seed, rng, num_prompts=None) -> Workload:
                  scale=_f32(1.0 / math.sqrt(D)), ops=ops, step_k=step_k, step_v=step_v,
                  step_slots=step_slots.astype(np.int32) if Nc else None)
     w.info.update(shared_kv=True, manager=mgr, prompt_len=prompt, continuation=cont,
-                  shared_prompt_blocks=shared_blocks,
+                  shared_prompt_blocks=shared_blocks, group_sizes=[n] * P,
                   physical_blocks=mgr.physical_blocks_in_use(),
                   logical_blocks=mgr.logical_blocks(), cow_pairs=len(cow))
+    return w
+
+
+def make_groups_workload(groups, Hq: int, Hkv: int, D: int = 128, pool_dtype: int = BF16,
+                         seed: int = 0, device="cpu", name: str = "groups") -> Workload:
+    """Groups of sequences forked from shared prompts: ``groups`` lists
+    (prompt tokens, [continuation tokens of each member]).  Each prompt is
+    written once; its members fork it (sharing its blocks, with reference
+    counts) and append their continuations, the first writers into a shared
+    partly filled block copying it first (glossary page, sharing blocks
+    between sequences).  Sequences are numbered group by group;
+    ``info["group_sizes"]`` holds the member counts.  bf16 inputs; an fp8
+    pool gets per-pool scales (max |x| / 448)."""
+    rng = np.random.default_rng(seed)
+    nb = int(sum(blocks_for(pl) + sum(blocks_for(pl + c) + 1 for c in cs) for pl, cs in groups))
+    mgr = BlockManager(nb, free_list=rng.permutation(nb))
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    pslots = []
+    for gi, (pl, _) in enumerate(groups):
+        mgr.add_sequence(("prompt", gi))
+        sl, _ = mgr.append_tokens(("prompt", gi), int(pl))
+        pslots.extend(sl)
+    seqs = [(gi, j) for gi, (_, cs) in enumerate(groups) for j in range(len(cs))]
+    q = _randn(gen, (len(seqs), Hq, D), torch.bfloat16, device)
+    kp = _randn(gen, (len(pslots), Hkv, D), torch.bfloat16, device)
+    vp = _randn(gen, (len(pslots), Hkv, D), torch.bfloat16, device)
+    ops = [("write", kp, vp, np.asarray(pslots, dtype=np.int32))]
+    for gi, (_, cs) in enumerate(groups):
+        for j in range(len(cs)):
+            mgr.fork(("prompt", gi), (gi, j))
+        mgr.free_sequence(("prompt", gi))
+    cslots, cow = [], []
+    for gi, (_, cs) in enumerate(groups):
+        for j, c in enumerate(cs):
+            sl, pairs = mgr.append_tokens((gi, j), int(c))
+            cslots.extend(sl)
+            cow.extend(pairs)
+    if cow:
+        ops.append(("copy", np.asarray(cow, dtype=np.int32).reshape(-1, 2)))
+    kc = _randn(gen, (len(cslots), Hkv, D), torch.bfloat16, device)
+    vc = _randn(gen, (len(cslots), Hkv, D), torch.bfloat16, device)
+    if cslots:
+        ops.append(("write", kc, vc, np.asarray(cslots, dtype=np.int32)))
+    k_scale = v_scale = 1.0
+    if pool_dtype == FP8:
+        k_scale = float((torch.cat([kp, kc]).abs().max().float() / 448.0).item())
+        v_scale = float((torch.cat([vp, vc]).abs().max().float() / 448.0).item())
+    ctx = np.asarray([mgr.length(sq) for sq in seqs], dtype=np.int32)
+    w = Workload(name=name, S=len(seqs), Hq=Hq, Hkv=Hkv, D=D, pool_dtype=pool_dtype, q_dtype=BF16,
+                 kv_in_dtype=BF16, num_blocks=nb, context_lens=ctx,
+                 block_tables=_tables_from(mgr, seqs), q=q, scale=_f32(1.0 / math.sqrt(D)),
+                 k_scale=k_scale, v_scale=v_scale, ops=ops)
+    w.info.update(manager=mgr, group_sizes=[len(cs) for _, cs in groups], cow_pairs=len(cow))
     return w
 
 

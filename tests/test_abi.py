@@ -269,3 +269,49 @@ def test_decode_rejects_misaligned_out():
     assert L.pa_decode(ctypes.byref(d), 16, ops.BF16, 1, 8, 16, 4, 16, 0.1, 20, 0, None, 0,
                        None) == -6
     assert b"out" in L.pa_last_error()
+
+
+def test_decode_prefix_shared_argument_rules():
+    """Host-side checks of the prefix-shared decode, before touching the GPU."""
+    L = ops.lib()
+    d = desc()                       # bf16, 8 KV heads, head dim 128
+
+    def call(pool=d, Hq=40, S=6, groups=2, mg=3, ptok=0, qdt=ops.BF16, ws=None, wsb=0, flags=0, q=16):
+        return L.pa_decode_prefix_shared(ctypes.byref(pool), q, qdt, S, Hq, 16, 8, 16, 16, 16, groups,
+                                         mg, 0.1, 16, ptok, ws, wsb, flags, None)
+
+    assert call(pool=desc(kv_dtype=ops.F32), qdt=ops.F32) == -4   # fp32 pool
+    assert call(qdt=ops.F32) == -2                                  # q must be bf16
+    assert call(Hq=12) == -3                                        # Hq % Hkv != 0
+    assert call(mg=4) == -3                                         # 4 members x 5 heads > 16
+    assert call(mg=0) == -3
+    assert call(groups=0) == -3                                     # sequences but no group
+    assert call(groups=7) == -3                                     # more groups than sequences
+    assert call(ptok=24) == -3 and call(ptok=8192 + 16) == -3
+    assert call(flags=2) == -3
+    assert call(q=None) == -1
+    assert call(q=20) == -6
+    # a split run needs its workspace
+    need = L.pa_decode_prefix_shared_workspace_size(ctypes.byref(d), 6, 40, 8, 2, 3, 64)
+    rows = 6 * 40 * 6            # 3 members x 8 blocks x 16 tokens / 64-token partitions = 6
+    assert need == rows * 128 * 4 + 2 * ((rows * 4 + 255) // 256 * 256) + 256
+    assert call(ptok=64) == -5
+    assert L.pa_decode_prefix_shared_workspace_size(ctypes.byref(d), 6, 40, 8, 2, 3, 0) == 0
+    assert L.pa_decode_prefix_shared_workspace_size(ctypes.byref(d), 6, 40, 8, 2, 4, 0) == 0  # invalid
+    assert L.pa_decode_prefix_shared(ctypes.byref(d), None, ops.BF16, 0, 40, None, 8, None, None, None,
+                                     0, 3, 0.1, None, 0, None, 0, 0, None) == 0   # nothing to do
+
+
+def test_decode_plan():
+    """The launch description agrees with the workspace the same arguments need."""
+    L = ops.lib()
+    d = desc()
+    plan = (ctypes.c_int32 * 4)()
+    assert L.pa_decode_plan(ctypes.byref(d), 4, 64, 256, 512, plan) == 0
+    assert list(plan) == [2, 512, 2, 4]          # matrix-core, partition groups: 8 partitions -> 2 partials
+    assert L.pa_decode_plan(ctypes.byref(d), 4, 8, 256, 512, plan) == 0
+    assert list(plan) == [0, 512, 8, 1]          # one query head per KV head: vector ALU
+    assert L.pa_decode_plan(ctypes.byref(d), 4, 64, 256, 4096, plan) == 0
+    assert list(plan)[0] == 1 and plan[2] == 1   # one partition: no partials
+    assert L.pa_decode_plan(ctypes.byref(d), 4, 12, 256, 0, plan) == -3
+    assert L.pa_decode_plan(ctypes.byref(d), 4, 64, 256, 0, None) == -1
