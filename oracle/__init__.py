@@ -31,19 +31,32 @@ BLOCK = 16
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "pa_oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+_BUILT = os.path.join(_HERE, "liboracle.so")
+# PA_ORACLE_LIB: load another build of the same source (the sanitizer build)
+_LIB = os.environ.get("PA_ORACLE_LIB") or _BUILT
 _lib = None
 
 
 def build(force: bool = True) -> str:
     """Compile the oracle with gcc (no fast-math, no FMA contraction)."""
-    if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp%d" % os.getpid()
+    if force or not os.path.exists(_BUILT):
+        tmp = _BUILT + ".tmp%d" % os.getpid()
         subprocess.check_call(
             ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
              "-fPIC", "-shared", "-std=c11", "-Wall", "-o", tmp, _SRC, "-lm"])
-        os.replace(tmp, _LIB)
-    return _LIB
+        os.replace(tmp, _BUILT)
+    return _BUILT
+
+
+def build_sanitized(out: str) -> str:
+    """The same source built with AddressSanitizer and UndefinedBehaviorSanitizer
+    (gcc; any finding aborts), for host-side checks of the oracle.  Load it by
+    setting PA_ORACLE_LIB, with gcc's libasan and libubsan preloaded."""
+    subprocess.check_call(
+        ["gcc", "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+         "-fno-sanitize-recover=all", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC",
+         "-shared", "-std=c11", "-o", out, _SRC, "-lm"])
+    return out
 
 
 def bind(L: ctypes.CDLL) -> ctypes.CDLL:

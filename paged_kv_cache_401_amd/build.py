@@ -68,5 +68,24 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_host_sanitized(out: str, verbose: bool = False) -> str:
+    """libpa.so with its host code (argument checks, sizing, dispatch: pa_api)
+    built with AddressSanitizer and UndefinedBehaviorSanitizer, linked with the
+    regular objects of the other sources (run build() first).  The sanitizer
+    flags apply to the host pass only (-Xarch_host); device code is unchanged.
+    Load it by setting PA_LIBPA, with clang's ASan runtime preloaded."""
+    objs = [os.path.join(BUILD_DIR, s.replace(".hip", ".o")) for s in SOURCES if s != "pa_api.hip"]
+    missing = [o for o in objs if not os.path.exists(o)]
+    if missing:
+        raise RuntimeError("build() first: missing %s" % missing)
+    san = os.path.join(os.path.dirname(out), "pa_api_san.o")
+    flags = common_flags() + ["-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host",
+                              "-fsanitize=undefined", "-Xarch_host", "-fno-sanitize-recover=all",
+                              "-Xarch_host", "-fno-omit-frame-pointer"]
+    _run([hipcc()] + flags + ["-c", os.path.join(CSRC, "pa_api.hip"), "-o", san], verbose)
+    _run([hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", out, san] + objs, verbose)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

@@ -19,7 +19,8 @@ ELEM_BYTES = {F32: 4, BF16: 2, FP8: 1}
 BLOCK_SIZE = 16
 TORCH_TO_PA = {torch.float32: F32, torch.bfloat16: BF16}
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
+# PA_LIBPA: load another build of the library (the host-sanitizer build)
+LIB_PATH = os.environ.get("PA_LIBPA") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 
 # every symbol include/pa.h declares
 EXPORTS = ("pa_pool_bytes", "pa_decode_partition_tokens", "pa_decode_workspace_size", "pa_decode",
