@@ -144,11 +144,12 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
         }
     }
 
-    float m[kGroups], m_use[kGroups], l[kGroups];
+    float m[kGroups], m_lazy[kGroups], m_use[kGroups], l[kGroups];  // m_lazy = m + kLazyMax
     floatx4 acc[kGroups][NT];
 #pragma unroll
     for (int k = 0; k < kGroups; ++k) {
         m[k] = kNegInfF;
+        m_lazy[k] = kNegInfF;
         m_use[k] = 0.f;
         l[k] = 0.f;
 #pragma unroll
@@ -226,18 +227,26 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
                 w0 &= k01;
                 w1 &= k23;
             }
-            vs[su] = u32x4{w0, w1, w0, w1};
+            // The upper pair as explicit copies: from the duplicated pair
+            // {w0, w1, w0, w1} this compiler (hipcc of ROCm 7.2) has emitted
+            // a 16-byte store whose upper half was the address register.
+            uint32_t c0, c1;
+            asm("v_mov_b32 %0, %2\n\tv_mov_b32 %1, %3" : "=v"(c0), "=v"(c1) : "v"(w0), "v"(w1));
+            vs[su] = u32x4{w0, w1, c0, c1};
         }
     };
 
-    // `skip`: the block's id is out of range, so all of its tokens are masked
-    auto compute_block = [&](int st, int j, bool skip) {
+    // Block j from stage st.  `bias` is -inf when the block id is out of
+    // range (its zero K gives zero scores, and every token is masked) and 0
+    // otherwise, which leaves the product's rounding unchanged; MASK: some
+    // row's position falls inside the block (the causal mask is applied).
+    auto compute_block = [&](auto mask_tag, int st, int j, float bias) {
+        constexpr bool MASK = decltype(mask_tag)::value;
         const u32x4 *ks = stage[st] + c * kBlock + n;  // K run c (+ 4 per step), token n
         const u32x4 *vs = stage[st] + KS_UNITS + c * D + n;  // V cell (token group c, dim n (+ 16 T))
         bf16x8 kop[NQK];
 #pragma unroll
         for (int u = 0; u < NQK; ++u) kop[u] = as_bf16x8(ks[u * 4 * kBlock]);
-        const bool need_mask = skip || j * kBlock + kBlock - 1 > minpos;
 
         // scores of both groups first, so their matrix-core products issue back to back
         floatx4 sacc[kGroups];
@@ -249,22 +258,22 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
                 sacc[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[u], qop[k][u], sacc[k], 0, 0, 0);
         }
         // Scaled scores; tokens 4c + i past a row's position are masked by
-        // selection, on the blocks that cross some row's position only.  The
-        // scaled score itself (not a fused multiply-add) enters the exponent,
-        // so the token holding the max gets probability exactly 1.
+        // selection.  The scaled score itself (not a fused multiply-add with
+        // the max) enters the exponent, so the token holding the max gets
+        // probability exactly 1.
         float sc[kGroups][4], bl[kGroups];
         bool want = false;
 #pragma unroll
         for (int k = 0; k < kGroups; ++k) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sc[k][i] = sacc[k][i] * p.qk_scale_log2;
-            if (need_mask) {
-                const int lim = skip ? -1 : pos_mask[k] - j * kBlock - 4 * c;
+            for (int i = 0; i < 4; ++i) sc[k][i] = __builtin_fmaf(sacc[k][i], p.qk_scale_log2, bias);
+            if constexpr (MASK) {
+                const int lim = pos_mask[k] - j * kBlock - 4 * c;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sc[k][i] = i > lim ? kNegInfF : sc[k][i];
             }
             bl[k] = fmaxf(fmaxf(sc[k][0], sc[k][1]), fmaxf(sc[k][2], sc[k][3]));
-            want = want || bl[k] > m[k] + kLazyMax;
+            want = want || bl[k] > m_lazy[k];
         }
         // the row max is exchanged across lanes, and the running max raised
         // (rescaling the numerators), only when some lane's block max exceeds
@@ -274,11 +283,12 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
 #pragma unroll
             for (int k = 0; k < kGroups; ++k) {
                 const float bm = max_xor32(max_xor16(bl[k]));
-                const bool grow = bm > m[k] + kLazyMax;
+                const bool grow = bm > m_lazy[k];
                 const float m_new = grow ? bm : m[k];
                 const float mu = m_new == kNegInfF ? 0.f : m_new;
                 const float alpha = grow ? __builtin_amdgcn_exp2f(m[k] - mu) : 1.f;
                 m[k] = m_new;
+                m_lazy[k] = m_new + kLazyMax;
                 m_use[k] = mu;
                 l[k] *= alpha;
 #pragma unroll
@@ -322,18 +332,28 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
         swrite(0, kpre, vpre, ctx);
         gload(id_next, kpre, vpre);
         __syncthreads();
-        for (int j = 0; j < nblk_wg; ++j) {
+        // blocks before jm lie at or before every row's position of the
+        // wavefront (no causal mask); the rest are masked
+        const int jm = min((minpos + 1) / kBlock, nblk_wg);
+        auto next = [&](int j) {
             const int32_t id_after = id_at(j + 2);
-            // Every wavefront computes every block of the workgroup: blocks past
-            // its own rows are masked out by the causal test (at most one block
-            // for G = 8), and a straight-line loop body keeps the accumulators
-            // in place.
-            compute_block(j & 1, j, !ok(id_cur));
             if (j + 1 < nblk_wg) swrite((j + 1) & 1, kpre, vpre, ctx - (j + 1) * kBlock);
             gload(id_after, kpre, vpre);
             id_cur = id_next;
             id_next = id_after;
             __syncthreads();
+        };
+        // Every wavefront computes every block of the workgroup: blocks past
+        // its own rows are masked out by the causal test (at most one block
+        // for G = 8), and a straight-line loop body keeps the accumulators
+        // in place.
+        for (int j = 0; j < jm; ++j) {
+            compute_block(std::false_type{}, j & 1, j, ok(id_cur) ? 0.f : kNegInfF);
+            next(j);
+        }
+        for (int j = jm; j < nblk_wg; ++j) {
+            compute_block(std::true_type{}, j & 1, j, ok(id_cur) ? 0.f : kNegInfF);
+            next(j);
         }
     }
 

@@ -202,3 +202,38 @@ def test_prefill_edge_cases():
         a = int(w.query_start[s])
         assert_same_bytes(got[a:a + 17], full[a:a + 17])
         assert (got[a + 17:a + 40] == 7.0).all()
+
+
+def _shape_workload(D, Hq, Hkv, pool_dt, seed):
+    """Chunked prefill over ragged contexts with the given head shape: three
+    sequences whose chunks (40, 77 and 16 tokens) follow cached prefixes of
+    0, 93 and 5 tokens, so the tiles cross block boundaries and the last
+    blocks are partial."""
+    import math
+    rng = np.random.default_rng(seed)
+    n_new = np.array([40, 77, 16])
+    ctx = (np.array([0, 93, 5]) + n_new).astype(np.int32)
+    w = wl._simple("shape", 3, Hq, Hkv, D, ctx, pool_dt, oracle.BF16, oracle.BF16,
+                   float(np.float32(1 / math.sqrt(D))), seed, "cpu", rng,
+                   fp8_scales=pool_dt == oracle.FP8)
+    qs = np.zeros(4, np.int32)
+    qs[1:] = np.cumsum(n_new)
+    w.query_start = qs
+    gen = torch.Generator().manual_seed(seed + 1)
+    w.prefill_q = torch.randn((int(qs[-1]), Hq, D), generator=gen).to(torch.bfloat16)
+    return w
+
+
+@pytest.mark.parametrize("D,Hq,Hkv", [(64, 16, 2), (64, 8, 8), (128, 12, 4), (128, 32, 1)])
+@pytest.mark.parametrize("dt", ["bf16", "fp8"])
+def test_prefill_head_shapes_match_oracle(D, Hq, Hkv, dt):
+    """Head dim 64 and 128 with 8, 1, 3 and 32 query heads per KV head (the
+    tile holds 16, 128, 42 and 4 chunk tokens), over bf16 and fp8 caches."""
+    pool_dt = oracle.BF16 if dt == "bf16" else oracle.FP8
+    w = _shape_workload(D, Hq, Hkv, pool_dt, 300 + D + Hq + pool_dt)
+    kp, vp = oracle_pools(w)
+    ref = oracle_prefill(w, kp, vp)
+    got = gpu_prefill(w, gpu_pool(w, fill=0xFF))
+    assert np.isfinite(got).all()
+    err = float(np.max(np.abs(got - ref)))
+    assert err <= tolerance(w), "max abs error %.3e" % err
