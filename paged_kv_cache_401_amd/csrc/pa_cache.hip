@@ -13,6 +13,8 @@
 #include "pa_internal.h"
 #include "pa_store.h"
 
+#include <type_traits>
+
 namespace pa {
 namespace {
 
@@ -93,19 +95,22 @@ __device__ __forceinline__ uint32_t encode4(const void *base, int64_t idx, float
     return f32x4_to_e4m3(x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv);
 }
 
-// Workgroup (window of 16 input tokens, KV head).  A run is 16 consecutive
-// input tokens whose slots are one whole block in order (16 b .. 16 b + 15:
-// a prompt written block by block).  The workgroup of the window holding a
-// run's first token writes that block's K and V tiles with 16-byte stores:
-// K unit (run r, token t) is the 16-byte run r of token t's input row
-// (converted for an fp8 pool), V cell (token group tg, dims W dw ..) is
-// gathered from four tokens' inputs.  Tokens of the window that no run
-// covers go to their slots one K run per thread (write_run: a decode step's
-// tokens, each in a different sequence, or the partial last block of a
-// prompt).  Runs are
-// found by every wavefront alike: lane l looks at token w0 - 16 + l, and
-// ballots mark the tokens whose slot follows the previous one's.
-template <int POOL, int IN, int D>
+// Workgroup (window of 16 input tokens, up to HPW KV heads).  A run is 16
+// consecutive input tokens whose slots are one whole block in order
+// (16 b .. 16 b + 15: a prompt written block by block).  The workgroup of the
+// window holding a run's first token writes that block's K and V tiles of
+// its heads with 16-byte stores: K unit (run r, token t) is the 16-byte run r
+// of token t's input row (converted for an fp8 pool), V cell (token group tg,
+// dims W dw ..) is gathered from four tokens' inputs -- for a bf16 pool two
+// neighbouring cells at once, from 8-byte loads of four dims.  Each thread
+// issues all its loads before its first store.  (The loads are ordinary
+// ones: several work items read parts of one input line.)  Tokens of the window that no
+// run covers go to their slots one K run per thread (write_run: a decode
+// step's tokens, each in a different sequence, or the partial last block of
+// a prompt).  Runs are found by every wavefront alike: lane l looks at token
+// w0 - 16 + l, and ballots mark the tokens whose slot follows the previous
+// one's.
+template <int POOL, int IN, int D, int HPW>
 __global__ __launch_bounds__(kThreads) void reshape_and_cache_kernel(CacheParams p) {
     constexpr int EB = POOL == kF32 ? 4 : (POOL == kBF16 ? 2 : 1);
     constexpr int IB = IN == kF32 ? 4 : 2;          // input bytes per element
@@ -113,7 +118,8 @@ __global__ __launch_bounds__(kThreads) void reshape_and_cache_kernel(CacheParams
     constexpr int W = 4 / EB;                       // V: dims per 16-byte cell
     constexpr int K_UNITS = kBlock * D * EB / 16;   // 16-byte units of one tile
     const int64_t w0 = (int64_t)blockIdx.x * kBlock;
-    const int g = blockIdx.y;
+    const int g0 = blockIdx.y * HPW;
+    const int nh = p.num_kv_heads - g0 < HPW ? p.num_kv_heads - g0 : HPW;  // heads of this workgroup
     const int lane = threadIdx.x & 63;
 
     const int64_t tok = w0 - kBlock + lane;
@@ -130,65 +136,153 @@ __global__ __launch_bounds__(kThreads) void reshape_and_cache_kernel(CacheParams
     const uint32_t mine = (uint32_t)(starts >> 16) & 0xffffu;
 
     const int64_t nt = p.num_tokens - w0 < kBlock ? p.num_tokens - w0 : kBlock;
-    constexpr int NR = D / X;                        // K runs per token
-    for (int e = threadIdx.x; e < nt * NR; e += kThreads) {
-        const int t = e / NR, r = e % NR;
-        if (!((cov >> t) & 1u)) write_run<POOL, IN, D>(p, w0 + t, g, r, p.slot_mapping[w0 + t]);
+    constexpr int NR = D / X;                        // K runs per token and head
+    for (int e = threadIdx.x; e < nt * NR * nh; e += kThreads) {
+        const int t = e / (NR * nh), hh = (e / NR) % nh, r = e % NR;
+        if (!((cov >> t) & 1u)) write_run<POOL, IN, D>(p, w0 + t, g0 + hh, r, p.slot_mapping[w0 + t]);
     }
     if (!mine) return;
     const int64_t i0 = w0 + __builtin_ctz(mine);    // the run's first token
     const int32_t s0 = p.slot_mapping[i0];
-    const int64_t tile = ((int64_t)(s0 >> 4) * p.num_kv_heads + g) * K_UNITS;
-    uint4 *kt = reinterpret_cast<uint4 *>(p.k_pool) + tile;
-    uint4 *vt = reinterpret_cast<uint4 *>(p.v_pool) + tile;
-    auto row = [&](int t) { return ((i0 + t) * p.num_kv_heads + g) * D; };  // first input element
-    for (int u = threadIdx.x; u < K_UNITS; u += kThreads) {
-        const int r = u / kBlock, t = u % kBlock;
-        const int64_t e = row(t) + r * X;
-        uint4 w;
-        if constexpr (POOL == kFP8) {
-            w.x = encode4<IN>(p.k, e, p.inv_k_scale);
-            w.y = encode4<IN>(p.k, e + 4, p.inv_k_scale);
-            w.z = encode4<IN>(p.k, e + 8, p.inv_k_scale);
-            w.w = encode4<IN>(p.k, e + 12, p.inv_k_scale);
-        } else {
-            w = *reinterpret_cast<const uint4 *>(static_cast<const char *>(p.k) + e * IB);
-        }
-        store16_nt(kt + u, w);
-    }
-    for (int u = threadIdx.x; u < K_UNITS; u += kThreads) {
-        const int tg = u / (D / W), dw = u % (D / W);
-        const int64_t e = row(4 * tg) + W * dw;      // token 4 tg, first dim of the cell
-        const int64_t step = (int64_t)p.num_kv_heads * D;  // next token, same dim
-        uint4 w;
-        if constexpr (POOL == kFP8) {  // word j: tokens 0..3 of dim 4 dw + j
-            uint32_t c[4];
+    const int64_t step = (int64_t)p.num_kv_heads * D;  // next token, same head and dim
+    // first input element of token t, head hh
+    auto row = [&](int t, int hh) { return (i0 + t) * step + (int64_t)(g0 + hh) * D; };
+    // pool unit u of head hh's tile
+    auto unit = [&](void *pool, int hh, int u) {
+        return reinterpret_cast<uint4 *>(pool) + ((int64_t)(s0 >> 4) * p.num_kv_heads + g0 + hh) * K_UNITS + u;
+    };
+
+    // The tiles in three phases -- every thread's input loads, then the
+    // conversions (whose fp8 NaN test may branch), then the 16-byte stores --
+    // so all loads are in flight before the first one is waited for.  FULL:
+    // all HPW heads present (the usual case), no per-item bounds.
+    constexpr int CPI = POOL == kBF16 ? 2 : 1;       // V cells per work item
+    constexpr int VU = K_UNITS / CPI;                // V work items per tile
+    constexpr int KI = (HPW * K_UNITS + kThreads - 1) / kThreads;
+    constexpr int VI = (HPW * VU + kThreads - 1) / kThreads;
+    constexpr int NKU = X * IB / 16;                 // 16-byte input units per K unit
+    constexpr int VB = W * CPI * IB;                 // input bytes per token of a V item
+    using VWord = typename std::conditional<VB == 4, uint32_t,
+                  typename std::conditional<VB == 8, uint2, uint4>::type>::type;
+    auto tiles = [&](auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
+        // K item i = hh * K_UNITS + (r * 16 + t); V item i = hh * VU +
+        // (tg * (D / W / CPI) + q), cells CPI q .. CPI q + CPI - 1 of token group tg
+        auto k_in = [&](int i) {
+            const int hh = i / K_UNITS, u = i % K_UNITS;
+            return row(u % kBlock, hh) + (u / kBlock) * X;
+        };
+        auto v_in = [&](int i) {
+            const int hh = i / VU, u = i % VU;
+            return row(4 * (u / (D / W / CPI)), hh) + W * CPI * (u % (D / W / CPI));
+        };
+        uint4 kr[KI][NKU];
+        VWord vr[VI][4];
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) c[tt] = encode4<IN>(p.v, e + tt * step, p.inv_v_scale);
-            // c[tt] byte j = (token tt, dim j): transpose the 4 x 4 bytes
-            const uint32_t a0 = __builtin_amdgcn_perm(c[1], c[0], 0x05010400u);  // t0d0 t1d0 t0d1 t1d1
-            const uint32_t a1 = __builtin_amdgcn_perm(c[3], c[2], 0x05010400u);  // t2d0 t3d0 t2d1 t3d1
-            const uint32_t b0 = __builtin_amdgcn_perm(c[1], c[0], 0x07030602u);  // t0d2 t1d2 t0d3 t1d3
-            const uint32_t b1 = __builtin_amdgcn_perm(c[3], c[2], 0x07030602u);  // t2d2 t3d2 t2d3 t3d3
-            w.x = __builtin_amdgcn_perm(a1, a0, 0x05040100u);  // d0: t0 t1 t2 t3
-            w.y = __builtin_amdgcn_perm(a1, a0, 0x07060302u);  // d1
-            w.z = __builtin_amdgcn_perm(b1, b0, 0x05040100u);  // d2
-            w.w = __builtin_amdgcn_perm(b1, b0, 0x07060302u);  // d3
-        } else if constexpr (POOL == kBF16) {  // words: (t0 t1)(t2 t3) of dim 2 dw, then of 2 dw + 1
-            const char *src = static_cast<const char *>(p.v);
-            uint32_t x[4];
+        for (int j = 0; j < KI; ++j) {
+            const int i = threadIdx.x + j * kThreads;
+            if (!FULL && i >= nh * K_UNITS) break;
+            const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const char *>(p.k) + k_in(i) * IB);
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) x[tt] = *reinterpret_cast<const uint32_t *>(src + (e + tt * step) * 2);
-            w.x = __builtin_amdgcn_perm(x[1], x[0], 0x05040100u);
-            w.y = __builtin_amdgcn_perm(x[3], x[2], 0x05040100u);
-            w.z = __builtin_amdgcn_perm(x[1], x[0], 0x07060302u);
-            w.w = __builtin_amdgcn_perm(x[3], x[2], 0x07060302u);
-        } else {  // fp32: tokens 0..3 of dim dw
-            const uint32_t *src = static_cast<const uint32_t *>(p.v);
-            w.x = src[e], w.y = src[e + step], w.z = src[e + 2 * step], w.w = src[e + 3 * step];
+            for (int c = 0; c < NKU; ++c) kr[j][c] = src[c];
         }
-        store16_nt(vt + u, w);
-    }
+#pragma unroll
+        for (int j = 0; j < VI; ++j) {
+            const int i = threadIdx.x + j * kThreads;
+            if (!FULL && i >= nh * VU) break;
+            const int64_t e = v_in(i);
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt)
+                vr[j][tt] = *reinterpret_cast<const VWord *>(static_cast<const char *>(p.v) + (e + tt * step) * IB);
+        }
+        uint4 kw[KI], vw[VI][CPI];
+#pragma unroll
+        for (int j = 0; j < KI; ++j) {
+            if constexpr (POOL == kFP8) {
+                uint32_t c4[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {  // input elements 4 q .. 4 q + 3
+                    float x[4];
+#pragma unroll
+                    for (int z = 0; z < 4; ++z) {
+                        const int el = 4 * q + z;
+                        if constexpr (IN == kF32) {
+                            x[z] = __uint_as_float(kr[j][el / 4][el % 4]);
+                        } else {
+                            const uint32_t wd = kr[j][el / 8][(el % 8) / 2];
+                            x[z] = __uint_as_float(el % 2 ? wd & 0xffff0000u : wd << 16);
+                        }
+                        x[z] *= p.inv_k_scale;
+                    }
+                    c4[q] = f32x4_to_e4m3(x[0], x[1], x[2], x[3]);
+                }
+                kw[j] = uint4{c4[0], c4[1], c4[2], c4[3]};
+            } else {
+                kw[j] = kr[j][0];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < VI; ++j) {
+            if constexpr (POOL == kFP8) {  // word j: tokens 0..3 of dim 4 q + j
+                uint32_t c[4];
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) {
+                    float x[4];
+#pragma unroll
+                    for (int z = 0; z < 4; ++z) {
+                        if constexpr (IN == kF32) {
+                            x[z] = __uint_as_float(vr[j][tt][z]);
+                        } else {
+                            const uint32_t wd = z < 2 ? vr[j][tt].x : vr[j][tt].y;
+                            x[z] = __uint_as_float(z % 2 ? wd & 0xffff0000u : wd << 16);
+                        }
+                        x[z] *= p.inv_v_scale;
+                    }
+                    c[tt] = f32x4_to_e4m3(x[0], x[1], x[2], x[3]);
+                }
+                // c[tt] byte j = (token tt, dim j): transpose the 4 x 4 bytes
+                const uint32_t a0 = __builtin_amdgcn_perm(c[1], c[0], 0x05010400u);  // t0d0 t1d0 t0d1 t1d1
+                const uint32_t a1 = __builtin_amdgcn_perm(c[3], c[2], 0x05010400u);  // t2d0 t3d0 t2d1 t3d1
+                const uint32_t b0 = __builtin_amdgcn_perm(c[1], c[0], 0x07030602u);  // t0d2 t1d2 t0d3 t1d3
+                const uint32_t b1 = __builtin_amdgcn_perm(c[3], c[2], 0x07030602u);  // t2d2 t3d2 t2d3 t3d3
+                vw[j][0].x = __builtin_amdgcn_perm(a1, a0, 0x05040100u);  // d0: t0 t1 t2 t3
+                vw[j][0].y = __builtin_amdgcn_perm(a1, a0, 0x07060302u);  // d1
+                vw[j][0].z = __builtin_amdgcn_perm(b1, b0, 0x05040100u);  // d2
+                vw[j][0].w = __builtin_amdgcn_perm(b1, b0, 0x07060302u);  // d3
+            } else if constexpr (POOL == kBF16) {
+                // dims 4 q .. 4 q + 3 of tokens 0..3; cell 0 holds dims 4 q, 4 q + 1
+                // as words (t0 t1)(t2 t3) of each dim, cell 1 dims 4 q + 2, 4 q + 3
+                const uint2 *x = vr[j];
+                vw[j][0].x = __builtin_amdgcn_perm(x[1].x, x[0].x, 0x05040100u);
+                vw[j][0].y = __builtin_amdgcn_perm(x[3].x, x[2].x, 0x05040100u);
+                vw[j][0].z = __builtin_amdgcn_perm(x[1].x, x[0].x, 0x07060302u);
+                vw[j][0].w = __builtin_amdgcn_perm(x[3].x, x[2].x, 0x07060302u);
+                vw[j][1].x = __builtin_amdgcn_perm(x[1].y, x[0].y, 0x05040100u);
+                vw[j][1].y = __builtin_amdgcn_perm(x[3].y, x[2].y, 0x05040100u);
+                vw[j][1].z = __builtin_amdgcn_perm(x[1].y, x[0].y, 0x07060302u);
+                vw[j][1].w = __builtin_amdgcn_perm(x[3].y, x[2].y, 0x07060302u);
+            } else {  // fp32: tokens 0..3 of dim q
+                vw[j][0] = uint4{vr[j][0], vr[j][1], vr[j][2], vr[j][3]};
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < KI; ++j) {
+            const int i = threadIdx.x + j * kThreads;
+            if (!FULL && i >= nh * K_UNITS) break;
+            store16_nt(unit(p.k_pool, i / K_UNITS, i % K_UNITS), kw[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < VI; ++j) {
+            const int i = threadIdx.x + j * kThreads;
+            if (!FULL && i >= nh * VU) break;
+#pragma unroll
+            for (int cc = 0; cc < CPI; ++cc) store16_nt(unit(p.v_pool, i / VU, (i % VU) * CPI + cc), vw[j][cc]);
+        }
+    };
+    if (nh == HPW)
+        tiles(std::true_type{});
+    else
+        tiles(std::false_type{});
 }
 
 // Workgroup (pair, pool, part): 16-byte copies of one part of the whole block
@@ -284,12 +378,16 @@ __global__ __launch_bounds__(kThreads) void append_tokens_kernel(DecodeParams p)
     for (int d = threadIdx.x; d < D; d += kThreads) append_element<POOL, D>(p, table, s, g, ctx - 1, d);
 }
 
+// heads per cache-write workgroup
+constexpr int kCacheHeads = 8;
+
 template <int POOL, int IN, int D>
 hipError_t launch_rc(const CacheParams &p, hipStream_t stream) {
     const int64_t groups = (p.num_tokens + kBlock - 1) / kBlock;
     if (groups > 0x7fffffffLL || p.num_kv_heads > 65535) return hipErrorInvalidValue;
-    reshape_and_cache_kernel<POOL, IN, D>
-        <<<dim3((unsigned)groups, (unsigned)p.num_kv_heads), dim3(kThreads), 0, stream>>>(p);
+    const unsigned hgroups = (unsigned)((p.num_kv_heads + kCacheHeads - 1) / kCacheHeads);
+    reshape_and_cache_kernel<POOL, IN, D, kCacheHeads>
+        <<<dim3((unsigned)groups, hgroups), dim3(kThreads), 0, stream>>>(p);
     return hipGetLastError();
 }
 
