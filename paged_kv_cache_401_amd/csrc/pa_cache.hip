@@ -155,7 +155,7 @@ __global__ __launch_bounds__(kThreads) void reshape_and_cache_kernel(CacheParams
     // The tiles in three phases -- every thread's input loads, then the
     // conversions (whose fp8 NaN test may branch), then the 16-byte stores --
     // so all loads are in flight before the first one is waited for.  FULL:
-    // all HPW heads present (the usual case), no per-item bounds.
+    // all HPW heads present (the usual case).
     constexpr int CPI = POOL == kBF16 ? 2 : 1;       // V cells per work item
     constexpr int VU = K_UNITS / CPI;                // V work items per tile
     constexpr int KI = (HPW * K_UNITS + kThreads - 1) / kThreads;
@@ -166,6 +166,10 @@ __global__ __launch_bounds__(kThreads) void reshape_and_cache_kernel(CacheParams
                   typename std::conditional<VB == 8, uint2, uint4>::type>::type;
     auto tiles = [&](auto full_tag) {
         constexpr bool FULL = decltype(full_tag)::value;
+        // every item of the K (V) loops exists: all heads present, and the
+        // items a multiple of the workgroup's threads
+        constexpr bool KFULL = FULL && (HPW * K_UNITS) % kThreads == 0;
+        constexpr bool VFULL = FULL && (HPW * VU) % kThreads == 0;
         // K item i = hh * K_UNITS + (r * 16 + t); V item i = hh * VU +
         // (tg * (D / W / CPI) + q), cells CPI q .. CPI q + CPI - 1 of token group tg
         auto k_in = [&](int i) {
@@ -181,7 +185,7 @@ __global__ __launch_bounds__(kThreads) void reshape_and_cache_kernel(CacheParams
 #pragma unroll
         for (int j = 0; j < KI; ++j) {
             const int i = threadIdx.x + j * kThreads;
-            if (!FULL && i >= nh * K_UNITS) break;
+            if (!KFULL && i >= nh * K_UNITS) break;
             const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const char *>(p.k) + k_in(i) * IB);
 #pragma unroll
             for (int c = 0; c < NKU; ++c) kr[j][c] = src[c];
@@ -189,7 +193,7 @@ __global__ __launch_bounds__(kThreads) void reshape_and_cache_kernel(CacheParams
 #pragma unroll
         for (int j = 0; j < VI; ++j) {
             const int i = threadIdx.x + j * kThreads;
-            if (!FULL && i >= nh * VU) break;
+            if (!VFULL && i >= nh * VU) break;
             const int64_t e = v_in(i);
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt)
@@ -268,13 +272,13 @@ __global__ __launch_bounds__(kThreads) void reshape_and_cache_kernel(CacheParams
 #pragma unroll
         for (int j = 0; j < KI; ++j) {
             const int i = threadIdx.x + j * kThreads;
-            if (!FULL && i >= nh * K_UNITS) break;
+            if (!KFULL && i >= nh * K_UNITS) break;
             store16_nt(unit(p.k_pool, i / K_UNITS, i % K_UNITS), kw[j]);
         }
 #pragma unroll
         for (int j = 0; j < VI; ++j) {
             const int i = threadIdx.x + j * kThreads;
-            if (!FULL && i >= nh * VU) break;
+            if (!VFULL && i >= nh * VU) break;
 #pragma unroll
             for (int cc = 0; cc < CPI; ++cc) store16_nt(unit(p.v_pool, i / VU, (i % VU) * CPI + cc), vw[j][cc]);
         }
@@ -378,16 +382,24 @@ __global__ __launch_bounds__(kThreads) void append_tokens_kernel(DecodeParams p)
     for (int d = threadIdx.x; d < D; d += kThreads) append_element<POOL, D>(p, table, s, g, ctx - 1, d);
 }
 
-// heads per cache-write workgroup
+// Heads per cache-write workgroup: 8 for bulk writes (prompts: thousands of
+// windows), 1 for small ones (a decode step's lone tokens, whose writes are
+// latency-bound round trips and need the workgroups: 256 tokens x 8 heads
+// took 17.8 us from 16 eight-head workgroups against ~4 us from 128).
 constexpr int kCacheHeads = 8;
+constexpr int64_t kCacheBulkGroups = 2048;  // workgroups of the 8-head grid from which it is used
 
 template <int POOL, int IN, int D>
 hipError_t launch_rc(const CacheParams &p, hipStream_t stream) {
     const int64_t groups = (p.num_tokens + kBlock - 1) / kBlock;
     if (groups > 0x7fffffffLL || p.num_kv_heads > 65535) return hipErrorInvalidValue;
-    const unsigned hgroups = (unsigned)((p.num_kv_heads + kCacheHeads - 1) / kCacheHeads);
-    reshape_and_cache_kernel<POOL, IN, D, kCacheHeads>
-        <<<dim3((unsigned)groups, hgroups), dim3(kThreads), 0, stream>>>(p);
+    const int64_t hgroups = (p.num_kv_heads + kCacheHeads - 1) / kCacheHeads;
+    if (groups * hgroups >= kCacheBulkGroups)
+        reshape_and_cache_kernel<POOL, IN, D, kCacheHeads>
+            <<<dim3((unsigned)groups, (unsigned)hgroups), dim3(kThreads), 0, stream>>>(p);
+    else
+        reshape_and_cache_kernel<POOL, IN, D, 1>
+            <<<dim3((unsigned)groups, (unsigned)p.num_kv_heads), dim3(kThreads), 0, stream>>>(p);
     return hipGetLastError();
 }
 

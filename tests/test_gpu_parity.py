@@ -41,13 +41,14 @@ def test_cache_write_and_copy_bit_exact(name):
     assert np.array_equal(gv, vp), "V pool bytes differ"
 
 
-def _mixed_slots(rng, nb):
+def _mixed_slots(rng, nb, reps=6):
     """A slot mapping mixing what a cache write meets: whole blocks in order
     at arbitrary input offsets, a block written out of order, partial blocks,
-    runs that straddle two blocks, skipped tokens and an out-of-range slot."""
+    runs that straddle two blocks, skipped tokens and an out-of-range slot
+    (`reps` of each kind)."""
     blocks = rng.permutation(nb)
     parts, k = [], 0
-    for kind in rng.permutation(np.repeat(np.arange(6), 6)):
+    for kind in rng.permutation(np.repeat(np.arange(6), reps)):
         b = int(blocks[k]); k += 1
         base = np.arange(16 * b, 16 * b + 16)
         if kind == 0:                      # whole block in order (a run)
@@ -78,6 +79,34 @@ def test_cache_write_mixed_slot_runs_bit_exact(pool_dt, in_dt, D):
     nb, Hkv = 64, 3
     slots = _mixed_slots(rng, nb)
     n = slots.size
+    tdt = torch.float32 if in_dt == ops.F32 else torch.bfloat16
+    gen = torch.Generator().manual_seed(int(rng.integers(1 << 30)))
+    k = (torch.randn((n, Hkv, D), generator=gen) * 3).to(tdt)
+    v = (torch.randn((n, Hkv, D), generator=gen) * 3).to(tdt)
+    scale = 0.05 if pool_dt == ops.FP8 else 1.0
+    kp = oracle.new_pool(nb, Hkv, D, pool_dt, fill=0xFF)
+    vp = oracle.new_pool(nb, Hkv, D, pool_dt, fill=0xFF)
+    oracle.reshape_and_cache(kp, vp, pool_dt, nb, Hkv, D, raw_numpy(k), raw_numpy(v), in_dt, slots,
+                             scale, scale)
+    pool = ops.KVPool(nb, Hkv, D, pool_dt, k_scale=scale, v_scale=scale, fill=0xFF)
+    ops.reshape_and_cache(pool, k.cuda(), v.cuda(), torch.from_numpy(slots).cuda())
+    gk, gv = _pool_bytes(pool)
+    assert np.array_equal(gk, kp), "K pool bytes differ"
+    assert np.array_equal(gv, vp), "V pool bytes differ"
+
+
+@pytest.mark.parametrize("pool_dt,in_dt", [(ops.F32, ops.F32), (ops.BF16, ops.BF16),
+                                           (ops.FP8, ops.BF16), (ops.FP8, ops.F32)])
+@pytest.mark.parametrize("D", [64, 128])
+def test_cache_write_bulk_grid_mixed_slot_runs_bit_exact(pool_dt, in_dt, D):
+    """The same mix at bulk size (about 25,000 tokens), which the library
+    writes with workgroups of up to 8 KV heads: 12 heads make one full group
+    of 8 and one of 4.  Pool bytes equal the oracle's."""
+    rng = np.random.default_rng(23 + D + 3 * pool_dt + in_dt)
+    nb, Hkv = 4096, 12
+    slots = _mixed_slots(rng, nb, reps=300)
+    n = slots.size
+    assert (n + 15) // 16 * 2 >= 2048       # the 8-head grid's size
     tdt = torch.float32 if in_dt == ops.F32 else torch.bfloat16
     gen = torch.Generator().manual_seed(int(rng.integers(1 << 30)))
     k = (torch.randn((n, Hkv, D), generator=gen) * 3).to(tdt)
