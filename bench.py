@@ -367,6 +367,8 @@ def decode_run(w, steps, warmup, ptok, append="separate", graph=False, flush_and
                   torch.as_tensor(np.asarray(pb, np.int32), device=dev), mg)
         sws = ops.decode_prefix_shared_workspace_size(pool, w.S, w.Hq, w.max_blocks_per_seq,
                                                       len(pb), mg, ptok)
+        ptok_used = ops.decode_prefix_shared_plan(pool, w.S, w.Hq, w.max_blocks_per_seq, len(pb), mg,
+                                                  ptok)["partition_tokens"]
         sws_t = torch.empty(max(sws, 16), dtype=torch.uint8, device=dev)
 
     def decode_call():

@@ -236,6 +236,14 @@ size_t pa_decode_prefix_shared_workspace_size(const pa_pool_t *pool, int32_t num
                                               int32_t num_groups, int32_t max_group_size,
                                               int32_t partition_tokens);
 
+/* The launch pa_decode_prefix_shared makes for these arguments (for tooling
+ * and profiles): plan[0] = partition tokens (the library's choice when
+ * partition_tokens is 0), plan[1] = partitions at most per group and KV head
+ * (1: outputs written at once, no merge kernel).  Returns a pa_status. */
+int pa_decode_prefix_shared_plan(const pa_pool_t *pool, int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t max_blocks_per_seq, int32_t num_groups, int32_t max_group_size,
+                                 int32_t partition_tokens, int32_t plan[2]);
+
 /*
  * pa_decode_append -- one decode step: write every sequence's newest token,
  * then attend as pa_decode_ex.  The newest token of sequence s sits at

@@ -564,6 +564,21 @@ size_t pa_decode_prefix_shared_workspace_size(const pa_pool_t *pool, int32_t num
                                 ptok, nullptr);
 }
 
+int pa_decode_prefix_shared_plan(const pa_pool_t *pool, int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t max_blocks_per_seq, int32_t num_groups, int32_t max_group_size,
+                                 int32_t partition_tokens, int32_t plan[2]) {
+    if (!plan) return fail(PA_ERR_NULL, "plan must be non-NULL");
+    int32_t ptok = 0, np = 0;
+    const int rc = check_shared_args(pool, num_seqs, num_q_heads, max_blocks_per_seq, num_groups,
+                                     max_group_size, partition_tokens, &ptok);
+    if (rc != PA_OK) return rc;
+    shared_workspace_for(pool, num_seqs, num_q_heads, max_blocks_per_seq, num_groups, max_group_size, ptok,
+                         &np);
+    plan[0] = ptok;
+    plan[1] = np;
+    return ok();
+}
+
 int pa_decode_prefix_shared(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t num_seqs,
                             int32_t num_q_heads, const int32_t *block_tables, int32_t max_blocks_per_seq,
                             const int32_t *context_lens, const int32_t *group_start,

@@ -25,7 +25,7 @@ LIB_PATH = os.environ.get("PA_LIBPA") or os.path.join(os.path.dirname(os.path.ab
 # every symbol include/pa.h declares
 EXPORTS = ("pa_pool_bytes", "pa_decode_partition_tokens", "pa_decode_workspace_size", "pa_decode",
            "pa_decode_ex", "pa_decode_noalloc", "pa_decode_append", "pa_decode_prefix_shared",
-           "pa_decode_prefix_shared_workspace_size",
+           "pa_decode_prefix_shared_workspace_size", "pa_decode_prefix_shared_plan",
            "pa_prefill", "pa_reshape_and_cache", "pa_swap_blocks", "pa_copy_blocks",
            "pa_check_workspace_size", "pa_check_tables", "pa_check_query_start", "pa_check_slots",
            "pa_check_copy_pairs", "pa_check_swap_pairs", "pa_set_debug",
@@ -83,6 +83,8 @@ def lib() -> ctypes.CDLL:
     L.pa_decode_prefix_shared.restype = ctypes.c_int
     L.pa_decode_prefix_shared_workspace_size.argtypes = [PD, I32, I32, I32, I32, I32, I32]
     L.pa_decode_prefix_shared_workspace_size.restype = SZ
+    L.pa_decode_prefix_shared_plan.argtypes = [PD, I32, I32, I32, I32, I32, I32, P]
+    L.pa_decode_prefix_shared_plan.restype = ctypes.c_int
     L.pa_decode_append.argtypes = [PD, P, I32, I32, I32, P, I32, P, F, P, I32, P, SZ, ctypes.c_uint32,
                                    P, P, I32, P]
     L.pa_decode_append.restype = ctypes.c_int
@@ -484,6 +486,18 @@ def decode_plan(pool: KVPool, num_seqs, num_q_heads, max_blocks_per_seq, partiti
                                 int(max_blocks_per_seq), int(partition_tokens), plan))
     return {"kernel": DECODE_KERNELS[plan[0]], "partition_tokens": plan[1],
             "partials_per_row": plan[2], "partitions_per_partial": plan[3]}
+
+
+def decode_prefix_shared_plan(pool: KVPool, num_seqs, num_q_heads, max_blocks_per_seq, num_groups,
+                              max_group_size, partition_tokens=0) -> dict:
+    """The launch pa_decode_prefix_shared makes: its partition tokens and the
+    partitions at most per group and KV head."""
+    plan = (ctypes.c_int32 * 2)()
+    d = pool.desc()
+    _check(lib().pa_decode_prefix_shared_plan(ctypes.byref(d), int(num_seqs), int(num_q_heads),
+                                              int(max_blocks_per_seq), int(num_groups),
+                                              int(max_group_size), int(partition_tokens), plan))
+    return {"partition_tokens": plan[0], "max_partitions": plan[1]}
 
 
 def set_profile_events(before, after) -> None:

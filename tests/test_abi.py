@@ -302,6 +302,29 @@ def test_decode_prefix_shared_argument_rules():
                                      0, 3, 0.1, None, 0, None, 0, 0, None) == 0   # nothing to do
 
 
+def test_decode_prefix_shared_plan():
+    """The shared-prefix launch description agrees with the workspace the same
+    arguments need, and follows the same argument rules."""
+    L = ops.lib()
+    d = desc()
+    plan = (ctypes.c_int32 * 2)()
+    assert L.pa_decode_prefix_shared_plan(ctypes.byref(d), 6, 40, 8, 2, 3, 64, plan) == 0
+    assert list(plan) == [64, 6]                  # 3 members x 8 blocks x 16 tokens / 64
+    assert L.pa_decode_prefix_shared_workspace_size(ctypes.byref(d), 6, 40, 8, 2, 3, 64) > 0
+    assert L.pa_decode_prefix_shared_plan(ctypes.byref(d), 6, 40, 8, 2, 3, 0, plan) == 0
+    assert plan[1] == 1                           # the library's choice: one partition, so
+    assert L.pa_decode_prefix_shared_workspace_size(ctypes.byref(d), 6, 40, 8, 2, 3, 0) == 0  # no workspace
+    assert plan[0] >= 3 * 8 * 16 and plan[0] % 16 == 0
+    assert L.pa_decode_prefix_shared_plan(ctypes.byref(d), 6, 40, 8, 2, 4, 0, plan) == -3   # 4 x 5 > 16
+    assert L.pa_decode_prefix_shared_plan(ctypes.byref(d), 6, 40, 8, 2, 3, 0, None) == -1
+
+    class Pool:  # the binding reads only the descriptor
+        def desc(self):
+            return d
+    assert ops.decode_prefix_shared_plan(Pool(), 6, 40, 8, 2, 3, 64) == {"partition_tokens": 64,
+                                                                        "max_partitions": 6}
+
+
 def test_decode_plan():
     """The launch description agrees with the workspace the same arguments need."""
     L = ops.lib()
