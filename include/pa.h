@@ -298,6 +298,12 @@ int pa_decode_append(const pa_pool_t *pool, const void *q, int32_t q_dtype, int3
  *                  chunk longer than its context) is written as zeros.
  * Pools: PA_BF16 or PA_FP8_E4M3 (PA_ERR_UNSUPPORTED for fp32); q_dtype must
  * be PA_BF16.  Cache entries inside each context must be finite.
+ * Precision: scores and the softmax in fp32; the probabilities enter the P.V
+ * product rounded to fp16 (relative error <= 2^-11; the row sum adds the
+ * same rounded values), against V widened to fp16 -- exact for E4M3 codes and
+ * for bf16 magnitudes in [2^-14, 2^16) (within 2^-25 below), so a bf16 pool's
+ * V entries inside each context must also be below 2^16 in magnitude (larger
+ * ones become infinite); accumulation in fp32.
  */
 int pa_prefill(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t num_seqs,
                int32_t num_q_heads, const int32_t *query_start, int32_t max_query_len,

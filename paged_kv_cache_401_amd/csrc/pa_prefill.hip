@@ -18,24 +18,29 @@
 // two 16-column matrix-core groups.  Workgroups are issued latest tile
 // first, so the longest causal ranges start first.
 //
-// Staging.  The workgroup walks blocks 0 .. (its last row's position) / 16.
-// Every block's K and V tiles are loaded once per workgroup and written to
-// one of two LDS stages (the next block is already in flight in registers
-// while the current one is computed, and is written to the other stage
-// afterwards; one barrier per block).  The stage holds K as bf16 runs and V as
-// duplicated bf16 cells that are directly the A operands of both products
-// (fp8 widened and tokens past the context zeroed once, at staging).
+// Staging.  The workgroup walks its blocks 0 .. (its last row's position) / 16
+// two at a time: a step covers blocks 2 i and 2 i + 1.  Every step's K and V
+// tiles are loaded once per workgroup and written to one of two LDS stages (the
+// next step is already in flight in registers while the current one is
+// computed, and is written to the other stage afterwards; one barrier per
+// step).  The stage holds K as bf16 runs and V as fp16 cells that are directly
+// the A operands of both products (fp8 widened, bf16 V narrowed to fp16, and
+// tokens past the context zeroed once, at staging).
 //
-// Per block, for each 16-row group (operand layouts as in the grouped decode
+// Per step, for each 16-row group (operand layouts as in the grouped decode
 // kernel):
-//     S^T[16 tokens][16 rows]  = K[16][D] . Q^T[D][16]
-//     O^T[D][16 rows]         += V^T[D][16 tokens] . P^T[16][16]
-// with P carried as bf16 hi + lo (16 significant bits).  Causal masking sets
-// the score of every token past a row's position to -inf (selection).  The
-// running maximum is raised lazily: only when some lane's block maximum
-// exceeds it by more than 8 (in log2 units) is the row maximum exchanged
-// across lanes and are the numerators rescaled, so probabilities stay below
-// 2^8 and most blocks skip both.
+//     S^T[16 tokens][16 rows]  = K[16][D] . Q^T[D][16]           (each block)
+//     O^T[D][16 rows]         += V^T[D][32 tokens] . P^T[32][16]  (both blocks)
+// with P rounded to fp16 for the second product (relative error <= 2^-11;
+// the row sum adds the same rounded values).  fp16 holds every E4M3 value
+// exactly, and a bf16 value exactly when its magnitude lies in [2^-14, 2^16)
+// and within 2^-25 below it; bf16 V of magnitude 2^16 or more is outside the
+// kernel's domain (it becomes infinite).  Causal masking sets the score
+// of every token past a row's position to -inf (selection).  The running
+// maximum is raised lazily: only when some lane's exponent exceeds it by
+// more than 8 (in log2 units) is the row maximum exchanged across lanes and
+// are the numerators rescaled, so probabilities stay below 2^8 and most steps
+// skip both.
 #include "pa_internal.h"
 #include "pa_mfma_util.h"
 
@@ -47,36 +52,41 @@ namespace {
 constexpr int kGroups = 2;                                    // 16-row groups per wavefront
 constexpr int kRowsPerWave = 16 * kGroups;                    // 32
 constexpr int kRowsPerTile = kRowsPerWave * (kThreads / 64);  // 128
-constexpr float kLazyMax = 8.0f;  // rescale when a block's max exceeds the running max by 2^8
+constexpr float kLazyMax = 8.0f;  // rescale when a step's max exceeds the running max by 2^8
 
-// [hi(p0..p3) | lo(p0..p3)] as bf16 pairs, packed with byte permutes: hi keeps
-// each p's top 16 bits, lo the top 16 bits of the remainder
-__device__ __forceinline__ bf16x8 p_hi_lo_perm(const float (&pr)[4]) {
-    uint32_t u[4], r[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        u[i] = __float_as_uint(pr[i]);
-        r[i] = __float_as_uint(pr[i] - __uint_as_float(u[i] & 0xffff0000u));
-    }
-    const u32x4 w = {__builtin_amdgcn_perm(u[1], u[0], 0x07060302u),
-                     __builtin_amdgcn_perm(u[3], u[2], 0x07060302u),
-                     __builtin_amdgcn_perm(r[1], r[0], 0x07060302u),
-                     __builtin_amdgcn_perm(r[3], r[2], 0x07060302u)};
-    return as_bf16x8(w);
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ uint32_t f16x2_bits(f16x2 h) { return __builtin_bit_cast(uint32_t, h); }
+
+// two bf16 (one word) -> two fp16 (one word), rounded to nearest: exact for
+// magnitudes in [2^-14, 2^16) (fp16 keeps bf16's 8 significant bits), within
+// 2^-25 below (the fp16 subnormal grid is 2^-24); 2^16 and above overflow
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+    const f16x2 h = {(_Float16)__uint_as_float(w << 16), (_Float16)__uint_as_float(w & 0xffff0000u)};
+    return f16x2_bits(h);
+}
+
+// four E4M3 codes -> four fp16 (exact: E4M3 has 4 significant bits and
+// exponents -9 .. 8, all inside fp16)
+__device__ __forceinline__ void e4m3x4_to_f16(uint32_t w, uint32_t &lo, uint32_t &hi) {
+    lo = f16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+    hi = f16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
 }
 
 template <int KV, int D>
-__global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void prefill_mfma_kernel(PrefillParams p) {
     constexpr int EB = KV == kBF16 ? 2 : 1;
     constexpr int TILE_BYTES = kBlock * D * EB;                  // one pool tile (K or V)
-    // LDS stage: K as a bf16 tile in the bf16 pool order (D/8 runs x 16 tokens
-    // x 16 bytes), then V as D x 4 duplicated bf16 cells: cell (token group
-    // tg, dim d) = [t0 t1 | t2 t3 | t0 t1 | t2 t3] of dim d, tokens 4 tg..4 tg+3,
-    // zeroed past the context -- exactly the A operand [V | V] of the
-    // hi + lo P.V product
+    // LDS stage of one step (two blocks A = 2 i, B = 2 i + 1): K of A, then K
+    // of B, each as a bf16 tile in the bf16 pool order (D/8 runs x 16 tokens x
+    // 16 bytes), then V as D x 4 fp16 cells: cell (token group tg, dim d) =
+    // [A t0..t3 | B t0..t3] of dim d, tokens 4 tg..4 tg+3 of each block, zeroed
+    // past the context -- exactly the A operand of the 32-deep P.V product
+    // over the step's 32 tokens
     constexpr int KS_UNITS = kBlock * D * 2 / 16;
     constexpr int VS_UNITS = 4 * D;
-    constexpr int STAGE_UNITS = KS_UNITS + VS_UNITS;
+    constexpr int STAGE_UNITS = 2 * KS_UNITS + VS_UNITS;
     constexpr int NQK = D / 32;  // 32-deep q.K steps per block
     constexpr int NT = D / 16;   // 16 x 16 output tiles per group: tile T = head dims 16 T .. 16 T + 15
 
@@ -107,26 +117,34 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
     const int pos_last = first + min(tile * BQ + BQ, n_new) - 1;
     const int nblk_wg = pos_last < 0 ? 0 : pos_last / kBlock + 1;
 
-    // this lane's two rows (one per group): chunk token, head, position
-    int row_tok[kGroups], row_head[kGroups], pos_mask[kGroups];
-    bool valid[kGroups], live[kGroups];
+    // this lane's two rows (one per group): chunk token, head, position (also
+    // recomputed after the loop rather than kept live across it)
+    struct Row {
+        int tok, head;
+        bool valid, live;
+    };
+    auto row_of = [&](int k) {
+        const int r = kRowsPerWave * wave + 16 * k + n;
+        Row w;
+        w.tok = tile * BQ + r / G;
+        w.head = g * G + r % G;
+        w.valid = r < BQ * G && w.tok < n_new;
+        w.live = w.valid && first + w.tok >= 0;
+        return w;
+    };
+    int pos_mask[kGroups];
     int minpos = 0x7fffffff;
 #pragma unroll
     for (int k = 0; k < kGroups; ++k) {
-        const int r = kRowsPerWave * wave + 16 * k + n;
-        row_tok[k] = tile * BQ + r / G;
-        row_head[k] = g * G + r % G;
-        valid[k] = r < BQ * G && row_tok[k] < n_new;
-        const int pos = first + row_tok[k];
-        live[k] = valid[k] && pos >= 0;
+        const Row w = row_of(k);
         // rows that produce no output are masked like the context's last token
-        pos_mask[k] = live[k] ? pos : ctx - 1;
+        pos_mask[k] = w.live ? first + w.tok : ctx - 1;
         minpos = min(minpos, pos_mask[k]);
     }
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) minpos = min(minpos, __shfl_xor(minpos, o));
-    // the same in every lane: as a uniform value the per-block mask test is a
-    // scalar branch, not an exec-masked region issued on every block
+    // the same in every lane: as a uniform value the per-step mask test is a
+    // scalar branch, not an exec-masked region issued on every step
     minpos = __builtin_amdgcn_readfirstlane(minpos);
 
     // Q^T operands (zero for rows outside the chunk): head dims 8 (4 u + c) .. +7
@@ -134,24 +152,26 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
     bf16x8 qop[kGroups][NQK];
 #pragma unroll
     for (int k = 0; k < kGroups; ++k) {
+        const Row w = row_of(k);
         const uint16_t *qrow = reinterpret_cast<const uint16_t *>(p.q) +
-                               ((int64_t)(q0 + row_tok[k]) * p.num_q_heads + row_head[k]) * D;
+                               ((int64_t)(q0 + w.tok) * p.num_q_heads + w.head) * D;
 #pragma unroll
         for (int u = 0; u < NQK; ++u) {
             u32x4 v = {0u, 0u, 0u, 0u};
-            if (valid[k]) v = *reinterpret_cast<const u32x4 *>(qrow + 8 * (4 * u + c));
+            if (w.valid) v = *reinterpret_cast<const u32x4 *>(qrow + 8 * (4 * u + c));
             qop[k][u] = as_bf16x8(v);
         }
     }
 
-    float m[kGroups], m_lazy[kGroups], m_use[kGroups], l[kGroups];  // m_lazy = m + kLazyMax
+    // per row: running max (log2 units), sum, and the exponent above which the
+    // max is raised (-inf until the first raise, then the margin)
+    float m[kGroups], l[kGroups], thr[kGroups];
     floatx4 acc[kGroups][NT];
 #pragma unroll
     for (int k = 0; k < kGroups; ++k) {
-        m[k] = kNegInfF;
-        m_lazy[k] = kNegInfF;
-        m_use[k] = 0.f;
+        m[k] = 0.f;
         l[k] = 0.f;
+        thr[k] = kNegInfF;
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[k][t] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
@@ -161,163 +181,209 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
     const char *vpool = static_cast<const char *>(p.v_pool);
     auto ok = [&](int32_t b) { return b >= 0 && b < p.num_blocks; };
 
-    // Staging.  K: thread t < KU loads pool unit t of the block's K tile and
-    // writes it to the stage (fp8: widened to two bf16 runs).  V: thread t
-    // writes stage cells t, t + 256, ... (cell (tg, d) = unit tg * D + d) and
-    // loads the words of dim d from the pool cell holding it (bf16: 8 bytes,
-    // fp8: 4); the lanes of one pool cell together load its 16 bytes.  Every lane writes one whole 16-byte
-    // unit after its neighbour's, which keeps the LDS stores free of bank
-    // conflicts.  The loads go through tile resources, so a lane past the K
-    // tile, or a block id out of range, loads zeros without touching memory.
-    constexpr int KU = TILE_BYTES / 16;   // K pool units per block (<= 256)
+    // Staging of one step.  K: the step's 2 KU pool units (KU per block) are
+    // spread over the threads -- one unit of each block per thread when
+    // KU = 256, else thread t takes unit t % KU of block t / KU (the same for
+    // a whole wavefront) -- and written to the stage (fp8: widened to two
+    // bf16 runs).  V: thread t writes stage cells t, t + 256,
+    // ... (cell (tg, d) = unit tg * D + d) and loads the words of dim d of both
+    // blocks from the pool cells holding them (bf16: 8 bytes each, fp8: 4);
+    // the lanes of one pool cell together load its 16 bytes.  Every lane
+    // writes one whole 16-byte unit after its neighbour's, which keeps the
+    // LDS stores free of bank conflicts.  The loads go through tile
+    // resources, so a block id out of range loads zeros without touching
+    // memory.
+    constexpr int KU = TILE_BYTES / 16;   // K pool units per block (64, 128 or 256)
+    constexpr int KI = KU == kThreads ? 2 : 1;  // K units per thread and step
     constexpr int VLOADS = VS_UNITS / kThreads;
     constexpr int W = 4 / EB;             // head dims per pool V cell
-    static_assert(KU <= kThreads && VS_UNITS % kThreads == 0, "staging split");
+    static_assert(KU % 64 == 0 && KU <= kThreads && VS_UNITS % kThreads == 0, "staging split");
     using VWords = typename std::conditional<KV == kBF16, uint2, uint32_t>::type;
-    auto gload = [&](int32_t b, u32x4 &kr, VWords (&vr)[VLOADS]) {
-        const bool good = ok(b);
-        const int64_t off = ((int64_t)(good ? b : 0) * p.num_kv_heads + g) * TILE_BYTES;
-        const auto kt = tile_rsrc(kpool + off, good ? TILE_BYTES : 0);
-        const auto vt = tile_rsrc(vpool + off, good ? TILE_BYTES : 0);
-        kr = load_tile<false>(kt, threadIdx.x * 16);
+    const int wave_t0 = __builtin_amdgcn_readfirstlane((int)threadIdx.x);  // first thread of the wavefront
+    auto gload = [&](int32_t ba, int32_t bb, u32x4 (&kr)[KI], VWords (&vr)[VLOADS][2]) {
+        const bool good_a = ok(ba), good_b = ok(bb);
+        const int64_t off_a = ((int64_t)(good_a ? ba : 0) * p.num_kv_heads + g) * TILE_BYTES;
+        const int64_t off_b = ((int64_t)(good_b ? bb : 0) * p.num_kv_heads + g) * TILE_BYTES;
+        const auto ka = tile_rsrc(kpool + off_a, good_a ? TILE_BYTES : 0);
+        const auto kb = tile_rsrc(kpool + off_b, good_b ? TILE_BYTES : 0);
+        const auto va = tile_rsrc(vpool + off_a, good_a ? TILE_BYTES : 0);
+        const auto vb = tile_rsrc(vpool + off_b, good_b ? TILE_BYTES : 0);
+        if constexpr (KU == kThreads) {  // one unit of each block per thread
+            kr[0] = load_tile<false>(ka, threadIdx.x * 16);
+            kr[1] = load_tile<false>(kb, threadIdx.x * 16);
+        } else if (wave_t0 < 2 * KU) {   // block wave_t0 / KU, unit t % KU
+            kr[0] = load_tile<false>(wave_t0 < KU ? ka : kb, (threadIdx.x % KU) * 16);
+        }
 #pragma unroll
         for (int i = 0; i < VLOADS; ++i) {
             const int su = threadIdx.x + i * kThreads;
             const int tg = su / D, d = su % D;
             const int off = (tg * (D / W) + d / W) * 16 + (d % W) * (4 * EB);
-            if constexpr (KV == kBF16)
-                vr[i] = load_tile_b64(vt, off);
-            else
-                vr[i] = load_tile_b32(vt, off);
+            if constexpr (KV == kBF16) {
+                vr[i][0] = load_tile_b64(va, off);
+                vr[i][1] = load_tile_b64(vb, off);
+            } else {
+                vr[i][0] = load_tile_b32(va, off);
+                vr[i][1] = load_tile_b32(vb, off);
+            }
         }
     };
-    // ... and writes them to a stage in the LDS order above (fp8 widened to
-    // bf16, exact); V of tokens at or past `nvalid` is zeroed
-    auto swrite = [&](int st, const u32x4 &kr, const VWords (&vr)[VLOADS], int nvalid) {
+    // ... and writes them to a stage in the LDS order above (K: fp8 widened to
+    // bf16; V: widened to fp16), the V of tokens at or past `nvalid` (counted
+    // from block A's first token) zeroed
+    auto swrite = [&](int st, const u32x4 (&kr)[KI], const VWords (&vr)[VLOADS][2], int nvalid) {
         u32x4 *ks = stage[st];
-        u32x4 *vs = stage[st] + KS_UNITS;
-        const int t = threadIdx.x;
-        if (t < KU) {
-            if constexpr (KV == kBF16) {
-                ks[t] = kr;
-            } else {  // fp8 run t / 16 (16 dims) of token t % 16 -> two bf16 runs
-                const int rr = t >> 4, tt = t & 15;
-                uint32_t a0, a1, a2, a3, b0, b1, b2, b3;
-                e4m3x4_to_bf16(kr[0], a0, a1);
-                e4m3x4_to_bf16(kr[1], a2, a3);
-                e4m3x4_to_bf16(kr[2], b0, b1);
-                e4m3x4_to_bf16(kr[3], b2, b3);
-                ks[(2 * rr) * kBlock + tt] = u32x4{a0, a1, a2, a3};
-                ks[(2 * rr + 1) * kBlock + tt] = u32x4{b0, b1, b2, b3};
+        u32x4 *vs = stage[st] + 2 * KS_UNITS;
+#pragma unroll
+        for (int i = 0; i < KI; ++i) {
+            // unit e = t + 256 i: block e / KU (wavefront-uniform), unit e % KU
+            const int e0 = KU == kThreads ? kThreads * i : wave_t0;
+            if (KU == kThreads || wave_t0 < 2 * KU) {
+                u32x4 *kb = ks + (e0 < KU ? 0 : KS_UNITS);
+                const int u = (int)threadIdx.x % KU;
+                if constexpr (KV == kBF16) {
+                    kb[u] = kr[i];
+                } else {  // fp8 run u / 16 (16 dims) of token u % 16 -> two bf16 runs
+                    const int rr = u >> 4, tt = u & 15;
+                    uint32_t a0, a1, a2, a3, b0, b1, b2, b3;
+                    e4m3x4_to_bf16(kr[i][0], a0, a1);
+                    e4m3x4_to_bf16(kr[i][1], a2, a3);
+                    e4m3x4_to_bf16(kr[i][2], b0, b1);
+                    e4m3x4_to_bf16(kr[i][3], b2, b3);
+                    kb[(2 * rr) * kBlock + tt] = u32x4{a0, a1, a2, a3};
+                    kb[(2 * rr + 1) * kBlock + tt] = u32x4{b0, b1, b2, b3};
+                }
             }
         }
 #pragma unroll
         for (int i = 0; i < VLOADS; ++i) {
-            const int su = t + i * kThreads;
-            uint32_t w0, w1;  // tokens (t0 t1) and (t2 t3) of dim d as bf16 pairs
-            if constexpr (KV == kBF16) {
-                w0 = vr[i].x;
-                w1 = vr[i].y;
-            } else {
-                e4m3x4_to_bf16(vr[i], w0, w1);
+            const int su = threadIdx.x + i * kThreads;
+            uint32_t w[4];  // A (t0 t1), A (t2 t3), B (t0 t1), B (t2 t3) of dim d as fp16 pairs
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                if constexpr (KV == kBF16) {
+                    w[2 * b] = bf16x2_to_f16x2(vr[i][b].x);
+                    w[2 * b + 1] = bf16x2_to_f16x2(vr[i][b].y);
+                } else {
+                    e4m3x4_to_f16(vr[i][b], w[2 * b], w[2 * b + 1]);
+                }
+                const int nv = nvalid - b * kBlock;
+                if (nv < kBlock) {  // the context's last block (or past it): zero the tokens past it
+                    uint32_t k01, k23;
+                    v_keep_masks(su / D, nv, k01, k23);
+                    w[2 * b] &= k01;
+                    w[2 * b + 1] &= k23;
+                }
             }
-            if (nvalid < kBlock) {  // the context's last block: zero the tokens past it
-                uint32_t k01, k23;
-                v_keep_masks(su / D, nvalid, k01, k23);
-                w0 &= k01;
-                w1 &= k23;
-            }
-            // The upper pair as explicit copies: from the duplicated pair
-            // {w0, w1, w0, w1} this compiler (hipcc of ROCm 7.2) has emitted
-            // a 16-byte store whose upper half was the address register.
-            uint32_t c0, c1;
-            asm("v_mov_b32 %0, %2\n\tv_mov_b32 %1, %3" : "=v"(c0), "=v"(c1) : "v"(w0), "v"(w1));
-            vs[su] = u32x4{w0, w1, c0, c1};
+            vs[su] = u32x4{w[0], w[1], w[2], w[3]};
         }
     };
 
-    // Block j from stage st.  `bias` is -inf when the block id is out of
-    // range (its zero K gives zero scores, and every token is masked) and 0
-    // otherwise, which leaves the product's rounding unchanged; MASK: some
-    // row's position falls inside the block (the causal mask is applied).
-    auto compute_block = [&](auto mask_tag, int st, int j, float bias) {
+    // Step i: blocks j = 2 i and j + 1, from stage st = i & 1.  `bias_a` / `bias_b` is
+    // -inf when that block's id is out of range (its zero K gives zero
+    // scores, and every token is masked) and 0 otherwise, which leaves the
+    // product's rounding unchanged; MASK: some row's position falls inside
+    // the step (the causal mask is applied).
+    auto compute_step = [&](auto mask_tag, int st, int j, float bias_a, float bias_b) {
         constexpr bool MASK = decltype(mask_tag)::value;
         const u32x4 *ks = stage[st] + c * kBlock + n;  // K run c (+ 4 per step), token n
-        const u32x4 *vs = stage[st] + KS_UNITS + c * D + n;  // V cell (token group c, dim n (+ 16 T))
-        bf16x8 kop[NQK];
-#pragma unroll
-        for (int u = 0; u < NQK; ++u) kop[u] = as_bf16x8(ks[u * 4 * kBlock]);
+        const u32x4 *vs = stage[st] + 2 * KS_UNITS + c * D + n;  // V cell (token group c, dim n (+ 16 T))
 
-        // scores of both groups first, so their matrix-core products issue back to back
-        floatx4 sacc[kGroups];
+        // scores of both blocks and groups first, so their matrix-core
+        // products issue back to back: sacc[k][b] = S^T of block b, group k
+        floatx4 sacc[kGroups][2];
 #pragma unroll
-        for (int k = 0; k < kGroups; ++k) {
-            sacc[k] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int b = 0; b < 2; ++b) {
 #pragma unroll
-            for (int u = 0; u < NQK; ++u)
-                sacc[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[u], qop[k][u], sacc[k], 0, 0, 0);
+            for (int k = 0; k < kGroups; ++k) sacc[k][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int u = 0; u < NQK; ++u) {
+                const bf16x8 kop = as_bf16x8(ks[b * KS_UNITS + u * 4 * kBlock]);
+#pragma unroll
+                for (int k = 0; k < kGroups; ++k)
+                    sacc[k][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[k][u], sacc[k][b], 0, 0, 0);
+            }
         }
-        // Scaled scores; tokens 4c + i past a row's position are masked by
-        // selection.  The scaled score itself (not a fused multiply-add with
-        // the max) enters the exponent, so the token holding the max gets
-        // probability exactly 1.
-        float sc[kGroups][4], bl[kGroups];
+        // Exponents relative to the running max, e = score * scale * log2(e)
+        // - m, one fused multiply-add per score (e[k][4 b + i] = token 4 c + i
+        // of block b); tokens past a row's position are masked by selection.
+        float e[kGroups][8], bl[kGroups];
         bool want = false;
 #pragma unroll
         for (int k = 0; k < kGroups; ++k) {
+            const float ca = bias_a - m[k], cb = bias_b - m[k];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sc[k][i] = __builtin_fmaf(sacc[k][i], p.qk_scale_log2, bias);
+            for (int i = 0; i < 4; ++i) {
+                e[k][i] = __builtin_fmaf(sacc[k][0][i], p.qk_scale_log2, ca);
+                e[k][4 + i] = __builtin_fmaf(sacc[k][1][i], p.qk_scale_log2, cb);
+            }
             if constexpr (MASK) {
                 const int lim = pos_mask[k] - j * kBlock - 4 * c;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sc[k][i] = i > lim ? kNegInfF : sc[k][i];
+                for (int i = 0; i < 4; ++i) {
+                    e[k][i] = i > lim ? kNegInfF : e[k][i];
+                    e[k][4 + i] = kBlock + i > lim ? kNegInfF : e[k][4 + i];
+                }
             }
-            bl[k] = fmaxf(fmaxf(sc[k][0], sc[k][1]), fmaxf(sc[k][2], sc[k][3]));
-            want = want || bl[k] > m_lazy[k];
+            bl[k] = fmaxf(fmaxf(fmaxf(e[k][0], e[k][1]), fmaxf(e[k][2], e[k][3])),
+                          fmaxf(fmaxf(e[k][4], e[k][5]), fmaxf(e[k][6], e[k][7])));
+            want = want || bl[k] > thr[k];
         }
-        // the row max is exchanged across lanes, and the running max raised
-        // (rescaling the numerators), only when some lane's block max exceeds
-        // the running max by more than the margin; otherwise every probability
-        // stays below 2^8 and the max stays put
+        // The running max m is raised only when some lane's exponent exceeds
+        // the threshold (the margin 8, or -inf before the row's first
+        // unmasked token): then the row's largest exponent d is exchanged
+        // across lanes, m grows by d, the numerators and the sum are rescaled
+        // by 2^-d (zero at the first raise) and the step's exponents lowered
+        // by d, so the row's max token gets probability exactly 1.  Otherwise
+        // every probability stays below 2^8 and m stays put.
         if (__builtin_amdgcn_ballot_w64(want) != 0) {
 #pragma unroll
             for (int k = 0; k < kGroups; ++k) {
                 const float bm = max_xor32(max_xor16(bl[k]));
-                const bool grow = bm > m_lazy[k];
-                const float m_new = grow ? bm : m[k];
-                const float mu = m_new == kNegInfF ? 0.f : m_new;
-                const float alpha = grow ? __builtin_amdgcn_exp2f(m[k] - mu) : 1.f;
-                m[k] = m_new;
-                m_lazy[k] = m_new + kLazyMax;
-                m_use[k] = mu;
+                const bool grow = bm > thr[k];
+                const float d = grow ? bm : 0.f;
+                const float alpha = grow ? (thr[k] == kNegInfF ? 0.f : __builtin_amdgcn_exp2f(-d)) : 1.f;
+                m[k] += d;
+                thr[k] = grow ? kLazyMax : thr[k];
                 l[k] *= alpha;
 #pragma unroll
                 for (int t = 0; t < NT; ++t) acc[k][t] *= alpha;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) e[k][i] -= d;
             }
         }
-        bf16x8 pop[kGroups];
+        // P^T operands: the step's 8 probabilities of the lane rounded to
+        // fp16; the row sum adds the rounded values, so the output is a
+        // weighted mean of V with exactly the weights the product used
+        f16x8 pop[kGroups];
 #pragma unroll
         for (int k = 0; k < kGroups; ++k) {
-            float pr[4];
+            f16x2 h[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(sc[k][i] - m_use[k]);
-            l[k] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-            pop[k] = p_hi_lo_perm(pr);
+            for (int i = 0; i < 4; ++i)
+                h[i] = f16x2{(_Float16)__builtin_amdgcn_exp2f(e[k][2 * i]),
+                             (_Float16)__builtin_amdgcn_exp2f(e[k][2 * i + 1])};
+            const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+            float ls = l[k];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ls = __builtin_amdgcn_fdot2(h[i], one, ls, false);
+            l[k] = ls;
+            pop[k] = f16x8{h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
         }
 
-        // O^T += V^T . P^T: the staged cell is the ready [V | V] operand
+        // O^T += V^T . P^T over the step's 32 tokens: the staged cell is the ready operand
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            const bf16x8 a = as_bf16x8(vs[16 * t]);
+            const f16x8 a = __builtin_bit_cast(f16x8, vs[16 * t]);
 #pragma unroll
             for (int k = 0; k < kGroups; ++k)
-                acc[k][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pop[k], acc[k][t], 0, 0, 0);
+                acc[k][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pop[k], acc[k][t], 0, 0, 0);
         }
     };
 
-    // Block ids come by scalar loads from the table, two blocks ahead.  Block
-    // j is computed from stage j & 1 while block j + 1 is in flight in
-    // registers; block j + 1 then goes to the other stage and block j + 2's
+    // Block ids come by scalar loads from the table, one step ahead.  Step i
+    // is computed from stage i & 1 while step i + 1 is in flight in
+    // registers; step i + 1 then goes to the other stage and step i + 2's
     // loads are issued (every step issues the same loads), and one barrier
     // ends the step.
     auto id_at = [&](int j) -> int32_t {
@@ -325,35 +391,37 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
         return j < nblk_wg ? b : -1;
     };
     if (nblk_wg > 0) {
-        int32_t id_cur = id_at(0), id_next = id_at(1);
-        u32x4 kpre;
-        VWords vpre[VLOADS];
-        gload(id_cur, kpre, vpre);
+        const int nstep = (nblk_wg + 1) / 2;
+        int32_t ida = id_at(0), idb = id_at(1), nida = id_at(2), nidb = id_at(3);
+        u32x4 kpre[KI];
+        VWords vpre[VLOADS][2];
+        gload(ida, idb, kpre, vpre);
         swrite(0, kpre, vpre, ctx);
-        gload(id_next, kpre, vpre);
+        gload(nida, nidb, kpre, vpre);
         __syncthreads();
-        // blocks before jm lie at or before every row's position of the
+        // steps whose blocks lie at or before every row's position of the
         // wavefront (no causal mask); the rest are masked
-        const int jm = min((minpos + 1) / kBlock, nblk_wg);
-        auto next = [&](int j) {
-            const int32_t id_after = id_at(j + 2);
-            if (j + 1 < nblk_wg) swrite((j + 1) & 1, kpre, vpre, ctx - (j + 1) * kBlock);
-            gload(id_after, kpre, vpre);
-            id_cur = id_next;
-            id_next = id_after;
+        const int sm = min((minpos + 1) / kBlock, nblk_wg) / 2;
+        auto next = [&](int i) {
+            const int32_t a2 = id_at(2 * i + 4), b2 = id_at(2 * i + 5);
+            if (i + 1 < nstep) swrite((i + 1) & 1, kpre, vpre, ctx - (2 * i + 2) * kBlock);
+            gload(a2, b2, kpre, vpre);
+            ida = nida;
+            idb = nidb;
+            nida = a2;
+            nidb = b2;
             __syncthreads();
         };
-        // Every wavefront computes every block of the workgroup: blocks past
-        // its own rows are masked out by the causal test (at most one block
-        // for G = 8), and a straight-line loop body keeps the accumulators
-        // in place.
-        for (int j = 0; j < jm; ++j) {
-            compute_block(std::false_type{}, j & 1, j, ok(id_cur) ? 0.f : kNegInfF);
-            next(j);
+        // Every wavefront computes every step of the workgroup: blocks past
+        // its own rows are masked out by the causal test, and a straight-line
+        // loop body keeps the accumulators in place.
+        for (int i = 0; i < sm; ++i) {
+            compute_step(std::false_type{}, i & 1, 2 * i, ok(ida) ? 0.f : kNegInfF, ok(idb) ? 0.f : kNegInfF);
+            next(i);
         }
-        for (int j = jm; j < nblk_wg; ++j) {
-            compute_block(std::true_type{}, j & 1, j, ok(id_cur) ? 0.f : kNegInfF);
-            next(j);
+        for (int i = sm; i < nstep; ++i) {
+            compute_step(std::true_type{}, i & 1, 2 * i, ok(ida) ? 0.f : kNegInfF, ok(idb) ? 0.f : kNegInfF);
+            next(i);
         }
     }
 
@@ -363,12 +431,13 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
     for (int k = 0; k < kGroups; ++k) {
         float lt = l[k];
         lt = add_xor32(add_xor16(lt));
-        if (!valid[k]) continue;
-        const float f = live[k] && lt > 0.f ? p.out_scale / lt : 0.f;
-        float *orow = p.out + ((int64_t)(q0 + row_tok[k]) * p.num_q_heads + row_head[k]) * D;
+        const Row w = row_of(k);
+        if (!w.valid) continue;
+        const float f = w.live && lt > 0.f ? p.out_scale / lt : 0.f;
+        float *orow = p.out + ((int64_t)(q0 + w.tok) * p.num_q_heads + w.head) * D;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            const float4 v = live[k] ? make_float4(acc[k][t][0] * f, acc[k][t][1] * f, acc[k][t][2] * f,
+            const float4 v = w.live ? make_float4(acc[k][t][0] * f, acc[k][t][1] * f, acc[k][t][2] * f,
                                                    acc[k][t][3] * f)
                                      : make_float4(0.f, 0.f, 0.f, 0.f);
             *reinterpret_cast<float4 *>(orow + 16 * t + 4 * c) = v;

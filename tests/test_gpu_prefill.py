@@ -87,8 +87,10 @@ def test_prefill_full_size_sampled_rows(name):
 @pytest.mark.parametrize("where", ["first", "boundary", "random"])
 def test_prefill_one_hot_probe_bit_exact(name, where):
     """K is zero except K[t][dim 0] = c (c * scale >= 200) and every query is
-    e0: each row at a position >= t returns V[t] exactly; rows before t never
-    see it."""
+    e0: each row at a position >= t returns V[t] as the product sees it --
+    exactly its fp16 value (the P.V operand type: equal to V for fp8 codes and
+    for bf16 magnitudes of 2^-14 and above) -- and rows before t never see
+    it."""
     w = wl.make_prefill_workload(name, small=True)
     fp8 = w.pool_dtype == ops.FP8
     c = 448.0 if fp8 else 1000.0
@@ -124,7 +126,7 @@ def test_prefill_one_hot_probe_bit_exact(name, where):
         for g in range(w.Hkv):
             raw = oracle.gather(vp, True, w.pool_dtype, w.Hkv, w.D, w.block_tables[s], t + 1, g)[t]
             row = oracle.fp8_decode(raw) if fp8 else as_f64(raw.view(np.uint16), w.pool_dtype)
-            vt[g * w.group:(g + 1) * w.group] = row
+            vt[g * w.group:(g + 1) * w.group] = row.astype(np.float16).astype(np.float64)
         a, b = int(w.query_start[s]), int(w.query_start[s + 1])
         first = int(w.context_lens[s]) - (b - a)
         for i in range(a, b):
@@ -202,6 +204,26 @@ def test_prefill_edge_cases():
         a = int(w.query_start[s])
         assert_same_bytes(got[a:a + 17], full[a:a + 17])
         assert (got[a + 17:a + 40] == 7.0).all()
+
+
+@pytest.mark.parametrize("factor", [2.0 ** 13, 2.0 ** -12])
+def test_prefill_v_scaled_toward_the_fp16_limits(factor):
+    """bf16 V scaled by a power of two toward the top of the fp16 range (max
+    |V| about 4e4, below the 2^16 limit) and toward its subnormals: the output
+    scales with V, and the error relative to that scale stays within the
+    tolerance (at 2^-12 V's fp16 subnormals, spaced 2^-24, add at most 2^-13
+    of that scale)."""
+    w = wl.make_prefill_workload("chunked_gqa70b", small=True)
+    _, k, v, slots = w.ops[0]
+    v2 = (v.float() * factor).to(v.dtype)
+    assert torch.equal(v2.float(), v.float() * factor)  # exact in bf16
+    w.ops = [("write", k, v2, slots)]
+    kp, vp = oracle_pools(w)
+    ref = oracle_prefill(w, kp, vp)
+    got = gpu_prefill(w, gpu_pool(w))
+    assert np.isfinite(got).all()
+    err = float(np.max(np.abs(got - ref))) / factor
+    assert err <= tolerance(w), "max abs error / factor %.3e" % err
 
 
 def _shape_workload(D, Hq, Hkv, pool_dt, seed):
