@@ -15,8 +15,8 @@
 // them) and BQ = 128 / G consecutive chunk tokens form 128 rows
 // (row r = token r / G, head g G + r % G); one workgroup (4 wavefronts) takes
 // one such tile of one sequence, and each wavefront owns 32 of its rows as
-// two 16-column matrix-core groups.  Workgroups are issued latest tile
-// first, so the longest causal ranges start first.
+// two 16-column matrix-core groups.  The tiles of one (sequence, KV head)
+// pair run together on one XCD, latest tile (longest causal range) first.
 //
 // Staging.  The workgroup walks its blocks 0 .. (its last row's position) / 16
 // two at a time: a step covers blocks 2 i and 2 i + 1.  Every step's K and V
@@ -52,6 +52,7 @@ namespace {
 constexpr int kGroups = 2;                                    // 16-row groups per wavefront
 constexpr int kRowsPerWave = 16 * kGroups;                    // 32
 constexpr int kRowsPerTile = kRowsPerWave * (kThreads / 64);  // 128
+constexpr int kXcds = 8;          // accelerator complex dies; workgroup b runs on XCD b % 8
 constexpr float kLazyMax = 8.0f;  // rescale when a step's max exceeds the running max by 2^8
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -99,10 +100,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
 
     const int G = p.group;
     const int BQ = kRowsPerTile / G;
-    const int sg = p.num_seqs * p.num_kv_heads;
-    const int tile = p.num_tiles - 1 - (int)(blockIdx.x / sg);
-    const int s = (int)(blockIdx.x % sg) / p.num_kv_heads;
-    const int g = (int)(blockIdx.x % sg) % p.num_kv_heads;
+    // Workgroup b runs on XCD b % 8.  Each (sequence, KV head) pair -- whose
+    // tiles all read the same blocks -- goes to one XCD (pair q to XCD q % 8),
+    // and an XCD takes its pairs one after another, all tiles of a pair
+    // together, longest first: the blocks the tiles in flight share stay in
+    // that XCD's L2.  Workgroups past the last pair have nothing to do.
+    const int pairs = p.num_seqs * p.num_kv_heads;
+    const int xcd = (int)(blockIdx.x % kXcds);
+    const int local = (int)(blockIdx.x / kXcds);
+    const int pair = xcd + kXcds * (local / p.num_tiles);
+    if (pair >= pairs) return;
+    const int tile = p.num_tiles - 1 - local % p.num_tiles;
+    const int s = pair / p.num_kv_heads;
+    const int g = pair % p.num_kv_heads;
 
     int ctx = p.context_lens[s];
     ctx = ctx < 0 ? 0 : (ctx > p.max_blocks_per_seq * kBlock ? p.max_blocks_per_seq * kBlock : ctx);
@@ -447,7 +457,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
 
 template <int KV, int D>
 hipError_t launch(const PrefillParams &p, hipStream_t stream, const LaunchEvents *ev) {
-    const int64_t grid = (int64_t)p.num_tiles * p.num_seqs * p.num_kv_heads;
+    const int64_t pairs = (int64_t)p.num_seqs * p.num_kv_heads;
+    const int64_t grid = (int64_t)p.num_tiles * kXcds * ((pairs + kXcds - 1) / kXcds);
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
     return launch_kernel(prefill_mfma_kernel<KV, D>, dim3((unsigned)grid), dim3(kThreads), stream, ev, p);
 }
