@@ -6,9 +6,10 @@
 // two products of decode attention become small dense contractions:
 //     S^T[16 tokens][16 heads]  = K[16][D] . Q^T[D][16]           (heads >= G are zero)
 //     O^T[D][16 heads]         += V^T[D][16 tokens] . P^T[16][16]
-// Both run on gfx950's bf16 matrix cores (v_mfma_f32_16x16x32_bf16 for the
-// scores, v_mfma_f32_16x16x16_bf16 for P.V) with fp32 accumulation.  An fp8
-// (E4M3FN) pool is widened to bf16 in registers, which is exact.
+// Both run on gfx950's matrix cores (v_mfma_f32_16x16x32_bf16 for the
+// scores, v_mfma_f32_16x16x16_bf16 -- or _f16 with an fp8 pool -- for P.V)
+// with fp32 accumulation.  An fp8 (E4M3FN) pool is widened in registers
+// (K to bf16, V to fp16), which is exact.
 //
 // Work split: one workgroup per (sequence, KV head, partition of
 // partition_tokens tokens); its four wavefronts take every fourth block and
@@ -33,7 +34,10 @@
 //   P^T is split into bf16 high and low parts (p = hi + lo to 16 significant
 //     bits); each 16 x 16 output tile takes two 16-deep products of the same
 //     V operand (tokens 4c..4c+3), one against hi and one against lo, so P
-//     enters at ~16-bit precision.
+//     enters at ~16-bit precision.  With an fp8 pool, V is widened to fp16
+//     instead (exact for every E4M3 code) and P rounded to fp16 (relative
+//     error <= 2^-11, far inside an fp8 cache's tolerance): one 16-deep fp16
+//     product per tile.
 //   Tokens past the context are excluded by selection: their scores are set
 //     to -inf and their V operand elements to zero before the product.
 #include "pa_internal.h"
@@ -228,7 +232,20 @@ __device__ __forceinline__ void walk_blocks(const DecodeParams &p, int s, int g,
 #pragma unroll
         for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(sc[i] - m_ref);
         m = m_new;
-        l = l * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+        // fp8 pool: P rounded to fp16 (relative error <= 2^-11) against V
+        // widened to fp16 (exact for every E4M3 code), one 16-deep product
+        // per tile; the sum adds the same rounded values.  bf16 / fp32-like
+        // pools: P carried as bf16 hi + lo (16 significant bits).
+        f16x4 pf;
+        if constexpr (KV == kFP8) {
+            const f16x2 h01 = {(_Float16)pr[0], (_Float16)pr[1]};
+            const f16x2 h23 = {(_Float16)pr[2], (_Float16)pr[3]};
+            const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+            l = __builtin_amdgcn_fdot2(h23, one, __builtin_amdgcn_fdot2(h01, one, l * alpha, false), false);
+            pf = f16x4{h01[0], h01[1], h23[0], h23[1]};
+        } else {
+            l = l * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+        }
         // rescale the numerators only when some real column's maximum moved
         if (__builtin_amdgcn_ballot_w64(n < ncols && alpha != 1.f) != 0) {
 #pragma unroll
@@ -236,9 +253,12 @@ __device__ __forceinline__ void walk_blocks(const DecodeParams &p, int s, int g,
         }
 
         // P^T operands: hi(p0..p3) and lo(p0..p3), tokens 4c..4c+3
-        const u32x4 pw = as_u32x4(p_operand_hi_lo(pr));
-        const bf16x4 phi = as_bf16x4(pw[0], pw[1]);
-        const bf16x4 plo = as_bf16x4(pw[2], pw[3]);
+        bf16x4 phi = {}, plo = {};
+        if constexpr (KV != kFP8) {
+            const u32x4 pw = as_u32x4(p_operand_hi_lo(pr));
+            phi = as_bf16x4(pw[0], pw[1]);
+            plo = as_bf16x4(pw[2], pw[3]);
+        }
 
         // zero the V elements of tokens past the context (last block only;
         // they may hold anything, NaN included)
@@ -253,17 +273,20 @@ __device__ __forceinline__ void walk_blocks(const DecodeParams &p, int s, int g,
         for (int jj = 0; jj < NVL; ++jj) {
 #pragma unroll
             for (int w = 0; w < W; ++w) {
-                uint32_t v01, v23;
-                if constexpr (KV == kBF16) {
-                    v01 = vr[jj][2 * w];
-                    v23 = vr[jj][2 * w + 1];
-                } else {
-                    e4m3x4_to_bf16(vr[jj][w], v01, v23);
-                }
-                const bf16x4 a = as_bf16x4(v01 & keep01, v23 & keep23);
                 floatx4 &o = acc[jj * W + w];
-                o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, phi, o, 0, 0, 0);
-                o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, plo, o, 0, 0, 0);
+                if constexpr (KV == kFP8) {
+                    const f16x2 lo2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(vr[jj][w], 1.0f, false);
+                    const f16x2 hi2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(vr[jj][w], 1.0f, true);
+                    const uint32_t v01 = __builtin_bit_cast(uint32_t, lo2) & keep01;
+                    const uint32_t v23 = __builtin_bit_cast(uint32_t, hi2) & keep23;
+                    const f16x4 a = __builtin_bit_cast(f16x4, (uint64_t)v01 | ((uint64_t)v23 << 32));
+                    o = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pf, o, 0, 0, 0);
+                } else {
+                    const uint32_t v01 = vr[jj][2 * w], v23 = vr[jj][2 * w + 1];
+                    const bf16x4 a = as_bf16x4(v01 & keep01, v23 & keep23);
+                    o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, phi, o, 0, 0, 0);
+                    o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, plo, o, 0, 0, 0);
+                }
             }
         }
     };

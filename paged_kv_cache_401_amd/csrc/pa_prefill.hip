@@ -55,9 +55,6 @@ constexpr int kRowsPerTile = kRowsPerWave * (kThreads / 64);  // 128
 constexpr int kXcds = 8;          // accelerator complex dies; workgroup b runs on XCD b % 8
 constexpr float kLazyMax = 8.0f;  // rescale when a step's max exceeds the running max by 2^8
 
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-
 __device__ __forceinline__ uint32_t f16x2_bits(f16x2 h) { return __builtin_bit_cast(uint32_t, h); }
 
 // two bf16 (one word) -> two fp16 (one word), rounded to nearest: exact for
