@@ -50,6 +50,7 @@ namespace pa {
 namespace {
 
 constexpr float kNegInf = kNegInfF;
+constexpr float kLazyMax = 8.0f;  // raise the running maximum only past 2^8 (base-2 scores)
 
 // LDS of one workgroup: the wavefronts' softmax states and numerators,
 // merged at the end of a work item
@@ -218,20 +219,29 @@ __device__ __forceinline__ void walk_blocks(const DecodeParams &p, int s, int g,
                 if (n < lo || n >= hi) sc[i] = kNegInf;
             }
         }
+        // The running maximum is raised lazily: only when some lane's score
+        // exceeds it by more than 8 (base 2) is the column maximum exchanged
+        // across lanes and the running state rescaled; otherwise the block's
+        // probabilities stay below 2^8 against the old maximum.  (Before a
+        // column's first finite score its maximum is -inf, so the first
+        // block always raises it.)
         float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-        bm = max_xor32(max_xor16(bm));
-        const float m_new = fmaxf(m, bm);
+        float alpha = 1.f;
+        if (__builtin_amdgcn_ballot_w64(bm > m + kLazyMax) != 0) {
+            bm = max_xor32(max_xor16(bm));
+            const float m_new = fmaxf(m, bm);
+            // a masked column may still have -inf here: -inf - (-inf) would
+            // be NaN, its (zero) state needs no rescale
+            alpha = m_new == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
+            m = m_new;
+        }
         // A masked column may meet a block before any token it attends: its
-        // maximum is still -inf, and -inf - (-inf) would be NaN; exponents
-        // against 0 keep its sum and numerators at 0.  (With every column
-        // attending every block, the first block makes every maximum finite.)
-        float m_ref = m_new;
-        if constexpr (Src::kColumnMask) m_ref = m_new == kNegInf ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m - m_ref);
+        // maximum is still -inf; exponents against 0 keep its sum and
+        // numerators at 0.
+        const float m_ref = m == kNegInf ? 0.f : m;
         float pr[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(sc[i] - m_ref);
-        m = m_new;
         // fp8 pool: P rounded to fp16 (relative error <= 2^-11) against V
         // widened to fp16 (exact for every E4M3 code), one 16-deep product
         // per tile; the sum adds the same rounded values.  bf16 / fp32-like
