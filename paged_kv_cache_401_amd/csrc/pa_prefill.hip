@@ -55,6 +55,18 @@ constexpr int kRowsPerTile = kRowsPerWave * (kThreads / 64);  // 128
 constexpr int kXcds = 8;          // accelerator complex dies; workgroup b runs on XCD b % 8
 constexpr float kLazyMax = 8.0f;  // rescale when a step's max exceeds the running max by 2^8
 
+// Pairs interleaved per XCD.  When every chunk may span its whole context
+// (whole prompts: the tiles of a pair range from one block to the full
+// causal length) and a pair has few tiles, the last pair's longest tile
+// would start last and run alone; taking 4 pairs together, their tiles
+// interleaved longest first, shortens that tail.  Chunks over long cached
+// contexts (tiles of nearly equal length, more tiles per pair) keep one pair
+// at a time, which keeps the blocks in flight in the XCD's L2.
+__host__ __device__ __forceinline__ int pair_window(const PrefillParams &p) {
+    return (p.num_tiles <= 16 && 2 * (int64_t)p.max_query_len >= (int64_t)p.max_blocks_per_seq * kBlock) ? 4
+                                                                                                         : 1;
+}
+
 __device__ __forceinline__ uint32_t f16x2_bits(f16x2 h) { return __builtin_bit_cast(uint32_t, h); }
 
 // two bf16 (one word) -> two fp16 (one word), rounded to nearest: exact for
@@ -99,15 +111,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
     const int BQ = kRowsPerTile / G;
     // Workgroup b runs on XCD b % 8.  Each (sequence, KV head) pair -- whose
     // tiles all read the same blocks -- goes to one XCD (pair q to XCD q % 8),
-    // and an XCD takes its pairs one after another, all tiles of a pair
-    // together, longest first: the blocks the tiles in flight share stay in
-    // that XCD's L2.  Workgroups past the last pair have nothing to do.
+    // and an XCD takes its pairs a window of PW at a time, the window's tiles
+    // together, longest first (pair by pair within a rank): the blocks the
+    // tiles in flight share stay in that XCD's L2.  Workgroups past the last
+    // pair have nothing to do.
     const int pairs = p.num_seqs * p.num_kv_heads;
+    const int PW = pair_window(p);
     const int xcd = (int)(blockIdx.x % kXcds);
     const int local = (int)(blockIdx.x / kXcds);
-    const int pair = xcd + kXcds * (local / p.num_tiles);
+    const int span = PW * p.num_tiles;
+    const int in_win = local % span;
+    const int pair = xcd + kXcds * ((local / span) * PW + in_win % PW);
     if (pair >= pairs) return;
-    const int tile = p.num_tiles - 1 - local % p.num_tiles;
+    const int tile = p.num_tiles - 1 - in_win / PW;
     const int s = pair / p.num_kv_heads;
     const int g = pair % p.num_kv_heads;
 
@@ -140,19 +156,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
         return w;
     };
     int pos_mask[kGroups];
-    int minpos = 0x7fffffff;
+    int minpos = 0x7fffffff, maxpos = -1;
 #pragma unroll
     for (int k = 0; k < kGroups; ++k) {
         const Row w = row_of(k);
         // rows that produce no output are masked like the context's last token
         pos_mask[k] = w.live ? first + w.tok : ctx - 1;
         minpos = min(minpos, pos_mask[k]);
+        maxpos = max(maxpos, pos_mask[k]);
     }
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) minpos = min(minpos, __shfl_xor(minpos, o));
-    // the same in every lane: as a uniform value the per-step mask test is a
-    // scalar branch, not an exec-masked region issued on every step
+    for (int o = 1; o < 64; o <<= 1) {
+        minpos = min(minpos, __shfl_xor(minpos, o));
+        maxpos = max(maxpos, __shfl_xor(maxpos, o));
+    }
+    // the same in every lane: as uniform values the per-step mask tests are
+    // scalar branches, not exec-masked regions issued on every step
     minpos = __builtin_amdgcn_readfirstlane(minpos);
+    maxpos = __builtin_amdgcn_readfirstlane(maxpos);
 
     // Q^T operands (zero for rows outside the chunk): head dims 8 (4 u + c) .. +7
     // for step u, matching the staged bf16 K runs
@@ -426,8 +447,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
             compute_step(std::false_type{}, i & 1, 2 * i, ok(ida) ? 0.f : kNegInfF, ok(idb) ? 0.f : kNegInfF);
             next(i);
         }
+        // A step wholly past every row of this wavefront (its first token
+        // beyond the wavefront's largest position: with one query head per
+        // KV head a tile spans 128 positions) only stages for the others:
+        // its scores would all be -inf, adding exact zeros.
+        const int sx = min(maxpos / (2 * kBlock) + 1, nstep);
         for (int i = sm; i < nstep; ++i) {
-            compute_step(std::true_type{}, i & 1, 2 * i, ok(ida) ? 0.f : kNegInfF, ok(idb) ? 0.f : kNegInfF);
+            if (i < sx)
+                compute_step(std::true_type{}, i & 1, 2 * i, ok(ida) ? 0.f : kNegInfF,
+                             ok(idb) ? 0.f : kNegInfF);
             next(i);
         }
     }
@@ -455,7 +483,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
 template <int KV, int D>
 hipError_t launch(const PrefillParams &p, hipStream_t stream, const LaunchEvents *ev) {
     const int64_t pairs = (int64_t)p.num_seqs * p.num_kv_heads;
-    const int64_t grid = (int64_t)p.num_tiles * kXcds * ((pairs + kXcds - 1) / kXcds);
+    const int64_t per_round = (int64_t)kXcds * pair_window(p);  // pairs per round of windows
+    const int64_t grid = (int64_t)p.num_tiles * per_round * ((pairs + per_round - 1) / per_round);
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
     return launch_kernel(prefill_mfma_kernel<KV, D>, dim3((unsigned)grid), dim3(kThreads), stream, ev, p);
 }
