@@ -259,3 +259,36 @@ def test_prefill_head_shapes_match_oracle(D, Hq, Hkv, dt):
     assert np.isfinite(got).all()
     err = float(np.max(np.abs(got - ref)))
     assert err <= tolerance(w), "max abs error %.3e" % err
+
+
+def test_prefill_whole_prompts_one_head_per_kv_head():
+    """Whole prompts (context = chunk) with one query head per KV head: tiles
+    of 128 positions, 15 (sequence, head) pairs.  With the table just wide
+    enough for the longest prompt the kernel takes its pairs four at a time;
+    with the same table padded to 64 blocks it takes them one at a time.
+    Both runs match the oracle and each other bit for bit (a row's arithmetic
+    does not depend on the order the workgroups run in), including the rows
+    whose wavefronts skip the steps past all their positions."""
+    import math
+    rng = np.random.default_rng(77)
+    D, H = 128, 5
+    ctx = np.array([300, 129, 77], np.int32)
+    w = wl._simple("whole", 3, H, H, D, ctx, oracle.BF16, oracle.BF16, oracle.BF16,
+                   float(np.float32(1 / math.sqrt(D))), 77, "cpu", rng)
+    qs = np.zeros(4, np.int32)
+    qs[1:] = np.cumsum(ctx)
+    w.query_start = qs
+    w.prefill_q = torch.randn((int(qs[-1]), H, D), generator=torch.Generator().manual_seed(78)
+                              ).to(torch.bfloat16)
+    assert w.block_tables.shape[1] * 16 <= 2 * int(ctx.max())
+    kp, vp = oracle_pools(w)
+    ref = oracle_prefill(w, kp, vp)
+    pool = gpu_pool(w, fill=0xFF)
+    narrow = gpu_prefill(w, pool)
+    wide_tables = np.full((3, 64), -1, np.int32)
+    wide_tables[:, :w.block_tables.shape[1]] = w.block_tables
+    wide = gpu_prefill(w, pool, tables=wide_tables)
+    assert np.isfinite(narrow).all()
+    err = float(np.max(np.abs(narrow - ref)))
+    assert err <= tolerance(w), "max abs error %.3e" % err
+    assert_same_bytes(narrow, wide)
