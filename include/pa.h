@@ -148,6 +148,11 @@ size_t pa_decode_workspace_size(const pa_pool_t *pool, int32_t num_seqs, int32_t
  *   workspace      device buffer of >= pa_decode_workspace_size(...) bytes
  *                  (may be NULL when that size is 0).
  * Query head h attends with KV head h / (num_q_heads / num_kv_heads).
+ * Precision: scores, softmax and accumulation in fp32.  The probabilities
+ * enter the P.V product in fp32 (fp32 pools) or to 16 significant bits as
+ * bf16 hi + lo pairs, except with an fp8 pool and several query heads per KV
+ * head, where they are rounded to fp16 (relative error <= 2^-11; the row sum
+ * adds the same rounded values) against V widened exactly to fp16.
  */
 int pa_decode(const pa_pool_t *pool, const void *q, int32_t q_dtype, int32_t num_seqs,
               int32_t num_q_heads, const int32_t *block_tables, int32_t max_blocks_per_seq,
