@@ -437,17 +437,19 @@ def decode_run(w, steps, warmup, ptok, append="separate", graph=False, flush_and
         return {"pairs": int(pairs.shape[0]), "what": label, "block_bytes_per_pool": block_bytes,
                 "ms": round(copy_ms, 5), "read_plus_write_GBps": round(moved / copy_ms / 1e6, 1)}
 
+    # The copy-on-write pairs alone, timed on a scratch pool of the same
+    # shape: in the real pool each copy's destination has since received its
+    # sequence's own token, which copying again without that write would
+    # overwrite (and the decode calls after this point read the real pool).
+    timed_pairs = None
     if step_pairs.shape[0]:
-        # the step's copies, each followed in the step by its token write
-        res["extra"]["copy_blocks"] = time_copies(step_pairs, "the step's copy-on-write pairs", pool)
+        timed_pairs = (step_pairs, "the step's copy-on-write pairs")
     elif cow_pairs is not None and cow_pairs.shape[0]:
-        # the fork's copies, timed on a scratch pool of the same shape: the
-        # samples have since written their own tokens into the copies, which
-        # copying again would overwrite
+        timed_pairs = (cow_pairs, "the fork's copy-on-write pairs (shared partial prompt blocks)")
+    if timed_pairs is not None:
         scratch = ops.KVPool(w.num_blocks, w.Hkv, w.D, w.pool_dtype, device=dev, k_scale=w.k_scale,
                              v_scale=w.v_scale, fill=0)
-        res["extra"]["copy_blocks"] = time_copies(
-            cow_pairs, "the fork's copy-on-write pairs (shared partial prompt blocks)", scratch)
+        res["extra"]["copy_blocks"] = time_copies(timed_pairs[0], timed_pairs[1], scratch)
         del scratch
     if groups is not None:
         # the plain decode (one workgroup per sequence and KV head) on the same
