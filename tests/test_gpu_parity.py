@@ -414,40 +414,24 @@ def _sampled_rows(w, seqs):
 
 
 @pytest.mark.parametrize("name", ["mha13b", "gqa70b", "fp8", "sampling_a", "sampling_b"])
-def test_full_size_sampled_rows(name):
-    """The full-size workload in the launch configuration the benchmark uses,
-    checked on sampled sequences (every head) against the oracle, and pool
-    bytes of those sequences' blocks bit-exact."""
+def test_full_size_whole_output(name):
+    """The full-size workload in the launch configuration the benchmark uses:
+    every pool byte equals the oracle's after the workload's cache writes and
+    copies, and the whole output tensor (every sequence and query head) is
+    within tolerance of the oracle."""
+    import time
     torch.manual_seed(0)
     w = wl.make_workload(name, small=False, device="cuda")
     pool = gpu_pool(w)
     out = gpu_decode(w, pool)
-    ctx = w.context_lens
-    seqs = sorted({int(np.argmax(ctx)), int(np.argmin(ctx)), 0, w.S - 1, w.S // 2, w.S // 3})
-    if name.startswith("sampling"):
-        kp, vp = oracle_pools(w)
-    else:
-        _, k, v, slots = w.ops[0]
-        off = np.concatenate([[0], np.cumsum(ctx.astype(np.int64))])
-        idx = np.concatenate([np.arange(off[s], off[s + 1]) for s in seqs])
-        kp = oracle.new_pool(w.num_blocks, w.Hkv, w.D, w.pool_dtype)
-        vp = oracle.new_pool(w.num_blocks, w.Hkv, w.D, w.pool_dtype)
-        it = torch.as_tensor(idx, device=k.device)
-        oracle.reshape_and_cache(kp, vp, w.pool_dtype, w.num_blocks, w.Hkv, w.D,
-                                 raw_numpy(k.index_select(0, it)),
-                                 raw_numpy(v.index_select(0, it)), w.kv_in_dtype,
-                                 slots[idx], w.k_scale, w.v_scale)
-        gk, gv = _pool_bytes(pool)
-        tile = 16 * w.D * oracle.ELEM_BYTES[w.pool_dtype] * w.Hkv
-        for s in seqs:
-            for b in w.block_tables[s][:blocks_for(ctx[s])]:
-                sl = slice(int(b) * tile, (int(b) + 1) * tile)
-                assert np.array_equal(gk[sl], kp[sl]) and np.array_equal(gv[sl], vp[sl])
-    rows = _sampled_rows(w, seqs)
-    ref = oracle_decode(w, kp, vp, rows=rows)
-    got = np.stack([out[s, h] for s, h in rows])
-    err = float(np.max(np.abs(got - ref)))
-    print("%s full size: %d rows, max abs err %.3e" % (name, len(rows), err))
+    t0 = time.perf_counter()
+    kp, vp = oracle_pools(w)
+    gk, gv = _pool_bytes(pool)
+    assert np.array_equal(gk, kp) and np.array_equal(gv, vp)
+    ref = oracle_decode(w, kp, vp).reshape(out.shape)
+    err = float(np.max(np.abs(out - ref)))
+    print("%s full size: %d rows, max abs err %.3e (oracle %.1f s)"
+          % (name, w.S * w.Hq, err, time.perf_counter() - t0))
     assert err <= tolerance(w)
 
 
