@@ -382,20 +382,25 @@ __global__ __launch_bounds__(kThreads) void append_tokens_kernel(DecodeParams p)
     for (int d = threadIdx.x; d < D; d += kThreads) append_element<POOL, D>(p, table, s, g, ctx - 1, d);
 }
 
-// Heads per cache-write workgroup: 8 for bulk writes (prompts: thousands of
-// windows), 1 for small ones (a decode step's lone tokens, whose writes are
+// Heads per cache-write workgroup: for bulk writes (prompts: thousands of
+// windows) 8 with a 16/32-bit pool and 2 with an fp8 pool, whose encoding
+// makes every work item heavier (the 70B-like fill: 8 heads 1.695 ms, 2
+// heads 1.718; the fp8 fill: 8 heads 0.596 ms, 4 heads 0.560, 2 heads
+// 0.548); 1 for small writes (a decode step's lone tokens, whose writes are
 // latency-bound round trips and need the workgroups: 256 tokens x 8 heads
 // took 17.8 us from 16 eight-head workgroups against ~4 us from 128).
-constexpr int kCacheHeads = 8;
-constexpr int64_t kCacheBulkGroups = 2048;  // workgroups of the 8-head grid from which it is used
+template <int POOL>
+constexpr int kCacheHeads = POOL == kFP8 ? 2 : 8;
+constexpr int64_t kCacheBulkGroups = 2048;  // workgroups of the bulk grid from which it is used
 
 template <int POOL, int IN, int D>
 hipError_t launch_rc(const CacheParams &p, hipStream_t stream) {
+    constexpr int HPW = kCacheHeads<POOL>;
     const int64_t groups = (p.num_tokens + kBlock - 1) / kBlock;
     if (groups > 0x7fffffffLL || p.num_kv_heads > 65535) return hipErrorInvalidValue;
-    const int64_t hgroups = (p.num_kv_heads + kCacheHeads - 1) / kCacheHeads;
+    const int64_t hgroups = (p.num_kv_heads + HPW - 1) / HPW;
     if (groups * hgroups >= kCacheBulkGroups)
-        reshape_and_cache_kernel<POOL, IN, D, kCacheHeads>
+        reshape_and_cache_kernel<POOL, IN, D, HPW>
             <<<dim3((unsigned)groups, (unsigned)hgroups), dim3(kThreads), 0, stream>>>(p);
     else
         reshape_and_cache_kernel<POOL, IN, D, 1>
