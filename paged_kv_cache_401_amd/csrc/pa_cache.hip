@@ -137,7 +137,10 @@ __global__ __launch_bounds__(kThreads) void reshape_and_cache_kernel(CacheParams
 
     const int64_t nt = p.num_tokens - w0 < kBlock ? p.num_tokens - w0 : kBlock;
     constexpr int NR = D / X;                        // K runs per token and head
-    for (int e = threadIdx.x; e < nt * NR * nh; e += kThreads) {
+    // A grid of depth 2 splits each window's tiles: z = 0 writes the K tiles
+    // (and the lone tokens), z = 1 the V tiles.
+    const bool do_k = blockIdx.z == 0, do_v = blockIdx.z == 1 || gridDim.z == 1;
+    for (int e = threadIdx.x; do_k && e < nt * NR * nh; e += kThreads) {
         const int t = e / (NR * nh), hh = (e / NR) % nh, r = e % NR;
         if (!((cov >> t) & 1u)) write_run<POOL, IN, D>(p, w0 + t, g0 + hh, r, p.slot_mapping[w0 + t]);
     }
@@ -185,7 +188,7 @@ __global__ __launch_bounds__(kThreads) void reshape_and_cache_kernel(CacheParams
 #pragma unroll
         for (int j = 0; j < KI; ++j) {
             const int i = threadIdx.x + j * kThreads;
-            if (!KFULL && i >= nh * K_UNITS) break;
+            if (!do_k || (!KFULL && i >= nh * K_UNITS)) break;
             const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const char *>(p.k) + k_in(i) * IB);
 #pragma unroll
             for (int c = 0; c < NKU; ++c) kr[j][c] = src[c];
@@ -193,7 +196,7 @@ __global__ __launch_bounds__(kThreads) void reshape_and_cache_kernel(CacheParams
 #pragma unroll
         for (int j = 0; j < VI; ++j) {
             const int i = threadIdx.x + j * kThreads;
-            if (!VFULL && i >= nh * VU) break;
+            if (!do_v || (!VFULL && i >= nh * VU)) break;
             const int64_t e = v_in(i);
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt)
@@ -272,13 +275,13 @@ __global__ __launch_bounds__(kThreads) void reshape_and_cache_kernel(CacheParams
 #pragma unroll
         for (int j = 0; j < KI; ++j) {
             const int i = threadIdx.x + j * kThreads;
-            if (!KFULL && i >= nh * K_UNITS) break;
+            if (!do_k || (!KFULL && i >= nh * K_UNITS)) break;
             store16_nt(unit(p.k_pool, i / K_UNITS, i % K_UNITS), kw[j]);
         }
 #pragma unroll
         for (int j = 0; j < VI; ++j) {
             const int i = threadIdx.x + j * kThreads;
-            if (!VFULL && i >= nh * VU) break;
+            if (!do_v || (!VFULL && i >= nh * VU)) break;
 #pragma unroll
             for (int cc = 0; cc < CPI; ++cc) store16_nt(unit(p.v_pool, i / VU, (i % VU) * CPI + cc), vw[j][cc]);
         }
@@ -391,6 +394,11 @@ __global__ __launch_bounds__(kThreads) void append_tokens_kernel(DecodeParams p)
 // took 17.8 us from 16 eight-head workgroups against ~4 us from 128).
 template <int POOL>
 constexpr int kCacheHeads = POOL == kFP8 ? 2 : 8;
+// ... and with 8 heads, K and V tiles from separate workgroups (twice as
+// many, each reading and writing 32 KiB: the 70B-like fill 1.689 ->
+// 1.665 ms; the fp8 fill with 2 heads is 0.5 % slower split)
+template <int POOL>
+constexpr unsigned kCacheSplit = kCacheHeads<POOL> == 8 ? 2u : 1u;
 constexpr int64_t kCacheBulkGroups = 2048;  // workgroups of the bulk grid from which it is used
 
 template <int POOL, int IN, int D>
@@ -401,7 +409,7 @@ hipError_t launch_rc(const CacheParams &p, hipStream_t stream) {
     const int64_t hgroups = (p.num_kv_heads + HPW - 1) / HPW;
     if (groups * hgroups >= kCacheBulkGroups)
         reshape_and_cache_kernel<POOL, IN, D, HPW>
-            <<<dim3((unsigned)groups, (unsigned)hgroups), dim3(kThreads), 0, stream>>>(p);
+            <<<dim3((unsigned)groups, (unsigned)hgroups, kCacheSplit<POOL>), dim3(kThreads), 0, stream>>>(p);
     else
         reshape_and_cache_kernel<POOL, IN, D, 1>
             <<<dim3((unsigned)groups, (unsigned)p.num_kv_heads), dim3(kThreads), 0, stream>>>(p);
