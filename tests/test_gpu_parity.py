@@ -311,6 +311,25 @@ def test_decode_many_rows(D, dt, ptok):
     assert err <= tolerance(w), "max abs error %.3e" % err
 
 
+@pytest.mark.parametrize("G,dt", [(1, oracle.BF16), (8, oracle.BF16), (8, oracle.FP8)])
+@pytest.mark.parametrize("ptok", [48, 512])
+def test_decode_long_tail_batch_past_one_wavefront(G, dt, ptok):
+    """130 sequences (more than one wavefront ranks by length, so the work
+    order is index order) with long-tailed contexts of 1..1200 tokens over
+    many split-K partitions: every row matches the oracle."""
+    S, Hkv, D = 130, 2, 128
+    rng = np.random.default_rng(7 * G + dt + ptok)
+    ctx = np.minimum(np.exp(rng.normal(5.0, 1.2, S)).astype(np.int64) + 1, 1200)
+    w = wl._simple("item_order", S, G * Hkv, Hkv, D, ctx, dt, oracle.BF16, oracle.BF16,
+                   float(np.float32(1 / math.sqrt(D))), 29, "cpu", rng, fp8_scales=dt == oracle.FP8)
+    kp, vp = oracle_pools(w)
+    ref = oracle_decode(w, kp, vp)
+    got = gpu_decode(w, gpu_pool(w, fill=0xFF), partition_tokens=ptok)
+    assert np.isfinite(got).all()
+    err = float(np.max(np.abs(got - ref)))
+    assert err <= tolerance(w), "max abs error %.3e" % err
+
+
 @pytest.mark.parametrize("Hq", [1, 2])
 def test_fp8_decode_all_codes_through_attention(Hq):
     """A one-hot probe on tokens whose V rows hold all 256 E4M3FN codes: the
