@@ -101,8 +101,16 @@ int32_t simd_count() {
 int wave_mode(const pa_pool_t *pool, int32_t num_seqs, int32_t num_q_heads, int32_t raw_partitions,
               int32_t ptok) {
     if (raw_partitions > 1 && ptok <= 512) return pa::kPartGroups;
-    return (int64_t)num_seqs * pool->num_kv_heads >= 2 * (int64_t)simd_count() ? pa::kOneWave
-                                                                                : pa::kFourWaves;
+    const int64_t rows = (int64_t)num_seqs * pool->num_kv_heads;
+    const int64_t simds = simd_count();
+    if (rows < 2 * simds) return pa::kFourWaves;
+    // With a bf16 pool and exactly one row per slot at two wavefronts per
+    // SIMD, three blocks in flight per wavefront (200 VGPRs): the 70B-like
+    // batch (2048 rows) after a 1 GiB read 0.666 -> 0.647 ms, back to back
+    // 0.643 -> 0.645 ms; with more rows the second round costs more (beam
+    // search, 4096 rows: 0.123 -> 0.131 ms), so they keep two.
+    if (pool->kv_dtype == PA_BF16 && rows <= 2 * simds) return pa::kOneWaveDeep;
+    return pa::kOneWave;
 }
 
 bool grouped_kernel(const pa_pool_t *pool, int32_t num_q_heads) {

@@ -106,7 +106,7 @@ struct TableBlocks {
 // them to the pool.  Stores issued before later loads would make every wait
 // on those loads wait for the stores as well (one counter covers both, in
 // issue order), and under full read traffic stores are slow.
-template <int KV, int D, bool STREAM, bool APPEND, class Src>
+template <int KV, int D, bool STREAM, bool APPEND, class Src, int NB = 2>
 __device__ __forceinline__ void walk_blocks(const DecodeParams &p, int s, int g, const Src &src,
                                             const uint16_t *qcol, int ncols, int ctx, bool writer,
                                             uint8_t *tok_k, uint8_t *tok_v, float &m, float &l,
@@ -314,10 +314,11 @@ __device__ __forceinline__ void walk_blocks(const DecodeParams &p, int s, int g,
         // the newest token's inputs go out first (lane elements lane + 64 i)
         NewToken<D> nt;
         if (APPEND && writer) nt = append_load<KV, D>(p, table, s, g, ctx - 1, lane);
-        u32x4 kb[2][NKL], vb[2][NVL];
-        int32_t idb[2];
+        static_assert(NB == 2 || NB == 3, "two or three register buffers");
+        u32x4 kb[NB][NKL], vb[NB][NVL];
+        int32_t idb[NB];
 #pragma unroll
-        for (int d = 0; d < 2; ++d) {
+        for (int d = 0; d < NB; ++d) {
             idb[d] = id_at(d);
             load_k(idb[d], kb[d], kFenced);
             load_v(idb[d], vb[d], kFenced);
@@ -379,10 +380,10 @@ __device__ __forceinline__ void walk_blocks(const DecodeParams &p, int s, int g,
             }
         };
 
-        int32_t id_pre = id_at(2);
+        int32_t id_pre = id_at(NB);
         auto step = [&](int d, int kk) {
-            const int32_t id_after = id_pre;  // block kk + 2
-            id_pre = id_at(kk + 3);
+            const int32_t id_after = id_pre;  // block kk + NB
+            id_pre = id_at(kk + NB + 1);
             if (APPEND && writer && src.block(kk) == jlast) patch(kb[d], vb[d]);
             const floatx4 sacc = qk(kb[d]);
             load_k(id_after, kb[d], kFree);
@@ -395,11 +396,21 @@ __device__ __forceinline__ void walk_blocks(const DecodeParams &p, int s, int g,
             idb[d] = id_after;
         };
         int k = 0;
-        for (; k + 1 < nk; k += 2) {
-            step(0, k);
-            step(1, k + 1);
+        if constexpr (NB == 3) {
+            for (; k + 2 < nk; k += 3) {
+                step(0, k);
+                step(1, k + 1);
+                step(2, k + 2);
+            }
+            if (k < nk) step(0, k);
+            if (k + 1 < nk) step(1, k + 1);
+        } else {
+            for (; k + 1 < nk; k += 2) {
+                step(0, k);
+                step(1, k + 1);
+            }
+            if (k < nk) step(0, k);
         }
-        if (k < nk) step(0, k);
 
         // the token to the pool (an id outside the pool is skipped): K runs
         // as 16-byte stores, V elements one by one
@@ -524,7 +535,7 @@ __device__ __forceinline__ void merge_and_store(const DecodeParams &p, const Dec
 // merged through LDS.  APPEND: the decode step's newest tokens are written
 // by this call unless `clamped` (the context was longer than its table row:
 // no slot to write).
-template <int KV, int D, bool STREAM, int NW, bool APPEND>
+template <int KV, int D, bool STREAM, int NW, bool APPEND, int NB = 2>
 __device__ __forceinline__ void decode_item(const DecodeParams &p, int s, int g, int part, int ctx,
                                             bool clamped, DecodeLds<D, NW> &sm) {
     constexpr int W = KV == kBF16 ? 2 : 4;
@@ -543,8 +554,8 @@ __device__ __forceinline__ void decode_item(const DecodeParams &p, int s, int g,
     const TableBlocks src{p.block_tables + (int64_t)s * p.max_blocks_per_seq, blk0 + wv, NW, nk, tok1};
     float m, l;
     floatx4 acc[D / 16];
-    walk_blocks<KV, D, STREAM, APPEND>(p, s, g, src, query_column<D>(p, s, g), p.group, ctx, writer,
-                                       sm.tok_k, sm.tok_v, m, l, acc);
+    walk_blocks<KV, D, STREAM, APPEND, TableBlocks, NB>(p, s, g, src, query_column<D>(p, s, g), p.group, ctx,
+                                                         writer, sm.tok_k, sm.tok_v, m, l, acc);
     state_to_lds<D, NW, W>(sm, wv, m, l, acc);
     __syncthreads();
     merge_and_store<D, NW>(p, sm, s, g, part, nparts <= 1, NW, threadIdx.x, 64 * NW, p.group);
@@ -557,8 +568,10 @@ __device__ __forceinline__ int clamp_ctx(const DecodeParams &p, int ctx) {
 
 // One workgroup of NW wavefronts per (sequence, KV head, partition) slot of
 // a rows x max_partitions grid.
-template <int KV, int D, bool STREAM, int NW, bool APPEND>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) void decode_mfma_kernel(DecodeParams p) {
+// NB: register buffers per wavefront (blocks in flight); three take 200 VGPRs
+// (2 waves/SIMD) at head dim 128.
+template <int KV, int D, bool STREAM, int NW, bool APPEND, int NB = 2>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NB == 3 ? 2 : 3))) void decode_mfma_kernel(DecodeParams p) {
     __shared__ DecodeLds<D, NW> sm;
     // Work order: the first num_seqs x num_kv_heads workgroups take partition
     // 0 of every (sequence, KV head) pair -- all real work, spread evenly over
@@ -575,7 +588,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
                                    bid / p.num_kv_heads);
     const int raw_ctx = p.context_lens[s];
     const int ctx = clamp_ctx(p, raw_ctx);
-    decode_item<KV, D, STREAM, NW, APPEND>(p, s, g, part, ctx, raw_ctx > ctx, sm);
+    decode_item<KV, D, STREAM, NW, APPEND, NB>(p, s, g, part, ctx, raw_ctx > ctx, sm);
 }
 
 // Partition groups: one workgroup of NG wavefronts per (sequence, KV head,
@@ -775,7 +788,11 @@ hipError_t launch_variant(const DecodeParams &p, int64_t grid, hipStream_t strea
     const dim3 g((unsigned)grid);
     if (p.wave_mode == kFourWaves)
         return launch_kernel(decode_mfma_kernel<KV, D, STREAM, 4, APPEND>, g, dim3(256), stream, ev, p);
-    if (p.wave_mode == kOneWave)
+    if constexpr (KV == kBF16) {
+        if (p.wave_mode == kOneWaveDeep)
+            return launch_kernel(decode_mfma_kernel<KV, D, STREAM, 1, APPEND, 3>, g, dim3(64), stream, ev, p);
+    }
+    if (p.wave_mode == kOneWave || p.wave_mode == kOneWaveDeep)
         return launch_kernel(decode_mfma_kernel<KV, D, STREAM, 1, APPEND>, g, dim3(64), stream, ev, p);
     return launch_kernel(decode_group_kernel<KV, D, STREAM, kGroupParts, APPEND>, g, dim3(64 * kGroupParts),
                          stream, ev, p);

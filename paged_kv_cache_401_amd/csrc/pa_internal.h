@@ -19,6 +19,8 @@ enum WaveMode : int {
     kOneWave = 1,     // one partition per one-wavefront workgroup
     kPartGroups = 2,  // kGroupParts consecutive partitions per workgroup, one per wavefront,
                       // merged on chip into one partial result
+    kOneWaveDeep = 3, // as kOneWave with three blocks in flight per wavefront (bf16 pools;
+                      // 2 waves/SIMD)
 };
 
 inline int elem_bytes(int kv) { return kv == kF32 ? 4 : (kv == kBF16 ? 2 : 1); }
