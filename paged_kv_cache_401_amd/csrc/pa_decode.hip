@@ -87,7 +87,7 @@ __device__ __forceinline__ float wave_max16(float x) {
 }
 
 template <int KV, int D, bool STREAM>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KV == kF32 ? 1 : 4))) void decode_valu_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KV == kF32 ? 1 : (KV == kBF16 ? 2 : 4)))) void decode_valu_kernel(DecodeParams p) {
     constexpr int EB = KV == kF32 ? 4 : (KV == kBF16 ? 2 : 1);
     constexpr int X = 16 / EB;          // K: elements per 16-byte run
     constexpr int W = 4 / EB;           // V: head-dim elements per 16-byte cell
@@ -301,11 +301,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KV == 
     };
 
     // This wavefront's blocks are j = blk0 + wave + 4k, k = 0..nk-1; their ids
-    // come from the table by scalar loads, one block ahead of their use.  Two
-    // register buffers hold blocks k and k + 1; block k + 2 reuses block k's
-    // buffer half by half (K once its dot products are formed, V once it is
-    // consumed), and every step issues the same loads (empty resources past
-    // the end), so each wait covers exactly the loads it needs.
+    // come from the table by scalar loads, one block ahead of their use.  NB
+    // register buffers hold blocks k .. k + NB - 1; block k + NB reuses block
+    // k's buffer half by half (K once its dot products are formed, V once it
+    // is consumed), and every step issues the same loads (empty resources
+    // past the end), so each wait covers exactly the loads it needs.  bf16
+    // pools keep three blocks in flight (176 VGPRs at head dim 128, 2
+    // waves/SIMD: the 13B-like batch 0.1077 -> 0.1060 ms), the others two.
     const int nk = blk1 - blk0 > wv ? (blk1 - blk0 - wv + 3) / 4 : 0;
     if (nk > 0) {
         const int32_t *wtable = table + blk0 + wv;
@@ -313,25 +315,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KV == 
             const int32_t b = wtable[4 * min(k, nk - 1)];
             return k < nk ? b : -1;
         };
-        // with two blocks or fewer the last one is loaded in the prologue: the
+        // with NB blocks or fewer the last one is loaded in the prologue: the
         // token is stored before it then
-        const bool early = writer && nk <= 2;
+        constexpr int NB = KV == kBF16 ? 3 : 2;
+        const bool early = writer && nk <= NB;
         NewToken<D> nt;
         if (writer) nt = append_load<KV, D>(p, table, s, g, ctx - 1, lane);
         if (early) append_store<KV, D>(p, nt, g, ctx - 1, lane);
-        uint4 kb[2][NKL], vb[2][NVL];
-        int32_t idb[2];
+        uint4 kb[NB][NKL], vb[NB][NVL];
+        int32_t idb[NB];
 #pragma unroll
-        for (int d = 0; d < 2; ++d) {
+        for (int d = 0; d < NB; ++d) {
             idb[d] = id_at(d);
             load_k(idb[d], kb[d], kFenced);
             load_v(idb[d], vb[d], kFenced);
         }
         if (writer && !early) append_store<KV, D>(p, nt, g, ctx - 1, lane);
-        int32_t id_pre = id_at(2);
+        int32_t id_pre = id_at(NB);
         auto step = [&](int d, int kk) {
-            const int32_t id_after = id_pre;  // block kk + 2
-            id_pre = id_at(kk + 3);
+            const int32_t id_after = id_pre;  // block kk + NB
+            id_pre = id_at(kk + NB + 1);
             const float part = qk(kb[d]);
             load_k(id_after, kb[d], kFree);
             if (valid(idb[d])) softmax_pv(part, vb[d], blk0 + wv + 4 * kk);
@@ -339,11 +342,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KV == 
             idb[d] = id_after;
         };
         int k = 0;
-        for (; k + 1 < nk; k += 2) {
-            step(0, k);
-            step(1, k + 1);
+        if constexpr (NB == 3) {
+            for (; k + 2 < nk; k += 3) {
+                step(0, k);
+                step(1, k + 1);
+                step(2, k + 2);
+            }
+            if (k < nk) step(0, k);
+            if (k + 1 < nk) step(1, k + 1);
+        } else {
+            for (; k + 1 < nk; k += 2) {
+                step(0, k);
+                step(1, k + 1);
+            }
+            if (k < nk) step(0, k);
         }
-        if (k < nk) step(0, k);
     }
 
     // add the four token quarters (rows c = 0..3)
