@@ -52,13 +52,13 @@ namespace {
 constexpr float kNegInf = kNegInfF;
 constexpr float kLazyMax = 8.0f;  // raise the running maximum only past 2^8 (base-2 scores)
 
-// LDS of one workgroup: the wavefronts' softmax states and numerators,
-// merged at the end of a work item
-template <int D, int NW>
+// LDS of one workgroup: the wavefronts' softmax states and numerators of
+// the first NC matrix-core columns, merged at the end of a work item
+template <int D, int NW, int NC = 16>
 struct DecodeLds {
-    float m[NW][16];
-    float l[NW][16];
-    float acc[NW][D * 17];   // [wave][d][head], padded
+    float m[NW][NC];
+    float l[NW][NC];
+    float acc[NW][D * (NC + 1)];   // [wave][d][head], padded
     // the newest token's K and V as the pool stores them (head-dim order;
     // used by the wavefront that writes it)
     alignas(16) uint8_t tok_k[D * 2];
@@ -458,14 +458,15 @@ __device__ __forceinline__ const uint16_t *query_column(const DecodeParams &p, i
 
 // One wavefront's (m, l, numerators) to slot `w` of the workgroup's LDS, in
 // [w][d][head] order.
-template <int D, int NW, int W>
-__device__ __forceinline__ void state_to_lds(DecodeLds<D, NW> &sm, int w, float m, float l,
+template <int D, int NW, int W, int NC = 16>
+__device__ __forceinline__ void state_to_lds(DecodeLds<D, NW, NC> &sm, int w, float m, float l,
                                              const floatx4 (&acc)[D / 16]) {
-    constexpr int LDS_STRIDE = 17;
+    constexpr int LDS_STRIDE = NC + 1;
     constexpr int NVL = D / W / 16;
     const int lane = threadIdx.x & 63;
     const int n = lane & 15;
     const int c = lane >> 4;
+    if (n >= NC) return;   // columns past NC hold no query head
     if (c == 0) {
         sm.m[w][n] = m;
         sm.l[w][n] = l;
@@ -492,11 +493,11 @@ __device__ __forceinline__ void state_to_lds(DecodeLds<D, NW> &sm, int w, float 
 // them switched off), so there are 4x fewer of them than with one per dim.
 // Final outputs go out non-temporal; split-K partials stay cacheable, since
 // the reduce kernel reads them right after.
-template <int D, int NW>
-__device__ __forceinline__ void merge_and_store(const DecodeParams &p, const DecodeLds<D, NW> &sm, int s,
+template <int D, int NW, int NC = 16>
+__device__ __forceinline__ void merge_and_store(const DecodeParams &p, const DecodeLds<D, NW, NC> &sm, int s,
                                                 int g, int slot, bool final, int nw, int t0,
                                                 int tstride, int ncols) {
-    constexpr int LDS_STRIDE = 17;
+    constexpr int LDS_STRIDE = NC + 1;
     constexpr int D4 = D / 4;
     const int G = p.group;
     for (int idx = t0; idx < ncols * D4; idx += tstride) {
@@ -602,9 +603,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NB == 3
 // of one per partition, and contexts of up to NG partitions need no reduce.
 // Wavefronts with no partition (past the end of a short context) leave at
 // once, after the one barrier that publishes the cleared counter.
-template <int KV, int D, bool STREAM, int NG, bool APPEND>
+// NC: LDS columns, 8 when the group has at most 8 query heads (half the LDS,
+// so more partly filled workgroups fit a CU: the fp8 long tail 0.1657 ->
+// 0.1648 ms), else 16.
+template <int KV, int D, bool STREAM, int NG, bool APPEND, int NC>
 __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(3))) void decode_group_kernel(DecodeParams p) {
-    __shared__ DecodeLds<D, NG> sm;
+    __shared__ DecodeLds<D, NG, NC> sm;
     constexpr int W = KV == kBF16 ? 2 : 4;
     int bid, grp;
     pair_and_partition(p.num_seqs * p.num_kv_heads, p.max_partitions, bid, grp);
@@ -635,7 +639,7 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(3))) vo
     floatx4 acc[D / 16];
     walk_blocks<KV, D, STREAM, APPEND>(p, s, g, src, query_column<D>(p, s, g), p.group, ctx, writer,
                                        sm.tok_k, sm.tok_v, m, l, acc);
-    state_to_lds<D, NG, W>(sm, wv, m, l, acc);
+    state_to_lds<D, NG, W, NC>(sm, wv, m, l, acc);
     // this wavefront's state is in LDS before it counts itself as done; the
     // last one to count sees every other state
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -645,7 +649,7 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(3))) vo
     before = __builtin_amdgcn_readfirstlane(before);
     if (before != (uint32_t)(nreal - 1)) return;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    merge_and_store<D, NG>(p, sm, s, g, grp, ngroups <= 1, nreal, threadIdx.x & 63, 64, p.group);
+    merge_and_store<D, NG, NC>(p, sm, s, g, grp, ngroups <= 1, nreal, threadIdx.x & 63, 64, p.group);
 }
 
 // Blocks of one partition of a prefix-sharing group, from the list its
@@ -794,7 +798,10 @@ hipError_t launch_variant(const DecodeParams &p, int64_t grid, hipStream_t strea
     }
     if (p.wave_mode == kOneWave || p.wave_mode == kOneWaveDeep)
         return launch_kernel(decode_mfma_kernel<KV, D, STREAM, 1, APPEND>, g, dim3(64), stream, ev, p);
-    return launch_kernel(decode_group_kernel<KV, D, STREAM, kGroupParts, APPEND>, g, dim3(64 * kGroupParts),
+    if (p.group <= 8)
+        return launch_kernel(decode_group_kernel<KV, D, STREAM, kGroupParts, APPEND, 8>, g,
+                             dim3(64 * kGroupParts), stream, ev, p);
+    return launch_kernel(decode_group_kernel<KV, D, STREAM, kGroupParts, APPEND, 16>, g, dim3(64 * kGroupParts),
                          stream, ev, p);
 }
 
